@@ -1,0 +1,210 @@
+"""Python binding of liboccult, the collaboration-aware MoE layer step
+(Occult) on one MI355X.
+
+Each function has the name of its C entry point in include/occ.h and only
+marshals arguments: tensors become device pointers, the current HIP stream is
+passed along, and a non-zero status raises OccError.  PyTorch provides device
+memory and streams; every step of the layer runs in the library's HIP kernels.
+There is no fallback: importing this package fails if liboccult.so has not
+been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboccult.so")
+
+OCC_OK, OCC_EINVAL, OCC_EUNSUP, OCC_ENOSPC, OCC_EHIP = 0, -1, -2, -3, -4
+OCC_F32, OCC_BF16 = 0, 1
+DTYPE_CODE = {"f32": OCC_F32, "bf16": OCC_BF16}
+
+
+class OccError(RuntimeError):
+    def __init__(self, code: int, where: str, text: str):
+        super().__init__(f"{where} failed with status {code}: {text}")
+        self.code = code
+
+
+class occ_layer_desc(C.Structure):
+    _fields_ = [("T", C.c_int32), ("d", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
+                ("D", C.c_int32), ("I", C.c_int32), ("n_shared", C.c_int32),
+                ("I_shared", C.c_int32), ("dtype", C.c_int32), ("renorm", C.c_int32)]
+
+
+class occ_brim(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("brim0", "brim1", "sfd_offset", "slot_offset",
+                                          "sfd_token", "epd_token", "epd_sfd", "epd_w", "S")]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m expert_top_router_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    P, I32, SZ = C.c_void_p, C.c_int32, C.c_size_t
+    DP, BP = C.POINTER(occ_layer_desc), C.POINTER(occ_brim)
+    sig = {
+        "occ_workspace_bytes": (SZ, [DP]),
+        "occ_ffn_workspace_bytes": (SZ, [DP]),
+        "occ_route_topk": (I32, [DP, P, P, P, P, P, P]),
+        "occ_build_brim": (I32, [DP, P, P, P, BP, P, SZ, P]),
+        "occ_dispatch": (I32, [DP, P, BP, P, P, P]),
+        "occ_expert_ffn": (I32, [DP, P, BP, P, P, P, P, SZ, P, P, P, P, P, P]),
+        "occ_expert_up": (I32, [DP, P, BP, P, P, P, SZ, P, P, P]),
+        "occ_expert_down": (I32, [DP, BP, P, P, P, SZ, P, P, P, P]),
+        "occ_combine": (I32, [DP, P, BP, P, P, P, P]),
+        "occ_coactivation": (I32, [DP, P, P, I32, P]),
+        "occ_place_greedy": (I32, [I32, I32, P, P]),
+        "occ_last_error": (C.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+# Every symbol the C header declares (checked by the tests).
+EXPORTED = ("occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk", "occ_build_brim",
+            "occ_dispatch", "occ_expert_ffn", "occ_expert_up", "occ_expert_down", "occ_combine",
+            "occ_coactivation", "occ_place_greedy", "occ_last_error")
+
+
+def lib():
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    """Device (or host) address of a tensor / numpy array / int, None for None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    if hasattr(t, "ctypes"):
+        return t.ctypes.data
+    raise TypeError(f"cannot take the address of {type(t)}")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != OCC_OK:
+        raise OccError(rc, where, _lib.occ_last_error().decode())
+
+
+def last_error() -> str:
+    return _lib.occ_last_error().decode()
+
+
+def make_desc(T, d, E, k, D, I, n_shared=0, I_shared=0, dtype="bf16", renorm=0) -> occ_layer_desc:
+    return occ_layer_desc(T, d, E, k, D, I, n_shared, I_shared,
+                          DTYPE_CODE.get(dtype, dtype), renorm)
+
+
+def desc_of(cfg) -> occ_layer_desc:
+    """Descriptor of a layer configuration object (T, d, E, k, D, I, ...)."""
+    return make_desc(cfg.T, cfg.d, cfg.E, cfg.k, cfg.D, cfg.I, cfg.n_shared, cfg.I_shared,
+                     cfg.dtype, cfg.renorm)
+
+
+def make_brim(**arrays) -> occ_brim:
+    return occ_brim(*[_ptr(arrays.get(n)) for n, _ in occ_brim._fields_])
+
+
+# ---- the entry points (same names as the C ABI) ---------------------------
+def occ_workspace_bytes(desc: occ_layer_desc) -> int:
+    return _lib.occ_workspace_bytes(C.byref(desc))
+
+
+def occ_ffn_workspace_bytes(desc: occ_layer_desc) -> int:
+    return _lib.occ_ffn_workspace_bytes(C.byref(desc))
+
+
+def occ_route_topk(desc, x, w_router, topk_idx, topk_w, logits=None, stream=None):
+    _check(_lib.occ_route_topk(C.byref(desc), _ptr(x), _ptr(w_router), _ptr(topk_idx),
+                               _ptr(topk_w), _ptr(logits), _stream(stream)), "occ_route_topk")
+
+
+def occ_build_brim(desc, topk_idx, topk_w, slot_expert_host, brim: occ_brim, ws, ws_bytes,
+                   stream=None):
+    import numpy as np
+    se = np.ascontiguousarray(slot_expert_host, dtype=np.int32)
+    _check(_lib.occ_build_brim(C.byref(desc), _ptr(topk_idx), _ptr(topk_w), se.ctypes.data,
+                               C.byref(brim), _ptr(ws), ws_bytes, _stream(stream)),
+           "occ_build_brim")
+
+
+def occ_dispatch(desc, x, brim: occ_brim, sfd, epd, stream=None):
+    _check(_lib.occ_dispatch(C.byref(desc), _ptr(x), C.byref(brim), _ptr(sfd), _ptr(epd),
+                             _stream(stream)), "occ_dispatch")
+
+
+def occ_expert_ffn(desc, epd, brim: occ_brim, slot_expert_host, w_gate_up, w_down, h_ws,
+                   h_ws_bytes, out_epd, x=None, w_gate_up_sh=None, w_down_sh=None,
+                   shared_out=None, stream=None):
+    import numpy as np
+    se = np.ascontiguousarray(slot_expert_host, dtype=np.int32)
+    _check(_lib.occ_expert_ffn(C.byref(desc), _ptr(epd), C.byref(brim), se.ctypes.data,
+                               _ptr(w_gate_up), _ptr(w_down), _ptr(h_ws), h_ws_bytes,
+                               _ptr(out_epd), _ptr(x), _ptr(w_gate_up_sh), _ptr(w_down_sh),
+                               _ptr(shared_out), _stream(stream)), "occ_expert_ffn")
+
+
+def occ_expert_up(desc, epd, brim: occ_brim, slot_expert_host, w_gate_up, h_ws, h_ws_bytes,
+                  x=None, w_gate_up_sh=None, stream=None):
+    import numpy as np
+    se = np.ascontiguousarray(slot_expert_host, dtype=np.int32)
+    _check(_lib.occ_expert_up(C.byref(desc), _ptr(epd), C.byref(brim), se.ctypes.data,
+                              _ptr(w_gate_up), _ptr(h_ws), h_ws_bytes, _ptr(x),
+                              _ptr(w_gate_up_sh), _stream(stream)), "occ_expert_up")
+
+
+def occ_expert_down(desc, brim: occ_brim, slot_expert_host, w_down, h_ws, h_ws_bytes, out_epd,
+                    w_down_sh=None, shared_out=None, stream=None):
+    import numpy as np
+    se = np.ascontiguousarray(slot_expert_host, dtype=np.int32)
+    _check(_lib.occ_expert_down(C.byref(desc), C.byref(brim), se.ctypes.data, _ptr(w_down),
+                                _ptr(h_ws), h_ws_bytes, _ptr(out_epd), _ptr(w_down_sh),
+                                _ptr(shared_out), _stream(stream)), "occ_expert_down")
+
+
+def occ_combine(desc, out_epd, brim: occ_brim, shared_out, out_sfd, y, stream=None):
+    _check(_lib.occ_combine(C.byref(desc), _ptr(out_epd), C.byref(brim), _ptr(shared_out),
+                            _ptr(out_sfd), _ptr(y), _stream(stream)), "occ_combine")
+
+
+def occ_coactivation(desc, topk_idx, counts, accumulate=0, stream=None):
+    _check(_lib.occ_coactivation(C.byref(desc), _ptr(topk_idx), _ptr(counts), int(accumulate),
+                                 _stream(stream)), "occ_coactivation")
+
+
+def occ_place_greedy(E: int, D: int, counts_host):
+    """Host greedy placement: returns slot_expert (numpy int32 [E])."""
+    import numpy as np
+    c = np.ascontiguousarray(counts_host, dtype=np.int32)
+    out = np.empty(E, dtype=np.int32)
+    _check(_lib.occ_place_greedy(E, D, c.ctypes.data, out.ctypes.data), "occ_place_greedy")
+    return out
+
+
+from .layer import MoELayer  # noqa: E402  (buffers + the call sequence)
+
+__all__ = ["MoELayer", "OccError", "occ_layer_desc", "occ_brim", "make_desc", "desc_of",
+           "make_brim", "occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk",
+           "occ_build_brim", "occ_dispatch", "occ_expert_ffn", "occ_expert_up",
+           "occ_expert_down", "occ_combine", "occ_coactivation", "occ_place_greedy",
+           "last_error"]

@@ -1,0 +1,309 @@
+// Host side of the C ABI: argument validation, error reporting and launch
+// sequencing.  Nothing here reads device memory or synchronises; every
+// check happens before the first launch of a call.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+#include <string>
+#include <vector>
+
+#include "occ.h"
+#include "occ_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+occ_status fail(occ_status code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+occ_status ok() {
+  g_err.clear();
+  return OCC_OK;
+}
+
+occ_status hip_status(hipError_t e, const char *where) {
+  if (e == hipSuccess) return ok();
+  return fail(OCC_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+int64_t elem_bytes(const occ_layer_desc &L) { return L.dtype == OCC_F32 ? 4 : 2; }
+int64_t s_max(const occ_layer_desc &L) { return (int64_t)L.T * (L.k < L.D ? L.k : L.D); }
+
+// A buffer of n > 0 elements must be set; an empty one may be NULL.
+bool missing(const void *p, int64_t n) { return n > 0 && p == nullptr; }
+
+// Shape checks shared by every call.
+occ_status check_desc(const occ_layer_desc *p) {
+  if (p == nullptr) return fail(OCC_EINVAL, "layer descriptor is NULL");
+  const occ_layer_desc &L = *p;
+  if (L.T < 0 || L.d <= 0 || L.E <= 0 || L.k <= 0 || L.D <= 0 || L.I <= 0)
+    return fail(OCC_EINVAL, "bad shape: T=%d d=%d E=%d k=%d D=%d I=%d", L.T, L.d, L.E, L.k, L.D,
+                L.I);
+  if (L.dtype != OCC_F32 && L.dtype != OCC_BF16)
+    return fail(OCC_EINVAL, "dtype %d is neither OCC_F32 nor OCC_BF16", L.dtype);
+  if (L.renorm != 0 && L.renorm != 1) return fail(OCC_EINVAL, "renorm must be 0 or 1");
+  if (L.k > L.E) return fail(OCC_EINVAL, "k=%d exceeds E=%d", L.k, L.E);
+  if (L.E % L.D != 0) return fail(OCC_EINVAL, "E=%d is not a multiple of D=%d", L.E, L.D);
+  if (L.n_shared < 0 || L.I_shared < 0 || (L.n_shared > 0 && L.I_shared <= 0))
+    return fail(OCC_EINVAL, "bad shared experts: n_shared=%d I_shared=%d", L.n_shared,
+                L.I_shared);
+  if (L.E > OCC_MAX_E) return fail(OCC_EUNSUP, "E=%d > %d", L.E, OCC_MAX_E);
+  if (L.k > OCC_MAX_K) return fail(OCC_EUNSUP, "k=%d > %d", L.k, OCC_MAX_K);
+  if (L.D > OCC_MAX_D) return fail(OCC_EUNSUP, "D=%d > %d", L.D, OCC_MAX_D);
+  if ((int64_t)L.T * L.k > INT32_MAX || (int64_t)L.T * L.E > INT32_MAX)
+    return fail(OCC_EUNSUP, "T=%d too large for 32-bit row indices", L.T);
+  if (L.d % 8 != 0) return fail(OCC_EUNSUP, "d=%d is not a multiple of 8", L.d);
+  if (L.d * elem_bytes(L) > 8192)
+    return fail(OCC_EUNSUP, "rows of %lld bytes exceed 8192", (long long)(L.d * elem_bytes(L)));
+  if (L.dtype == OCC_BF16 && (L.d % 64 != 0 || L.I % 64 != 0 || L.I_shared % 64 != 0))
+    return fail(OCC_EUNSUP, "bf16 expert GEMMs need d, I, I_shared multiples of 64");
+  return OCC_OK;
+}
+
+occ_status check_brim(const occ_layer_desc &L, const occ_brim *b, bool need_all) {
+  if (b == nullptr) return fail(OCC_EINVAL, "brim is NULL");
+  const int64_t R = (int64_t)L.T * L.k, Sm = s_max(L);
+  if (missing(b->brim0, (int64_t)L.D * L.T) || missing(b->brim1, (int64_t)(L.E / L.D) * Sm) ||
+      !b->slot_offset)
+    return fail(OCC_EINVAL, "brim0, brim1 and slot_offset must be set");
+  if (need_all && (!b->sfd_offset || missing(b->sfd_token, Sm) || missing(b->epd_token, R) ||
+                   missing(b->epd_sfd, R) || missing(b->epd_w, R) || !b->S))
+    return fail(OCC_EINVAL, "every occ_brim array must be set");
+  return OCC_OK;
+}
+
+occ_status make_placement(const occ_layer_desc &L, const int32_t *slot_expert_host,
+                          occ::Placement &pl) {
+  if (slot_expert_host == nullptr) return fail(OCC_EINVAL, "slot_expert_host is NULL");
+  for (int i = 0; i < OCC_MAX_E; ++i) pl.expert_at[i] = pl.slot_of[i] = -1;
+  for (int g = 0; g < L.E; ++g) {
+    const int e = slot_expert_host[g];
+    if (e < 0 || e >= L.E || pl.slot_of[e] != -1)
+      return fail(OCC_EINVAL, "slot_expert is not a permutation of 0..%d (slot %d -> %d)",
+                  L.E - 1, g, e);
+    pl.expert_at[g] = e;
+    pl.slot_of[e] = g;
+  }
+  return OCC_OK;
+}
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t h_bytes(const occ_layer_desc &L) {
+  return align256((size_t)L.T * L.k * L.I * elem_bytes(L));
+}
+size_t h_sh_bytes(const occ_layer_desc &L) {
+  return (size_t)L.T * L.n_shared * L.I_shared * elem_bytes(L);
+}
+
+#define OCC_TRY(expr)                \
+  do {                               \
+    const occ_status s_ = (expr);    \
+    if (s_ != OCC_OK) return s_;     \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *occ_last_error(void) { return g_err.c_str(); }
+
+size_t occ_workspace_bytes(const occ_layer_desc *desc) {
+  if (check_desc(desc) != OCC_OK) return 0;
+  return occ::brim_workspace_bytes(desc->T, desc->D, desc->E);
+}
+
+size_t occ_ffn_workspace_bytes(const occ_layer_desc *desc) {
+  if (check_desc(desc) != OCC_OK) return 0;
+  return h_bytes(*desc) + h_sh_bytes(*desc);
+}
+
+occ_status occ_route_topk(const occ_layer_desc *desc, const void *x, const void *w_router,
+                          int32_t *topk_idx, float *topk_w, float *logits, hipStream_t stream) {
+  OCC_TRY(check_desc(desc));
+  const int64_t Td = (int64_t)desc->T * desc->d, Tk = (int64_t)desc->T * desc->k;
+  if (missing(x, Td) || !w_router || missing(topk_idx, Tk) || missing(topk_w, Tk))
+    return fail(OCC_EINVAL, "x, w_router, topk_idx and topk_w must be set");
+  return hip_status(occ::launch_route_topk(*desc, x, w_router, topk_idx, topk_w, logits, stream),
+                    "occ_route_topk");
+}
+
+occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *topk_idx,
+                          const float *topk_w, const int32_t *slot_expert_host,
+                          const occ_brim *brim, void *ws, size_t ws_bytes, hipStream_t stream) {
+  OCC_TRY(check_desc(desc));
+  OCC_TRY(check_brim(*desc, brim, true));
+  const int64_t Tk = (int64_t)desc->T * desc->k;
+  if (missing(topk_idx, Tk) || missing(topk_w, Tk))
+    return fail(OCC_EINVAL, "topk_idx and topk_w must be set");
+  occ::Placement pl;
+  OCC_TRY(make_placement(*desc, slot_expert_host, pl));
+  const size_t need = occ::brim_workspace_bytes(desc->T, desc->D, desc->E);
+  if (ws == nullptr) return fail(OCC_EINVAL, "workspace is NULL");
+  if (ws_bytes < need)
+    return fail(OCC_ENOSPC, "workspace of %zu bytes < %zu required", ws_bytes, need);
+  return hip_status(occ::launch_build_brim(*desc, topk_idx, topk_w, pl, *brim, ws, stream),
+                    "occ_build_brim");
+}
+
+occ_status occ_dispatch(const occ_layer_desc *desc, const void *x, const occ_brim *brim,
+                        void *sfd, void *epd, hipStream_t stream) {
+  OCC_TRY(check_desc(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const int64_t Td = (int64_t)desc->T * desc->d;
+  if (missing(x, Td) || missing(sfd, s_max(*desc)) || missing(epd, Td * desc->k))
+    return fail(OCC_EINVAL, "x, sfd and epd must be set");
+  return hip_status(occ::launch_dispatch(*desc, x, *brim, sfd, epd, stream), "occ_dispatch");
+}
+
+// Shared-expert pointers: all set when n_shared > 0, all NULL otherwise.
+static occ_status check_shared_args(const occ_layer_desc &L, std::initializer_list<const void *> ps,
+                                    const char *names) {
+  for (const void *p : ps) {
+    if (L.n_shared > 0 && p == nullptr) return fail(OCC_EINVAL, "n_shared > 0 needs %s", names);
+    if (L.n_shared == 0 && p != nullptr)
+      return fail(OCC_EINVAL, "n_shared == 0 but %s given", names);
+  }
+  return OCC_OK;
+}
+
+occ_status occ_expert_up(const occ_layer_desc *desc, const void *epd, const occ_brim *brim,
+                         const int32_t *slot_expert_host, const void *w_gate_up, void *h_ws,
+                         size_t h_ws_bytes, const void *x, const void *w_gate_up_sh,
+                         hipStream_t stream) {
+  OCC_TRY(check_desc(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const occ_layer_desc &L = *desc;
+  const int64_t Rd = (int64_t)L.T * L.k * L.d;
+  if (missing(epd, Rd) || !w_gate_up || missing(h_ws, (int64_t)(h_bytes(L) + h_sh_bytes(L))))
+    return fail(OCC_EINVAL, "epd, w_gate_up and h_ws must be set");
+  OCC_TRY(check_shared_args(L, {x, w_gate_up_sh}, "x and w_gate_up_sh"));
+  if (h_ws_bytes < h_bytes(L) + h_sh_bytes(L))
+    return fail(OCC_ENOSPC, "h workspace of %zu bytes < %zu required", h_ws_bytes,
+                h_bytes(L) + h_sh_bytes(L));
+  occ::Placement pl;
+  OCC_TRY(make_placement(L, slot_expert_host, pl));
+  char *h = static_cast<char *>(h_ws);
+  return hip_status(occ::launch_expert_up(L, epd, brim->slot_offset, pl, w_gate_up, h, x,
+                                          w_gate_up_sh, h + h_bytes(L), stream),
+                    "occ_expert_up");
+}
+
+occ_status occ_expert_down(const occ_layer_desc *desc, const occ_brim *brim,
+                           const int32_t *slot_expert_host, const void *w_down,
+                           const void *h_ws, size_t h_ws_bytes, void *out_epd,
+                           const void *w_down_sh, void *shared_out, hipStream_t stream) {
+  OCC_TRY(check_desc(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const occ_layer_desc &L = *desc;
+  const int64_t Rd = (int64_t)L.T * L.k * L.d;
+  if (!w_down || missing(h_ws, (int64_t)(h_bytes(L) + h_sh_bytes(L))) || missing(out_epd, Rd))
+    return fail(OCC_EINVAL, "w_down, h_ws and out_epd must be set");
+  OCC_TRY(check_shared_args(L, {w_down_sh, shared_out}, "w_down_sh and shared_out"));
+  if (h_ws_bytes < h_bytes(L) + h_sh_bytes(L))
+    return fail(OCC_ENOSPC, "h workspace of %zu bytes < %zu required", h_ws_bytes,
+                h_bytes(L) + h_sh_bytes(L));
+  occ::Placement pl;
+  OCC_TRY(make_placement(L, slot_expert_host, pl));
+  const char *h = static_cast<const char *>(h_ws);
+  return hip_status(occ::launch_expert_down(L, brim->slot_offset, pl, w_down, h, out_epd,
+                                            w_down_sh, h + h_bytes(L), shared_out, stream),
+                    "occ_expert_down");
+}
+
+occ_status occ_expert_ffn(const occ_layer_desc *desc, const void *epd, const occ_brim *brim,
+                          const int32_t *slot_expert_host, const void *w_gate_up,
+                          const void *w_down, void *h_ws, size_t h_ws_bytes, void *out_epd,
+                          const void *x, const void *w_gate_up_sh, const void *w_down_sh,
+                          void *shared_out, hipStream_t stream) {
+  // validate both halves before launching either
+  OCC_TRY(check_desc(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const occ_layer_desc &L = *desc;
+  const int64_t Rd = (int64_t)L.T * L.k * L.d;
+  if (missing(epd, Rd) || !w_gate_up || !w_down ||
+      missing(h_ws, (int64_t)(h_bytes(L) + h_sh_bytes(L))) || missing(out_epd, Rd))
+    return fail(OCC_EINVAL, "epd, w_gate_up, w_down, h_ws and out_epd must be set");
+  OCC_TRY(check_shared_args(L, {x, w_gate_up_sh, w_down_sh, shared_out},
+                            "x, w_gate_up_sh, w_down_sh and shared_out"));
+  if (h_ws_bytes < h_bytes(L) + h_sh_bytes(L))
+    return fail(OCC_ENOSPC, "h workspace of %zu bytes < %zu required", h_ws_bytes,
+                h_bytes(L) + h_sh_bytes(L));
+  occ::Placement pl;
+  OCC_TRY(make_placement(L, slot_expert_host, pl));
+  char *h = static_cast<char *>(h_ws);
+  hipError_t e = occ::launch_expert_up(L, epd, brim->slot_offset, pl, w_gate_up, h, x,
+                                       w_gate_up_sh, h + h_bytes(L), stream);
+  if (e != hipSuccess) return hip_status(e, "occ_expert_ffn (up)");
+  return hip_status(occ::launch_expert_down(L, brim->slot_offset, pl, w_down, h, out_epd,
+                                            w_down_sh, h + h_bytes(L), shared_out, stream),
+                    "occ_expert_ffn (down)");
+}
+
+occ_status occ_combine(const occ_layer_desc *desc, const void *out_epd, const occ_brim *brim,
+                       const void *shared_out, void *out_sfd, void *y, hipStream_t stream) {
+  OCC_TRY(check_desc(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const int64_t Td = (int64_t)desc->T * desc->d;
+  if (missing(brim->epd_w, (int64_t)desc->T * desc->k))
+    return fail(OCC_EINVAL, "brim->epd_w must be set");
+  if (missing(out_epd, Td * desc->k) || missing(out_sfd, s_max(*desc)) || missing(y, Td))
+    return fail(OCC_EINVAL, "out_epd, out_sfd and y must be set");
+  return hip_status(occ::launch_combine(*desc, out_epd, *brim, shared_out, out_sfd, y, stream),
+                    "occ_combine");
+}
+
+occ_status occ_coactivation(const occ_layer_desc *desc, const int32_t *topk_idx,
+                            int32_t *counts, int32_t accumulate, hipStream_t stream) {
+  OCC_TRY(check_desc(desc));
+  if (missing(topk_idx, (int64_t)desc->T * desc->k) || !counts)
+    return fail(OCC_EINVAL, "topk_idx and counts must be set");
+  if (accumulate != 0 && accumulate != 1) return fail(OCC_EINVAL, "accumulate must be 0 or 1");
+  return hip_status(occ::launch_coactivation(*desc, topk_idx, counts, accumulate, stream),
+                    "occ_coactivation");
+}
+
+occ_status occ_place_greedy(int32_t E, int32_t D, const int32_t *counts_host,
+                            int32_t *slot_expert_host) {
+  if (E <= 0 || D <= 0 || E % D != 0) return fail(OCC_EINVAL, "bad E=%d D=%d", E, D);
+  if (!counts_host || !slot_expert_host) return fail(OCC_EINVAL, "NULL counts or output");
+  const int L = E / D;
+  std::vector<char> placed(E, 0);
+  std::vector<int64_t> affinity(E);
+  auto n_of = [&](int e) { return counts_host[(size_t)e * E + e]; };
+  for (int dv = 0; dv < D; ++dv) {
+    // seed: most tokens, lower index on ties
+    int seed = -1;
+    for (int e = 0; e < E; ++e)
+      if (!placed[e] && (seed < 0 || n_of(e) > n_of(seed))) seed = e;
+    placed[seed] = 1;
+    slot_expert_host[dv * L] = seed;
+    for (int e = 0; e < E; ++e) affinity[e] = counts_host[(size_t)e * E + seed];
+    for (int l = 1; l < L; ++l) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (placed[e]) continue;
+        if (best < 0 || affinity[e] > affinity[best] ||
+            (affinity[e] == affinity[best] && n_of(e) > n_of(best)))
+          best = e;
+      }
+      placed[best] = 1;
+      slot_expert_host[dv * L + l] = best;
+      for (int e = 0; e < E; ++e) affinity[e] += counts_host[(size_t)e * E + best];
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,426 @@
+// Grouped expert GEMMs on the EPD layout.
+//
+// Expert Coupling in MoE Pretraining, Abstract: tokens are dispatched to
+// "expert networks"; Occult, Figure 4 caption: expert computing runs on the
+// EPD state.  The experts are SwiGLU FFNs without biases:
+//   up:   h   = silu(A W_gate^T) * (A W_up^T)    (SwiGLU fused in the epilogue)
+//   down: out = h W_down^T
+// EPD rows of slot g are contiguous ([slot_offset[g], slot_offset[g+1])), so
+// each slot is one dense GEMM with a data-dependent row count: the grid is
+// sized for the worst case and each block decodes its (slot, n-tile, m-tile)
+// from slot_offset on the device, so no host synchronisation is needed.
+//
+// bf16: 256 threads = 2 x 2 waves, block tile BM x BN x 64, wave tile
+// (BM/2) x (BN/2) of v_mfma_f32_16x16x32_bf16, fp32 accumulators.  Global
+// tiles go through registers into double-buffered, padded LDS (row stride 72
+// elements = 144 bytes, so the 16 rows read by one MFMA operand load fall in
+// distinct banks); one barrier per k-step.  The output tile is staged in LDS
+// and written with 16-byte row stores.
+// Tile order: slot-major, then n-tile, m-tile fastest, with block ids
+// remapped so that each XCD (blocks are dealt round-robin to the 8 XCDs)
+// works on a contiguous range of tiles: the m-tiles of one slot that share a
+// weight panel run together and share that XCD's L2.
+#include "occ_internal.h"
+
+namespace occ {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct GemmArgs {
+  const int32_t *row_offset;  // [G+1] on the device (slots); nullptr: one dense group
+  int G;
+  int dense_rows;
+  const void *A;
+  int64_t lda;
+  const void *B;
+  int64_t ldb;
+  int64_t b_group_stride;  // elements between the weights of consecutive experts
+  int64_t up_offset;       // SwiGLU: elements from a gate row to its up row
+  int nseg;                // output columns per weight segment
+  int64_t nseg_stride;     // elements between weight segments along the output
+  int kseg;                // K per weight segment
+  int64_t kseg_stride;     // elements between weight segments along K
+  int K;
+  int N;                   // output columns
+  void *C;
+  int64_t ldc;
+  int32_t expert_of_group[OCC_MAX_E];
+};
+
+constexpr int kThreads = 256;
+constexpr int kBK = 64;
+constexpr int kLdsK = kBK + 8;
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Wave 0 writes cumulative m-tile counts of the groups into ts[0..G].
+__device__ __forceinline__ void group_tile_scan(const int32_t *row_offset, int G, int BM,
+                                                int32_t *ts) {
+  const int lane = threadIdx.x;
+  int carry = 0;
+  if (lane == 0) ts[0] = 0;
+  for (int g0 = 0; g0 < G; g0 += kWave) {
+    const int g = g0 + lane;
+    int v = 0;
+    if (g < G) v = (row_offset[g + 1] - row_offset[g] + BM - 1) / BM;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int u = __shfl_up(v, off);
+      if (lane >= off) v += u;
+    }
+    if (g < G) ts[g + 1] = carry + v;
+    carry += __shfl(v, kWave - 1);
+  }
+}
+
+struct TileCoord {
+  int group, row_begin, rows, n0;
+};
+
+// Decodes this block's tile; returns false for blocks beyond the last tile.
+template <int BM, int BNO>
+__device__ __forceinline__ bool decode_tile(const GemmArgs &a, int32_t *ts, TileCoord &tc) {
+  const int ntn = (a.N + BNO - 1) / BNO;
+  int total_mt;
+  if (a.row_offset != nullptr) {
+    if (threadIdx.x < kWave) group_tile_scan(a.row_offset, a.G, BM, ts);
+    __syncthreads();
+    total_mt = ts[a.G];
+  } else {
+    total_mt = (a.dense_rows + BM - 1) / BM;
+  }
+  const int ntiles = total_mt * ntn;
+  const int bid = blockIdx.x;
+  if (bid >= ntiles) return false;
+  // XCD-aware remap: the blocks of XCD x (bid % 8 == x) take a contiguous range
+  const int xcd = bid % kXcds;
+  const int logical = xcd * (ntiles / kXcds) + min(xcd, ntiles % kXcds) + bid / kXcds;
+  if (a.row_offset != nullptr) {
+    int lo = 0, hi = a.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ts[mid] * ntn <= logical) lo = mid;
+      else hi = mid - 1;
+    }
+    const int mtg = ts[lo + 1] - ts[lo];
+    const int local = logical - ts[lo] * ntn;
+    const int nt = local / mtg, mt = local - nt * mtg;
+    const int r0 = a.row_offset[lo], r1 = a.row_offset[lo + 1];
+    tc.group = lo;
+    tc.row_begin = r0 + mt * BM;
+    tc.rows = min(BM, r1 - tc.row_begin);
+    tc.n0 = nt * BNO;
+  } else {
+    const int nt = logical / total_mt, mt = logical - nt * total_mt;
+    tc.group = 0;
+    tc.row_begin = mt * BM;
+    tc.rows = min(BM, a.dense_rows - tc.row_begin);
+    tc.n0 = nt * BNO;
+  }
+  return true;
+}
+
+template <int BM, int BN, bool SWIGLU>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int MI = WM / 16, NI = WN / 16;
+  constexpr int BNO = SWIGLU ? BN / 2 : BN;  // output columns per tile
+  constexpr int A_CH = BM * (kBK / 8) / kThreads;  // 16-byte chunks per thread
+  constexpr int B_CH = BN * (kBK / 8) / kThreads;
+  constexpr int STAGE = (BM + BN) * kLdsK;          // elements per LDS stage
+  constexpr int CLD = BNO + 8;                      // staged output row stride
+  static_assert(BM * CLD <= 2 * STAGE, "output staging must fit in the tile buffers");
+  static_assert(!SWIGLU || NI % 2 == 0, "gate and up halves");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ int32_t ts[OCC_MAX_E + 1];
+
+  TileCoord tc;
+  if (!decode_tile<BM, BNO>(a, ts, tc)) return;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int expert = a.expert_of_group[tc.group];
+  const uint16_t *Ab = static_cast<const uint16_t *>(a.A) + (int64_t)tc.row_begin * a.lda;
+  const int nsg = tc.n0 / a.nseg;
+  const uint16_t *Bb = static_cast<const uint16_t *>(a.B) + (int64_t)expert * a.b_group_stride +
+                       (int64_t)nsg * a.nseg_stride + (int64_t)(tc.n0 - nsg * a.nseg) * a.ldb;
+
+  // per-thread global source rows (clamped inside the tile, never out of bounds)
+  const uint16_t *a_src[A_CH];
+  const uint16_t *b_src[B_CH];
+  int a_dst[A_CH], b_dst[B_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int c = tid + kThreads * i, r = c >> 3, cc = c & 7;
+    a_src[i] = Ab + (int64_t)min(r, tc.rows - 1) * a.lda + cc * 8;
+    a_dst[i] = r * kLdsK + cc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int c = tid + kThreads * i, r = c >> 3, cc = c & 7;
+    int64_t off;
+    if (SWIGLU) {
+      const int rr = r < BN / 2 ? r : r - BN / 2;
+      const int re = min(rr, a.N - 1 - tc.n0);
+      off = (int64_t)re * a.ldb + (r < BN / 2 ? 0 : a.up_offset);
+    } else {
+      off = (int64_t)min(r, a.N - 1 - tc.n0) * a.ldb;
+    }
+    b_src[i] = Bb + off + cc * 8;
+    b_dst[i] = BM * kLdsK + r * kLdsK + cc * 8;
+  }
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  u32x4 ra[A_CH], rb[B_CH];
+#define OCC_LOAD_REGS(kt_)                                                          \
+  do {                                                                              \
+    const int k0_ = (kt_) * kBK;                                                    \
+    const int ks_ = k0_ / a.kseg;                                                   \
+    const int64_t bk_ = (int64_t)ks_ * a.kseg_stride + (k0_ - ks_ * a.kseg);        \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) ra[i] =                        \
+        *reinterpret_cast<const u32x4 *>(a_src[i] + k0_);                           \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) rb[i] =                        \
+        *reinterpret_cast<const u32x4 *>(b_src[i] + bk_);                           \
+  } while (0)
+#define OCC_STORE_LDS(buf_)                                                         \
+  do {                                                                              \
+    uint16_t *s_ = smem + (buf_) * STAGE;                                           \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                \
+        *reinterpret_cast<u32x4 *>(s_ + a_dst[i]) = ra[i];                          \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                \
+        *reinterpret_cast<u32x4 *>(s_ + b_dst[i]) = rb[i];                          \
+  } while (0)
+
+  int brow[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    if (SWIGLU)
+      brow[ni] = ni < NI / 2 ? wn * (WN / 2) + ni * 16 : BN / 2 + wn * (WN / 2) + (ni - NI / 2) * 16;
+    else
+      brow[ni] = wn * WN + ni * 16;
+  }
+
+  const int nk = a.K / kBK;
+  OCC_LOAD_REGS(0);
+  OCC_STORE_LDS(0);
+  __syncthreads();
+  const int frag_r = lane & 15, frag_k = (lane >> 4) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) OCC_LOAD_REGS(kt + 1);
+    const uint16_t *As = smem + cur * STAGE;
+    const uint16_t *Bs = As + BM * kLdsK;
+#pragma unroll
+    for (int ks = 0; ks < kBK; ks += 32) {
+      bf16x8 af[MI], bfr[NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        af[mi] = *reinterpret_cast<const bf16x8 *>(As + (wm * WM + mi * 16 + frag_r) * kLdsK + ks +
+                                                   frag_k);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        bfr[ni] =
+            *reinterpret_cast<const bf16x8 *>(Bs + (brow[ni] + frag_r) * kLdsK + ks + frag_k);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (kt + 1 < nk) OCC_STORE_LDS(cur ^ 1);
+    __syncthreads();
+  }
+#undef OCC_LOAD_REGS
+#undef OCC_STORE_LDS
+
+  // ---- epilogue: (SwiGLU), round to bf16, stage, coalesced row stores -----
+  uint16_t *Cs = smem;
+  const int orow = (lane >> 4) * 4, ocol = lane & 15;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < (SWIGLU ? NI / 2 : NI); ++ni) {
+      const int col = SWIGLU ? wn * (WN / 2) + ni * 16 + ocol : wn * WN + ni * 16 + ocol;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * WM + mi * 16 + orow + i;
+        float v;
+        if (SWIGLU) v = silu(acc[mi][ni][i]) * acc[mi][ni + NI / 2][i];
+        else v = acc[mi][ni][i];
+        Cs[row * CLD + col] = f32_to_bf16(v);
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int RCH = BNO / 8;  // 16-byte chunks per output row
+  uint16_t *Cg = static_cast<uint16_t *>(a.C) + (int64_t)tc.row_begin * a.ldc + tc.n0;
+  for (int c = tid; c < BM * RCH; c += kThreads) {
+    const int r = c / RCH, cc = c - r * RCH;
+    if (r < tc.rows && tc.n0 + cc * 8 < a.N)
+      *reinterpret_cast<u32x4 *>(Cg + (int64_t)r * a.ldc + cc * 8) =
+          *reinterpret_cast<const u32x4 *>(Cs + r * CLD + cc * 8);
+  }
+}
+
+// fp32 layers: one thread per output element, fp32 FMAs in K order.
+template <bool SWIGLU>
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a, int max_rows) {
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int row = (int)(gid / a.N), col = (int)(gid % a.N);
+  if (row >= max_rows) return;
+  int g = 0;
+  if (a.row_offset != nullptr) {
+    if (row >= a.row_offset[a.G]) return;
+    int lo = 0, hi = a.G - 1;  // last group whose start is <= row
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.row_offset[mid] <= row) lo = mid;
+      else hi = mid - 1;
+    }
+    g = lo;
+  } else if (row >= a.dense_rows) {
+    return;
+  }
+  const float *A = static_cast<const float *>(a.A) + (int64_t)row * a.lda;
+  const int nsg = col / a.nseg;
+  const float *Bn = static_cast<const float *>(a.B) + (int64_t)a.expert_of_group[g] * a.b_group_stride +
+                    (int64_t)nsg * a.nseg_stride + (int64_t)(col - nsg * a.nseg) * a.ldb;
+  float s0 = 0.0f, s1 = 0.0f;
+  for (int k = 0; k < a.K; ++k) {
+    const int ks = k / a.kseg;
+    const int64_t bk = (int64_t)ks * a.kseg_stride + (k - ks * a.kseg);
+    s0 = __builtin_fmaf(A[k], Bn[bk], s0);
+    if (SWIGLU) s1 = __builtin_fmaf(A[k], Bn[a.up_offset + bk], s1);
+  }
+  const float v = SWIGLU ? silu(s0) * s1 : s0;
+  static_cast<float *>(a.C)[(int64_t)row * a.ldc + col] = v;
+}
+
+constexpr int kBM = 128, kBN = 128;
+
+template <bool SWIGLU>
+hipError_t run_gemm(const GemmArgs &a, int dtype, int max_rows, hipStream_t st) {
+  if (max_rows <= 0) return hipSuccess;
+  if (dtype == OCC_F32) {
+    const int64_t n = (int64_t)max_rows * a.N;
+    gemm_f32_kernel<SWIGLU><<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, st>>>(
+        a, max_rows);
+    return hipGetLastError();
+  }
+  constexpr int BNO = SWIGLU ? kBN / 2 : kBN;
+  // worst case over all splits of max_rows rows into G groups
+  const int64_t groups = a.row_offset != nullptr ? a.G : 1;
+  const int64_t mt = (max_rows + groups * (kBM - 1)) / kBM;
+  const int64_t grid = mt * ((a.N + BNO - 1) / BNO);
+  gemm_bf16_kernel<kBM, kBN, SWIGLU><<<(unsigned)grid, kThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+GemmArgs base_args(const Placement &pl) {
+  GemmArgs a{};
+  for (int g = 0; g < OCC_MAX_E; ++g) a.expert_of_group[g] = pl.expert_at[g];
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_expert_up(const occ_layer_desc &L, const void *epd, const int32_t *slot_offset,
+                            const Placement &pl, const void *w_gate_up, void *h, const void *x,
+                            const void *w_gate_up_sh, void *h_sh, hipStream_t st) {
+  const int64_t d = L.d, I = L.I;
+  GemmArgs a = base_args(pl);
+  a.row_offset = slot_offset;
+  a.G = L.E;
+  a.A = epd;
+  a.lda = d;
+  a.B = w_gate_up;
+  a.ldb = d;
+  a.b_group_stride = 2 * I * d;
+  a.up_offset = I * d;
+  a.nseg = (int)I;
+  a.nseg_stride = 0;
+  a.kseg = (int)d;
+  a.kseg_stride = 0;
+  a.K = (int)d;
+  a.N = (int)I;
+  a.C = h;
+  a.ldc = I;
+  hipError_t err = run_gemm<true>(a, L.dtype, L.T * L.k, st);
+  if (err != hipSuccess || L.n_shared == 0) return err;
+  const int64_t Is = L.I_shared;
+  GemmArgs s{};
+  s.row_offset = nullptr;
+  s.G = 1;
+  s.dense_rows = L.T;
+  s.A = x;
+  s.lda = d;
+  s.B = w_gate_up_sh;
+  s.ldb = d;
+  s.b_group_stride = 0;
+  s.up_offset = Is * d;
+  s.nseg = (int)Is;
+  s.nseg_stride = 2 * Is * d;
+  s.kseg = (int)d;
+  s.kseg_stride = 0;
+  s.K = (int)d;
+  s.N = (int)(L.n_shared * Is);
+  s.C = h_sh;
+  s.ldc = L.n_shared * Is;
+  return run_gemm<true>(s, L.dtype, L.T, st);
+}
+
+hipError_t launch_expert_down(const occ_layer_desc &L, const int32_t *slot_offset,
+                              const Placement &pl, const void *w_down, const void *h,
+                              void *out_epd, const void *w_down_sh, const void *h_sh,
+                              void *shared_out, hipStream_t st) {
+  const int64_t d = L.d, I = L.I;
+  GemmArgs a = base_args(pl);
+  a.row_offset = slot_offset;
+  a.G = L.E;
+  a.A = h;
+  a.lda = I;
+  a.B = w_down;
+  a.ldb = I;
+  a.b_group_stride = d * I;
+  a.up_offset = 0;
+  a.nseg = (int)d;
+  a.nseg_stride = 0;
+  a.kseg = (int)I;
+  a.kseg_stride = 0;
+  a.K = (int)I;
+  a.N = (int)d;
+  a.C = out_epd;
+  a.ldc = d;
+  hipError_t err = run_gemm<false>(a, L.dtype, L.T * L.k, st);
+  if (err != hipSuccess || L.n_shared == 0) return err;
+  const int64_t Is = L.I_shared;
+  GemmArgs s{};
+  s.row_offset = nullptr;
+  s.G = 1;
+  s.dense_rows = L.T;
+  s.A = h_sh;
+  s.lda = L.n_shared * Is;
+  s.B = w_down_sh;
+  s.ldb = Is;
+  s.b_group_stride = 0;
+  s.up_offset = 0;
+  s.nseg = (int)d;
+  s.nseg_stride = 0;
+  s.kseg = (int)Is;
+  s.kseg_stride = d * Is;
+  s.K = (int)(L.n_shared * Is);
+  s.N = (int)d;
+  s.C = shared_out;
+  s.ldc = d;
+  return run_gemm<false>(s, L.dtype, L.T, st);
+}
+
+}  // namespace occ

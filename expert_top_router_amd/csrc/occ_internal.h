@@ -1,0 +1,86 @@
+// Internal declarations shared by the HIP sources of liboccult (not part of
+// the C ABI).  gfx950 only: wave64, 160 KB LDS per CU, 256 CUs in 8 XCDs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "occ.h"
+
+namespace occ {
+
+constexpr int kWave = 64;
+
+// Native 16-byte vector (HIP's uint4 is a union wrapper that can keep
+// register arrays of it in scratch).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kXcds = 8;
+
+// Placement passed by value to kernels, so it needs no device copy:
+// slot g = dv * L + l holds expert expert_at[g]; slot_of is its inverse.
+struct Placement {
+  int32_t expert_at[OCC_MAX_E];
+  int32_t slot_of[OCC_MAX_E];
+};
+
+// ---- element conversions --------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// Round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <int DT> struct Elem;
+template <> struct Elem<OCC_F32> {
+  using T = float;
+  static __device__ __forceinline__ float load(const T *p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ T from_f32(float v) { return v; }
+  static __device__ __forceinline__ float to_f32(T v) { return v; }
+};
+template <> struct Elem<OCC_BF16> {
+  using T = uint16_t;
+  static __device__ __forceinline__ float load(const T *p, size_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ T from_f32(float v) { return f32_to_bf16(v); }
+  static __device__ __forceinline__ float to_f32(T v) { return bf16_to_f32(v); }
+};
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & (kWave - 1);
+  return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+}
+
+// ---- launchers (each returns hipGetLastError() of its launches) -----------
+hipError_t launch_route_topk(const occ_layer_desc &L, const void *x, const void *wr,
+                             int32_t *idx, float *w, float *logits, hipStream_t st);
+
+// workspace layout of the BRIM build: counts then scanned offsets
+size_t brim_workspace_bytes(int T, int D, int E);
+hipError_t launch_build_brim(const occ_layer_desc &L, const int32_t *idx, const float *w,
+                             const Placement &pl, const occ_brim &b, void *ws, hipStream_t st);
+
+hipError_t launch_dispatch(const occ_layer_desc &L, const void *x, const occ_brim &b, void *sfd,
+                           void *epd, hipStream_t st);
+
+hipError_t launch_combine(const occ_layer_desc &L, const void *out_epd, const occ_brim &b,
+                          const void *shared_out, void *out_sfd, void *y, hipStream_t st);
+
+hipError_t launch_coactivation(const occ_layer_desc &L, const int32_t *idx, int32_t *counts,
+                               int accumulate, hipStream_t st);
+
+// Expert GEMMs.  up: h = swiglu(A W_gu^T); down: out = h W_dn^T.
+hipError_t launch_expert_up(const occ_layer_desc &L, const void *epd, const int32_t *slot_offset,
+                            const Placement &pl, const void *w_gate_up, void *h,
+                            const void *x, const void *w_gate_up_sh, void *h_sh,
+                            hipStream_t st);
+hipError_t launch_expert_down(const occ_layer_desc &L, const int32_t *slot_offset,
+                              const Placement &pl, const void *w_down, const void *h,
+                              void *out_epd, const void *w_down_sh, const void *h_sh,
+                              void *shared_out, hipStream_t st);
+
+}  // namespace occ

@@ -1,0 +1,265 @@
+// Dispatch (ORI -> SFD -> EPD) and combine (EPD -> SFD -> ORI).
+//
+// Occult, Figure 4 caption: token tensors ORI, SFD and EPD are stored
+// compactly on HBM and the all-to-all and expert computing are guided by the
+// BRIMs in both directions.  One wave owns one ORI token:
+//   dispatch: read x[t] once into registers, write it to each of its SFD rows
+//             (BRIM_0 column t) and each of its EPD rows (BRIM_1 columns of
+//             those SFD rows);
+//   combine:  for each of its devices (ascending) sum w * out_EPD over the
+//             device's experts (local index ascending) in fp32, store that
+//             pre-reduced row to out_SFD (the return payload) and add it, as
+//             stored, into y[t].
+// Index lookups are lane-parallel: lane p of a pass holds pair (device
+// p / L, local expert p % L); ballots then walk the present rows in
+// ascending (device, local) order.  Rows move as 16-byte per-lane chunks,
+// 1 KiB per wave instruction, so every row access is fully coalesced.
+#include "occ_internal.h"
+
+namespace occ {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTokPerBlock = kThreads / kWave;
+
+template <int NCH>
+__global__ __launch_bounds__(kThreads) void dispatch_kernel(
+    int T, int D, int L, int ld, int row16, const u32x4 *__restrict__ x,
+    const int32_t *__restrict__ brim0, const int32_t *__restrict__ brim1,
+    u32x4 *__restrict__ sfd, u32x4 *__restrict__ epd) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * kTokPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;  // whole wave leaves together
+  u32x4 v[NCH];
+  const u32x4 *src = x + (size_t)t * row16;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i = lane + kWave * c;
+    if (i < row16) v[c] = src[i];
+  }
+  const int npairs = D * L;
+  for (int p0 = 0; p0 < npairs; p0 += kWave) {
+    const int p = p0 + lane;
+    int32_t s = -1, r = -1;
+    bool first = false;
+    if (p < npairs) {
+      const int dv = p / L, l = p - dv * L;
+      s = brim0[(size_t)dv * T + t];
+      first = l == 0;
+      if (s >= 0) r = brim1[(size_t)l * ld + s];
+    }
+    uint64_t ms = __ballot(first && s >= 0);
+    uint64_t mr = __ballot(r >= 0);
+    while (ms) {
+      const int b = __ffsll((long long)ms) - 1;
+      ms &= ms - 1;
+      const int32_t row = __builtin_amdgcn_readlane(s, b);
+      u32x4 *dst = sfd + (size_t)row * row16;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int i = lane + kWave * c;
+        if (i < row16) dst[i] = v[c];
+      }
+    }
+    while (mr) {
+      const int b = __ffsll((long long)mr) - 1;
+      mr &= mr - 1;
+      const int32_t row = __builtin_amdgcn_readlane(r, b);
+      u32x4 *dst = epd + (size_t)row * row16;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int i = lane + kWave * c;
+        if (i < row16) dst[i] = v[c];
+      }
+    }
+  }
+}
+
+// 16-byte chunk <-> fp32 lanes
+template <int DT> struct Chunk;
+template <> struct Chunk<OCC_BF16> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void unpack(const u32x4 &u, float *f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ u32x4 pack(const float *f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+    return u32x4{w[0], w[1], w[2], w[3]};
+  }
+  // value as stored (rounded to bf16), back in fp32
+  static __device__ __forceinline__ float stored(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+};
+template <> struct Chunk<OCC_F32> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void unpack(const u32x4 &u, float *f) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+  }
+  static __device__ __forceinline__ u32x4 pack(const float *f) {
+    return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                 __float_as_uint(f[3])};
+  }
+  static __device__ __forceinline__ float stored(float f) { return f; }
+};
+
+template <int DT, int NCH>
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    int T, int D, int L, int ld, int row16, const u32x4 *__restrict__ out_epd,
+    const int32_t *__restrict__ brim0, const int32_t *__restrict__ brim1,
+    const float *__restrict__ epd_w, const u32x4 *__restrict__ shared, u32x4 *__restrict__ out_sfd,
+    u32x4 *__restrict__ y) {
+  using CK = Chunk<DT>;
+  constexpr int VE = CK::N;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * kTokPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;
+  float yacc[NCH][VE], acc[NCH][VE];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i = lane + kWave * c;
+    if (shared != nullptr && i < row16) {
+      CK::unpack(shared[(size_t)t * row16 + i], yacc[c]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < VE; ++u) yacc[c][u] = 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < VE; ++u) acc[c][u] = 0.0f;
+  }
+  int cur_dev = -1;
+  int32_t cur_s = -1;
+  auto finish_device = [&]() {
+    u32x4 *dst = out_sfd + (size_t)cur_s * row16;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int i = lane + kWave * c;
+#pragma unroll
+      for (int u = 0; u < VE; ++u) {
+        const float v = CK::stored(acc[c][u]);
+        acc[c][u] = v;
+      }
+      if (i < row16) dst[i] = CK::pack(acc[c]);
+#pragma unroll
+      for (int u = 0; u < VE; ++u) {
+        yacc[c][u] += acc[c][u];
+        acc[c][u] = 0.0f;
+      }
+    }
+  };
+  const int npairs = D * L;
+  for (int p0 = 0; p0 < npairs; p0 += kWave) {
+    const int p = p0 + lane;
+    int32_t s = -1, r = -1;
+    float wr = 0.0f;
+    if (p < npairs) {
+      const int dv = p / L, l = p - dv * L;
+      s = brim0[(size_t)dv * T + t];
+      if (s >= 0) {
+        r = brim1[(size_t)l * ld + s];
+        if (r >= 0) wr = epd_w[r];
+      }
+    }
+    uint64_t mr = __ballot(r >= 0);
+    while (mr) {
+      const int b = __ffsll((long long)mr) - 1;
+      mr &= mr - 1;
+      const int dv = (p0 + b) / L;
+      if (dv != cur_dev) {
+        if (cur_dev >= 0) finish_device();
+        cur_dev = dv;
+        cur_s = __builtin_amdgcn_readlane(s, b);
+      }
+      const int32_t row = __builtin_amdgcn_readlane(r, b);
+      const float wb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(wr), b));
+      const u32x4 *srcp = out_epd + (size_t)row * row16;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int i = lane + kWave * c;
+        if (i < row16) {
+          float f[VE];
+          CK::unpack(srcp[i], f);
+#pragma unroll
+          for (int u = 0; u < VE; ++u) acc[c][u] = __builtin_fmaf(wb, f[u], acc[c][u]);
+        }
+      }
+    }
+  }
+  if (cur_dev >= 0) finish_device();
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i = lane + kWave * c;
+    if (i < row16) y[(size_t)t * row16 + i] = CK::pack(yacc[c]);
+  }
+}
+
+int chunks_per_lane(int row16) { return (row16 + kWave - 1) / kWave; }
+
+}  // namespace
+
+hipError_t launch_dispatch(const occ_layer_desc &Ld, const void *x, const occ_brim &b, void *sfd,
+                           void *epd, hipStream_t st) {
+  if (Ld.T == 0) return hipSuccess;
+  const int es = Ld.dtype == OCC_F32 ? 4 : 2;
+  const int row16 = Ld.d * es / 16;
+  const int L = Ld.E / Ld.D;
+  const int ld = Ld.T * (Ld.k < Ld.D ? Ld.k : Ld.D);
+  const dim3 grid((Ld.T + kTokPerBlock - 1) / kTokPerBlock);
+  const u32x4 *xp = static_cast<const u32x4 *>(x);
+  u32x4 *sp = static_cast<u32x4 *>(sfd);
+  u32x4 *ep = static_cast<u32x4 *>(epd);
+  const int nch = chunks_per_lane(row16);
+#define OCC_DISPATCH(N)                                                                       \
+  dispatch_kernel<N><<<grid, kThreads, 0, st>>>(Ld.T, Ld.D, L, ld, row16, xp, b.brim0, b.brim1, \
+                                                sp, ep)
+  if (nch <= 1) OCC_DISPATCH(1);
+  else if (nch <= 2) OCC_DISPATCH(2);
+  else if (nch <= 4) OCC_DISPATCH(4);
+  else if (nch <= 8) OCC_DISPATCH(8);
+  else OCC_DISPATCH(8);
+#undef OCC_DISPATCH
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t combine_dt(const occ_layer_desc &Ld, const void *out_epd, const occ_brim &b,
+                             const void *shared_out, void *out_sfd, void *y, hipStream_t st) {
+  const int es = DT == OCC_F32 ? 4 : 2;
+  const int row16 = Ld.d * es / 16;
+  const int L = Ld.E / Ld.D;
+  const int ld = Ld.T * (Ld.k < Ld.D ? Ld.k : Ld.D);
+  const dim3 grid((Ld.T + kTokPerBlock - 1) / kTokPerBlock);
+  const u32x4 *oe = static_cast<const u32x4 *>(out_epd);
+  const u32x4 *sh = static_cast<const u32x4 *>(shared_out);
+  u32x4 *os = static_cast<u32x4 *>(out_sfd);
+  u32x4 *yp = static_cast<u32x4 *>(y);
+  const int nch = chunks_per_lane(row16);
+#define OCC_COMBINE(N)                                                                         \
+  combine_kernel<DT, N><<<grid, kThreads, 0, st>>>(Ld.T, Ld.D, L, ld, row16, oe, b.brim0,      \
+                                                   b.brim1, b.epd_w, sh, os, yp)
+  if (nch <= 1) OCC_COMBINE(1);
+  else if (nch <= 2) OCC_COMBINE(2);
+  else if (nch <= 4) OCC_COMBINE(4);
+  else if (nch <= 8) OCC_COMBINE(8);
+  else OCC_COMBINE(8);
+#undef OCC_COMBINE
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const occ_layer_desc &Ld, const void *out_epd, const occ_brim &b,
+                          const void *shared_out, void *out_sfd, void *y, hipStream_t st) {
+  if (Ld.T == 0) return hipSuccess;
+  return Ld.dtype == OCC_F32 ? combine_dt<OCC_F32>(Ld, out_epd, b, shared_out, out_sfd, y, st)
+                             : combine_dt<OCC_BF16>(Ld, out_epd, b, shared_out, out_sfd, y, st);
+}
+
+}  // namespace occ

@@ -1,0 +1,173 @@
+"""Device buffers of one MoE layer and the call sequence of its forward step.
+
+The buffers are laid out as the C ABI describes them (include/occ.h); torch
+only allocates them.  ``forward()`` issues occ_route_topk, occ_build_brim,
+occ_dispatch, occ_expert_ffn and occ_combine back to back on one stream with
+no host synchronisation; ``coactivation()`` is the placement side output.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from . import (desc_of, make_brim, occ_build_brim, occ_coactivation, occ_combine, occ_dispatch,
+               occ_expert_down, occ_expert_ffn, occ_expert_up, occ_ffn_workspace_bytes,
+               occ_route_topk, occ_workspace_bytes)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(a: np.ndarray, device="cuda"):
+    """numpy (float32, or bfloat16 kept as uint16 bits, or int32) -> torch."""
+    torch = _torch()
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device)
+
+
+def to_host(t) -> np.ndarray:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+@dataclass
+class Weights:
+    x: object
+    w_router: object
+    w_gate_up: object
+    w_down: object
+    w_gate_up_sh: Optional[object] = None
+    w_down_sh: Optional[object] = None
+
+
+class MoELayer:
+    """All device buffers of one layer configuration (duck-typed ``cfg`` with
+    T, d, E, I, k, D, dtype, renorm, n_shared, I_shared)."""
+
+    def __init__(self, cfg, weights: Weights, slot_expert, with_logits=False, device="cuda"):
+        torch = _torch()
+        self.cfg = cfg
+        self.desc = desc_of(cfg)
+        self.slot_expert = np.ascontiguousarray(slot_expert, dtype=np.int32)
+        self.w = weights
+        T, d, E, k, D = cfg.T, cfg.d, cfg.E, cfg.k, cfg.D
+        L = E // D
+        S_max = T * min(k, D)
+        R = T * k
+        el = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        i32, f32 = torch.int32, torch.float32
+
+        def buf(shape, dt):
+            # at least one element so that no pointer is NULL at T = 0
+            n = int(np.prod(shape))
+            return torch.empty(max(n, 1), dtype=dt, device=device)[:n].view(*shape)
+
+        self.topk_idx = buf((T, k), i32)
+        self.topk_w = buf((T, k), f32)
+        self.logits = buf((T, E), f32) if with_logits else None
+        self.brim0 = buf((D, T), i32)
+        self.brim1 = buf((L, S_max), i32)
+        self.sfd_offset = buf((D + 1,), i32)
+        self.slot_offset = buf((E + 1,), i32)
+        self.sfd_token = buf((S_max,), i32)
+        self.epd_token = buf((R,), i32)
+        self.epd_sfd = buf((R,), i32)
+        self.epd_w = buf((R,), f32)
+        self.S = buf((1,), i32)
+        self.brim = make_brim(brim0=self.brim0, brim1=self.brim1, sfd_offset=self.sfd_offset,
+                              slot_offset=self.slot_offset, sfd_token=self.sfd_token,
+                              epd_token=self.epd_token, epd_sfd=self.epd_sfd, epd_w=self.epd_w,
+                              S=self.S)
+        self.ws_bytes = occ_workspace_bytes(self.desc)
+        self.ws = buf((self.ws_bytes,), torch.uint8)
+        self.sfd = buf((S_max, d), el)
+        self.epd = buf((R, d), el)
+        self.h_bytes = occ_ffn_workspace_bytes(self.desc)
+        self.h_ws = buf((self.h_bytes,), torch.uint8)
+        self.out_epd = buf((R, d), el)
+        self.shared_out = buf((T, d), el) if cfg.n_shared else None
+        self.out_sfd = buf((S_max, d), el)
+        self.y = buf((T, d), el)
+        self.counts = buf((E, E), i32)
+
+    # ---- the hot path ------------------------------------------------------
+    def route(self, stream=None):
+        occ_route_topk(self.desc, self.w.x, self.w.w_router, self.topk_idx, self.topk_w,
+                       self.logits, stream)
+
+    def build_brim(self, stream=None):
+        occ_build_brim(self.desc, self.topk_idx, self.topk_w, self.slot_expert, self.brim,
+                       self.ws, self.ws_bytes, stream)
+
+    def dispatch(self, stream=None):
+        occ_dispatch(self.desc, self.w.x, self.brim, self.sfd, self.epd, stream)
+
+    def _shared(self):
+        if self.cfg.n_shared:
+            return self.w.x, self.w.w_gate_up_sh, self.w.w_down_sh, self.shared_out
+        return None, None, None, None
+
+    def expert_ffn(self, stream=None):
+        x, gu, dn, so = self._shared()
+        occ_expert_ffn(self.desc, self.epd, self.brim, self.slot_expert, self.w.w_gate_up,
+                       self.w.w_down, self.h_ws, self.h_bytes, self.out_epd, x, gu, dn, so,
+                       stream)
+
+    def expert_up(self, stream=None):
+        x, gu, _, _ = self._shared()
+        occ_expert_up(self.desc, self.epd, self.brim, self.slot_expert, self.w.w_gate_up,
+                      self.h_ws, self.h_bytes, x, gu, stream)
+
+    def expert_down(self, stream=None):
+        _, _, dn, so = self._shared()
+        occ_expert_down(self.desc, self.brim, self.slot_expert, self.w.w_down, self.h_ws,
+                        self.h_bytes, self.out_epd, dn, so, stream)
+
+    def combine(self, stream=None):
+        occ_combine(self.desc, self.out_epd, self.brim, self.shared_out, self.out_sfd, self.y,
+                    stream)
+
+    def forward(self, stream=None):
+        self.route(stream)
+        self.build_brim(stream)
+        self.dispatch(stream)
+        self.expert_ffn(stream)
+        self.combine(stream)
+
+    def coactivation(self, accumulate=0, stream=None):
+        occ_coactivation(self.desc, self.topk_idx, self.counts, accumulate, stream)
+
+    # ---- test support --------------------------------------------------------
+    def poison(self):
+        """Fill every output with a recognisable pattern (unwritten entries
+        then show up in the comparisons)."""
+        torch = _torch()
+        for t in (self.topk_idx, self.brim0, self.brim1, self.sfd_offset, self.slot_offset,
+                  self.sfd_token, self.epd_token, self.epd_sfd, self.S, self.counts):
+            t.fill_(0x7A7A7A7A)
+        for t in (self.topk_w, self.epd_w):
+            t.fill_(float("nan"))
+        for t in (self.sfd, self.epd, self.out_epd, self.out_sfd, self.y, self.shared_out,
+                  self.logits):
+            if t is not None:
+                t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).fill_(-1)
+
+    def host(self, name):
+        return to_host(getattr(self, name))
+
+
+def upload_inputs(inp, device="cuda") -> Weights:
+    """Device copies of ``workloads.LayerInputs``."""
+    def dev(a):
+        return None if a is None else to_device(a, device)
+    return Weights(dev(inp.x), dev(inp.w_router), dev(inp.w_gate_up), dev(inp.w_down),
+                   dev(inp.w_gate_up_sh), dev(inp.w_down_sh))

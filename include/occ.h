@@ -1,0 +1,205 @@
+/*
+ * occ.h -- C ABI of the collaboration-aware MoE layer step (Occult) on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages describe it:
+ *   - each token is routed to k of E experts (Expert Coupling in MoE
+ *     Pretraining, Abstract);
+ *   - the token tensor passes through three states stored compactly in HBM,
+ *     ORI (original order), SFD (one row per token and expert-parallel
+ *     device) and EPD (one row per token and expert), guided by two
+ *     bidirectional re-index matrices, BRIM_0 [devices x ORI tokens] and
+ *     BRIM_1 [local experts per device x SFD tokens] (Occult, Figure 4 and
+ *     Figure 5 captions);
+ *   - a token is sent to each device once, not once per expert (Expert
+ *     Coupling, Abstract), and its co-located expert outputs are reduced
+ *     before the way back;
+ *   - experts that one token activates together are "collaborated" (Occult,
+ *     Abstract); their counts drive correlated placement (Expert Coupling,
+ *     Abstract; Occult, TL;DR: expert-placement rescheduling).
+ *
+ * The expert-parallel devices are logical partitions of one GPU's buffers:
+ * device dv owns SFD rows [sfd_offset[dv], sfd_offset[dv+1]) and slots
+ * dv*L .. dv*L+L-1, with L = E / D local experts per device.  Every buffer is
+ * laid out exactly as it would be sent.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_host are host memory; all others are device memory
+ *     allocated and owned by the caller.  The library never allocates.
+ *   - Row-major, K-contiguous layouts; "dtype" is the layer's storage type
+ *     (OCC_F32: float, OCC_BF16: bfloat16 as 16-bit words).
+ *   - Calls are asynchronous on the given stream and never synchronise the
+ *     host; no call reads device memory on the host.
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     an error nothing is launched and no output is touched; the return code
+ *     says why and occ_last_error() gives the text.
+ *   - The library holds no state besides the per-thread error text; calls on
+ *     different streams are independent.
+ */
+#ifndef OCC_H
+#define OCC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t occ_status;
+#define OCC_OK 0
+#define OCC_EINVAL (-1) /* bad shape, null pointer or argument */
+#define OCC_EUNSUP (-2) /* valid but outside what the kernels support */
+#define OCC_ENOSPC (-3) /* workspace smaller than required */
+#define OCC_EHIP (-4)   /* a HIP launch failed; see occ_last_error() */
+
+#define OCC_F32 0
+#define OCC_BF16 1
+
+/* Limits checked by every call (OCC_EUNSUP beyond them). */
+#define OCC_MAX_E 128 /* routed experts */
+#define OCC_MAX_K 16  /* experts per token */
+#define OCC_MAX_D 32  /* logical expert-parallel devices */
+
+/* Shape of one MoE layer.  T tokens of hidden size d; E routed experts of
+ * intermediate size I, k chosen per token; D logical devices (E % D == 0);
+ * n_shared always-active experts of intermediate size I_shared (0 if none);
+ * renorm = 1 divides the chosen softmax weights by their sum. */
+typedef struct occ_layer_desc {
+  int32_t T, d, E, k, D, I;
+  int32_t n_shared, I_shared;
+  int32_t dtype;
+  int32_t renorm;
+} occ_layer_desc;
+
+/* The re-index state of one batch (all device memory, caller-allocated).
+ * S_max = T * min(k, D); R = T * k.
+ *   brim0       int32 [D][T]      SFD row of (device, token), -1 if the token
+ *                                 selects no expert on that device
+ *   brim1       int32 [L][S_max]  EPD row of (local expert, SFD row), -1 if
+ *                                 the token of that SFD row does not select
+ *                                 that local expert; columns >= S unspecified
+ *   sfd_offset  int32 [D+1]       first SFD row of each device; [D] = S
+ *   slot_offset int32 [E+1]       first EPD row of each slot; [E] = R
+ *   sfd_token   int32 [S_max]     ORI token of each SFD row (rows < S)
+ *   epd_token   int32 [R]         ORI token of each EPD row
+ *   epd_sfd     int32 [R]         SFD row of each EPD row
+ *   epd_w       float [R]         routing weight of each EPD row
+ *   S           int32 [1]         number of SFD rows (dispatched rows)
+ * Inside a device (SFD) or a slot (EPD) rows are in ascending token order. */
+typedef struct occ_brim {
+  int32_t *brim0;
+  int32_t *brim1;
+  int32_t *sfd_offset;
+  int32_t *slot_offset;
+  int32_t *sfd_token;
+  int32_t *epd_token;
+  int32_t *epd_sfd;
+  float *epd_w;
+  int32_t *S;
+} occ_brim;
+
+/* Bytes of device workspace occ_build_brim needs (0 on a bad descriptor). */
+size_t occ_workspace_bytes(const occ_layer_desc *desc);
+
+/* Bytes of device workspace occ_expert_ffn / occ_expert_up / occ_expert_down
+ * need for the SwiGLU activations h: R*I (+ T*n_shared*I_shared) elements of
+ * dtype (0 on a bad descriptor). */
+size_t occ_ffn_workspace_bytes(const occ_layer_desc *desc);
+
+/* Routing (Expert Coupling, Abstract: each token goes to k of E experts).
+ *   x        dtype [T][d]     ORI tokens
+ *   w_router dtype [E][d]     router weights
+ *   topk_idx int32 [T][k]     chosen experts, by logit descending, lower
+ *                             expert index first on equal logits
+ *   topk_w   float [T][k]     softmax over all E logits at the chosen
+ *                             experts (divided by their sum if renorm)
+ *   logits   float [T][E]     optional (NULL to skip)
+ * Each logit is the fp32 chain acc = fma(x[t][j], w_router[e][j], acc) over
+ * j = 0..d-1 in order, from +0: bit-reproducible on any IEEE machine. */
+occ_status occ_route_topk(const occ_layer_desc *desc, const void *x, const void *w_router,
+                          int32_t *topk_idx, float *topk_w, float *logits, hipStream_t stream);
+
+/* BRIM construction (Occult, Figure 5 caption; Expert Coupling, Abstract:
+ * each token to each device once).
+ *   topk_idx, topk_w  as written by occ_route_topk
+ *   slot_expert_host  int32 [E] host: expert held by slot g = dv*L + l; must
+ *                     be a permutation of 0..E-1 (OCC_EINVAL otherwise)
+ *   brim              outputs, see occ_brim
+ *   ws, ws_bytes      device workspace of occ_workspace_bytes(desc) bytes
+ * Deterministic: stable counting sorts, no dependence on atomics order. */
+occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *topk_idx,
+                          const float *topk_w, const int32_t *slot_expert_host,
+                          const occ_brim *brim, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dispatch ORI -> SFD -> EPD (Occult, Figure 4 caption): bit copies
+ *   sfd[s] = x[sfd_token[s]]  (dtype [S_max][d], rows < S written): the
+ *            all-to-all send buffer, grouped by device
+ *   epd[r] = sfd[epd_sfd[r]]  (dtype [R][d]): the experts' input, by slot
+ * Both are written from one read of each ORI row. */
+occ_status occ_dispatch(const occ_layer_desc *desc, const void *x, const occ_brim *brim,
+                        void *sfd, void *epd, hipStream_t stream);
+
+/* Expert networks on EPD (Expert Coupling, Abstract: "expert networks";
+ * SwiGLU without biases).  For EPD row r of slot g, e = slot_expert_host[g]:
+ *   h[r]       = silu(W_gate[e] epd[r]) * (W_up[e] epd[r])    (stored in dtype)
+ *   out_epd[r] = W_down[e] h[r]                               (dtype [R][d])
+ * w_gate_up dtype [E][2I][d] (rows 0..I-1 gate, I..2I-1 up), w_down dtype
+ * [E][d][I]; fp32 accumulation.  Shared experts (n_shared > 0) run on the ORI
+ * rows with weight 1: shared_out = sum_s FFN_s(x) (dtype [T][d]) from
+ * w_gate_up_sh [n_shared][2*I_shared][d] and w_down_sh [n_shared][d][I_shared].
+ * h_ws holds h (occ_ffn_workspace_bytes).  x, w_*_sh and shared_out must be
+ * NULL when n_shared == 0.  occ_expert_up runs the gate/up GEMM with the SwiGLU
+ * epilogue, occ_expert_down the down GEMM; occ_expert_ffn runs both. */
+occ_status occ_expert_ffn(const occ_layer_desc *desc, const void *epd, const occ_brim *brim,
+                          const int32_t *slot_expert_host, const void *w_gate_up,
+                          const void *w_down, void *h_ws, size_t h_ws_bytes, void *out_epd,
+                          const void *x, const void *w_gate_up_sh, const void *w_down_sh,
+                          void *shared_out, hipStream_t stream);
+occ_status occ_expert_up(const occ_layer_desc *desc, const void *epd, const occ_brim *brim,
+                         const int32_t *slot_expert_host, const void *w_gate_up, void *h_ws,
+                         size_t h_ws_bytes, const void *x, const void *w_gate_up_sh,
+                         hipStream_t stream);
+occ_status occ_expert_down(const occ_layer_desc *desc, const occ_brim *brim,
+                           const int32_t *slot_expert_host, const void *w_down,
+                           const void *h_ws, size_t h_ws_bytes, void *out_epd,
+                           const void *w_down_sh, void *shared_out, hipStream_t stream);
+
+/* Combine (Occult, Figure 4 caption, the way back over the same BRIMs):
+ *   out_sfd[s] = sum over l ascending with r = brim1[l][s] >= 0 of
+ *                epd_w[r] * out_epd[r]        (dtype [S_max][d]: the
+ *                pre-reduced return payload, rows < S written)
+ *   y[t]       = shared_out[t] + sum over devices dv ascending with
+ *                s = brim0[dv][t] >= 0 of out_sfd[s]        (dtype [T][d])
+ * fp32 accumulation, each stored row rounded to dtype (ties to even).
+ * shared_out may be NULL. */
+occ_status occ_combine(const occ_layer_desc *desc, const void *out_epd, const occ_brim *brim,
+                       const void *shared_out, void *out_sfd, void *y, hipStream_t stream);
+
+/* Co-activation (collaboration) counts (Occult, Abstract):
+ *   counts int32 [E][E]: counts[i][j] += #tokens choosing both i and j
+ *   (diagonal: tokens per expert).  accumulate = 0 zeroes counts first.
+ * Integer atomics only, so the result does not depend on scheduling. */
+occ_status occ_coactivation(const occ_layer_desc *desc, const int32_t *topk_idx,
+                            int32_t *counts, int32_t accumulate, hipStream_t stream);
+
+/* Greedy correlated placement on the host (Expert Coupling, Abstract:
+ * experts often selected together go on one GPU; Occult, TL;DR: placement
+ * rescheduling).  For each device in turn: take the unplaced expert with the
+ * most tokens (lower index on ties), then repeatedly the unplaced expert
+ * with the largest summed count against the device's experts (ties: more
+ * tokens, then lower index) until the device holds E/D experts.
+ *   counts_host      int32 [E][E] host (from occ_coactivation)
+ *   slot_expert_host int32 [E] host output */
+occ_status occ_place_greedy(int32_t E, int32_t D, const int32_t *counts_host,
+                            int32_t *slot_expert_host);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char *occ_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OCC_H */

@@ -1,0 +1,153 @@
+"""Helpers of the GPU parity tests: run the HIP layer through the C ABI and
+the oracle on the same seeded inputs, then compare stage by stage."""
+import concurrent.futures as cf
+import os
+import sys
+
+import numpy as np
+
+import workloads as W
+from tests.checks import check_brim_invariants
+from tests.tolerance import TOL, assert_close
+
+_POOL = cf.ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1)))
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def oracle_logits_parallel(orc, x, wr, dtype, parts=16):
+    """The oracle's logits, computed on row blocks in threads (ctypes drops
+    the GIL); each row is still one in-order fmaf chain per expert."""
+    T = x.shape[0]
+    bounds = np.linspace(0, T, parts + 1).astype(int)
+    futs = [_POOL.submit(orc.logits, x[a:b], wr, dtype) for a, b in zip(bounds[:-1], bounds[1:])
+            if b > a]
+    return np.concatenate([f.result() for f in futs]) if futs else np.zeros((0, wr.shape[0]),
+                                                                            np.float32)
+
+
+def oracle_expert_rows_parallel(orc, x, tok, ex, wgu, wdn, dtype, parts=16):
+    n = len(tok)
+    bounds = np.linspace(0, n, parts + 1).astype(int)
+    futs = [_POOL.submit(orc.expert_rows, x, tok[a:b], ex[a:b], wgu, wdn, dtype)
+            for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+    return np.concatenate([f.result() for f in futs]) if futs else np.zeros((0, x.shape[1]),
+                                                                            np.float32)
+
+
+def oracle_layer(orc, inp, tokens=None):
+    """Oracle results; routing, BRIMs and counts on the full batch, expert
+    arithmetic for ``tokens`` (all by default) and their EPD rows."""
+    cfg = inp.cfg
+    T, E, k, D = cfg.T, cfg.E, cfg.k, cfg.D
+    L = E // D
+    lg = oracle_logits_parallel(orc, inp.x, inp.w_router, cfg.dtype)
+    idx, w = orc.topk(lg, k, cfg.renorm)
+    b = orc.brim(idx, w, inp.slot_expert, E, D)
+    res = dict(logits=lg, idx=idx, w=w, brim=b, coact=orc.coactivation(idx, E))
+    if inp.w_gate_up is None:
+        return res
+    tok = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
+    rows = []
+    for dv in range(D):
+        s = b["brim0"][dv, tok]
+        s = s[s >= 0]
+        for l in range(L):
+            r = b["brim1"][l, s]
+            rows.append(r[r >= 0])
+    rows = np.sort(np.concatenate(rows)).astype(np.int64) if rows else np.zeros(0, np.int64)
+    ex_of_slot = np.repeat(np.asarray(inp.slot_expert), np.diff(b["slot_offset"]))
+    out_rows = oracle_expert_rows_parallel(orc, inp.x, b["epd_token"][rows].astype(np.int32),
+                                           ex_of_slot[rows].astype(np.int32), inp.w_gate_up,
+                                           inp.w_down, cfg.dtype)
+    epd_row = np.full(T * k, -1, np.int32)
+    epd_row[rows] = np.arange(rows.size, dtype=np.int32)
+    shared = None
+    if cfg.n_shared:
+        shared = orc.shared_rows(inp.x, tok, inp.w_gate_up_sh, inp.w_down_sh, cfg.dtype)
+    y, osfd = orc.combine(tok, b, T, D, L, cfg.d, cfg.dtype, out_rows, epd_row, shared,
+                          want_sfd=True)
+    res.update(tokens=tok, epd_rows=rows, out_epd_rows=out_rows, shared=shared, y=y, out_sfd=osfd)
+    return res
+
+
+def gpu_layer(inp, runs=1, poison=True):
+    """Run the HIP layer (forward + co-activation) and fetch every buffer."""
+    import torch
+    from expert_top_router_amd.layer import MoELayer, upload_inputs
+    cfg = inp.cfg
+    lay = MoELayer(cfg, upload_inputs(inp), inp.slot_expert, with_logits=True)
+    outs = []
+    for _ in range(runs):
+        if poison:
+            lay.poison()
+        say(f"  gpu forward {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} D={cfg.D} "
+            f"I={cfg.I} dtype={cfg.dtype}")
+        lay.forward()
+        lay.coactivation()
+        torch.cuda.synchronize()
+        names = ["logits", "topk_idx", "topk_w", "brim0", "brim1", "sfd_offset", "slot_offset",
+                 "sfd_token", "epd_token", "epd_sfd", "epd_w", "S", "sfd", "epd", "out_epd",
+                 "out_sfd", "y", "counts"] + (["shared_out"] if cfg.n_shared else [])
+        outs.append({n: lay.host(n) for n in names})
+    del lay
+    torch.cuda.empty_cache()
+    return outs if runs > 1 else outs[0]
+
+
+def as_f32(a, dtype):
+    return W.to_f32(a, dtype)
+
+
+def compare(g, o, inp, full=True):
+    """Stage-by-stage comparison; integer work bit-exact, floats by TOL."""
+    cfg = inp.cfg
+    dt = cfg.dtype
+    T, k, D, E = cfg.T, cfg.k, cfg.D, cfg.E
+    # routing: logits and indices bit-exact (same fp32 FMA chain), weights by 1e-4
+    assert np.array_equal(g["logits"].view(np.uint32), o["logits"].view(np.uint32)), "logits"
+    assert np.array_equal(g["topk_idx"], o["idx"]), "topk_idx"
+    assert_close(g["topk_w"], o["w"], "f32", "topk_w")
+    b = o["brim"]
+    S = b["S"]
+    assert int(g["S"][0]) == S, ("S", int(g["S"][0]), S)
+    for name in ("brim0", "sfd_offset", "slot_offset"):
+        assert np.array_equal(g[name], b[name]), name
+    assert np.array_equal(g["brim1"][:, :S], b["brim1"][:, :S]), "brim1"
+    assert np.array_equal(g["sfd_token"][:S], b["sfd_token"][:S]), "sfd_token"
+    assert np.array_equal(g["epd_token"], b["epd_token"]), "epd_token"
+    assert np.array_equal(g["epd_sfd"], b["epd_sfd"]), "epd_sfd"
+    # epd_w is a copy of the GPU's own routing weights
+    assert np.array_equal(g["epd_w"], g["topk_w"].reshape(-1)[
+        _flat_pos(g["topk_idx"], b, inp.slot_expert, k)]), "epd_w copy"
+    assert np.array_equal(g["counts"], o["coact"]), "coactivation"
+    # dispatch: bit copies
+    xs = inp.x
+    assert np.array_equal(g["sfd"][:S], xs[b["sfd_token"][:S]]), "sfd"
+    assert np.array_equal(g["epd"], xs[b["epd_token"]]), "epd"
+    gb = dict(brim0=g["brim0"], brim1=g["brim1"], sfd_offset=g["sfd_offset"],
+              slot_offset=g["slot_offset"], sfd_token=g["sfd_token"], epd_token=g["epd_token"],
+              epd_sfd=g["epd_sfd"], epd_w=g["epd_w"], S=S)
+    if full:
+        check_brim_invariants(gb, g["topk_idx"], g["topk_w"], inp.slot_expert, E, D)
+    if "y" not in o:
+        return
+    rows = o["epd_rows"]
+    assert_close(as_f32(g["out_epd"][rows], dt), o["out_epd_rows"], dt, "out_epd")
+    tok = o["tokens"]
+    if cfg.n_shared:
+        assert_close(as_f32(g["shared_out"][tok], dt), o["shared"], dt, "shared_out")
+    srows = np.unique(b["brim0"][:, tok][b["brim0"][:, tok] >= 0])
+    assert_close(as_f32(g["out_sfd"][srows], dt), o["out_sfd"][srows], dt, "out_sfd")
+    assert_close(as_f32(g["y"][tok], dt), o["y"], dt, "y")
+
+
+def _flat_pos(idx, b, slot_expert, k):
+    """Position t*k + j of each EPD row's (token, choice) in topk arrays."""
+    slot_of_row = np.repeat(np.arange(len(slot_expert)), np.diff(b["slot_offset"]))
+    t = b["epd_token"].astype(np.int64)
+    e = np.asarray(slot_expert)[slot_of_row]
+    j = np.argmax(idx[t] == e[:, None], axis=1) if t.size else np.zeros(0, np.int64)
+    return t * k + j

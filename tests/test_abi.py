@@ -1,0 +1,123 @@
+"""The C-ABI library on the host: it loads, exports what include/occ.h
+declares, and rejects bad arguments before any launch (so these run without
+a GPU).  The host-side greedy placement is checked against the oracle."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def occ():
+    if not os.path.exists(os.path.join(ROOT, "expert_top_router_amd", "liboccult.so")):
+        from expert_top_router_amd import build
+        build.build()
+    import expert_top_router_amd as occ
+    return occ
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "occ.h")).read()
+    return set(re.findall(r"^(?:occ_status|size_t|const char \*)\s*(occ_\w+)\s*\(", src, re.M))
+
+
+def test_every_declared_symbol_is_exported(occ):
+    names = declared_symbols()
+    assert len(names) == 12, names
+    lib = C.CDLL(occ.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert names == set(occ.EXPORTED)
+
+
+def _desc(occ, **kw):
+    base = dict(T=64, d=64, E=8, k=2, D=2, I=128, n_shared=0, I_shared=0, dtype="bf16", renorm=0)
+    base.update(kw)
+    return occ.make_desc(**base)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(E=10, D=4), -1),          # E % D != 0
+    (dict(k=9), -1),                # k > E
+    (dict(T=-1), -1),
+    (dict(dtype=7), -1),
+    (dict(renorm=2), -1),
+    (dict(E=256, D=2, k=2), -2),    # E beyond OCC_MAX_E
+    (dict(E=64, D=64, k=17), -2),   # k beyond OCC_MAX_K
+    (dict(E=128, D=64), -2),        # D beyond OCC_MAX_D
+    (dict(d=60), -2),               # d % 8
+    (dict(d=72), -2),               # bf16 GEMM tiles need d % 64
+    (dict(I=96), -2),
+    (dict(dtype="f32", d=4096), -2),  # 16 KiB rows
+    (dict(n_shared=1, I_shared=0), -1),
+])
+def test_bad_descriptors_are_rejected(occ, kw, code):
+    d = _desc(occ, **kw)
+    rc = occ.lib().occ_route_topk(C.byref(d), FAKE, FAKE, FAKE, FAKE, None, None)
+    assert rc == code, occ.last_error()
+    assert occ.last_error()
+    assert occ.occ_workspace_bytes(d) == 0
+
+
+def test_null_pointers_and_workspace(occ):
+    d = _desc(occ)
+    lib = occ.lib()
+    assert lib.occ_route_topk(None, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert lib.occ_route_topk(C.byref(d), None, FAKE, FAKE, FAKE, None, None) == -1
+    brim = occ.make_brim(brim0=FAKE, brim1=FAKE, sfd_offset=FAKE, slot_offset=FAKE,
+                         sfd_token=FAKE, epd_token=FAKE, epd_sfd=FAKE, epd_w=FAKE, S=FAKE)
+    se = np.arange(8, dtype=np.int32)
+    need = occ.occ_workspace_bytes(d)
+    assert need > 0
+    rc = lib.occ_build_brim(C.byref(d), FAKE, FAKE, se.ctypes.data, C.byref(brim), FAKE,
+                            need - 1, None)
+    assert rc == -3 and "workspace" in occ.last_error()
+    bad = np.array([0, 1, 2, 3, 4, 5, 6, 6], dtype=np.int32)
+    rc = lib.occ_build_brim(C.byref(d), FAKE, FAKE, bad.ctypes.data, C.byref(brim), FAKE,
+                            need, None)
+    assert rc == -1 and "permutation" in occ.last_error()
+    partial = occ.make_brim(brim0=FAKE, brim1=FAKE, slot_offset=FAKE)
+    rc = lib.occ_build_brim(C.byref(d), FAKE, FAKE, se.ctypes.data, C.byref(partial), FAKE,
+                            need, None)
+    assert rc == -1
+
+
+def test_shared_expert_arguments_are_checked(occ):
+    lib = occ.lib()
+    brim = occ.make_brim(brim0=FAKE, brim1=FAKE, slot_offset=FAKE, epd_w=FAKE)
+    se = np.arange(8, dtype=np.int32)
+    d = _desc(occ, n_shared=2, I_shared=64)
+    hb = occ.occ_ffn_workspace_bytes(d)
+    assert hb == 64 * 2 * 128 * 2 + 64 * 2 * 64 * 2
+    rc = lib.occ_expert_ffn(C.byref(d), FAKE, C.byref(brim), se.ctypes.data, FAKE, FAKE, FAKE,
+                            hb, FAKE, None, None, None, None, None)
+    assert rc == -1 and "n_shared" in occ.last_error()
+    d0 = _desc(occ)
+    rc = lib.occ_expert_ffn(C.byref(d0), FAKE, C.byref(brim), se.ctypes.data, FAKE, FAKE, FAKE,
+                            occ.occ_ffn_workspace_bytes(d0), FAKE, FAKE, None, None, None, None)
+    assert rc == -1
+    rc = lib.occ_expert_ffn(C.byref(d0), FAKE, C.byref(brim), se.ctypes.data, FAKE, FAKE, FAKE,
+                            10, FAKE, None, None, None, None, None)
+    assert rc == -3
+
+
+def test_greedy_placement_matches_oracle(occ, orc):
+    rng = np.random.default_rng(0)
+    for E, D in [(4, 2), (8, 2), (16, 4), (64, 8), (128, 16)]:
+        for trial in range(5):
+            k = min(6, E)
+            idx = np.stack([rng.permutation(E)[:k] for _ in range(300)]).astype(np.int32)
+            Cm = orc.coactivation(idx, E)
+            if trial == 0:
+                Cm = np.zeros((E, E), np.int32)  # all ties
+            got = occ.occ_place_greedy(E, D, Cm)
+            assert np.array_equal(got, orc.greedy_placement(Cm, D))
+    with pytest.raises(occ.OccError):
+        occ.occ_place_greedy(10, 4, np.zeros((10, 10), np.int32))

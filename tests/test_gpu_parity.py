@@ -1,0 +1,122 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small layers are compared element by element at every stage (routing, BRIMs,
+dispatch, expert outputs, pre-reduction, combine, co-activation); they span
+several GEMM tiles with ragged tails, both dtypes, shared experts, more than
+64 (device, expert) pairs, non-power-of-two expert counts, D = 1, L = 1 and an
+empty batch.  The five full-size layers are compared on the full batch for
+all integer work and on sampled tokens for the expert arithmetic.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from tests.gpu_common import compare, gpu_layer, oracle_layer, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # name: config (several tiles, ragged tails)
+    "tiny_fp32": W.CONFIGS["tiny_fp32"],
+    "bf16_ragged": W.LayerConfig("bf16_ragged", T=300, d=128, E=16, I=128, k=4, D=4,
+                                 dtype="bf16", clusters=4),
+    "bf16_shared": W.LayerConfig("bf16_shared", T=200, d=128, E=8, I=64, k=2, D=2,
+                                 dtype="bf16", n_shared=2, I_shared=64, renorm=1),
+    "bf16_e128_pairs": W.LayerConfig("bf16_e128_pairs", T=513, d=64, E=128, I=64, k=6, D=16,
+                                     dtype="bf16", clusters=8),
+    "f32_e12": W.LayerConfig("f32_e12", T=77, d=64, E=12, I=32, k=3, D=3, dtype="f32"),
+    "bf16_one_device": W.LayerConfig("bf16_one_device", T=129, d=64, E=8, I=64, k=3, D=1,
+                                     dtype="bf16"),
+    "bf16_one_expert_per_device": W.LayerConfig("bf16_one_expert_per_device", T=150, d=128,
+                                                E=8, I=64, k=2, D=8, dtype="bf16"),
+    "bf16_wide_rows": W.LayerConfig("bf16_wide_rows", T=130, d=4096, E=4, I=64, k=2, D=2,
+                                    dtype="bf16"),
+    "f32_empty": W.LayerConfig("f32_empty", T=0, d=64, E=8, I=32, k=2, D=2, dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layer_parity(orc, name):
+    cfg = SMALL[name]
+    say(f"case {name}")
+    inp = W.make_layer(cfg, seed=3)
+    o = oracle_layer(orc, inp)
+    g = gpu_layer(inp)
+    compare(g, o, inp)
+
+
+def test_placement_permutation_and_determinism(orc):
+    """A non-contiguous placement (greedy from the co-activation counts) and
+    two runs that must agree bit for bit."""
+    cfg = SMALL["bf16_ragged"]
+    inp = W.make_layer(cfg, seed=4)
+    base = oracle_layer(orc, inp)
+    inp.slot_expert = orc.greedy_placement(base["coact"], cfg.D)
+    o = oracle_layer(orc, inp)
+    g1, g2 = gpu_layer(inp, runs=2)
+    compare(g1, o, inp)
+    for n in g1:
+        assert np.array_equal(g1[n].view(np.uint8), g2[n].view(np.uint8)), n
+
+
+def test_routing_ties_lower_index_first(orc):
+    """Integer-valued tokens and router rows make many logits equal; the
+    chosen experts must still match the oracle (lower index on ties)."""
+    cfg = W.LayerConfig("ties", T=256, d=64, E=16, I=64, k=4, D=4, dtype="bf16")
+    inp = W.make_layer(cfg, seed=5)
+    rng = np.random.default_rng(5)
+    inp.x = W.from_f64(rng.integers(-1, 2, size=(cfg.T, cfg.d)).astype(np.float64), "bf16")
+    wr = rng.integers(-1, 2, size=(cfg.E, cfg.d)).astype(np.float64)
+    wr[8:] = wr[:8]  # duplicated experts: exact ties everywhere
+    inp.w_router = W.from_f64(wr, "bf16")
+    o = oracle_layer(orc, inp)
+    assert (np.diff(np.sort(o["logits"], axis=1), axis=1) == 0).any()
+    g = gpu_layer(inp)
+    compare(g, o, inp)
+
+
+def test_coactivation_accumulates(orc):
+    import torch
+    from expert_top_router_amd.layer import MoELayer, upload_inputs
+    cfg = SMALL["bf16_ragged"]
+    inp = W.make_layer(cfg, seed=6)
+    lay = MoELayer(cfg, upload_inputs(inp), inp.slot_expert)
+    say("case coactivation accumulate")
+    lay.route()
+    lay.coactivation(accumulate=0)
+    lay.coactivation(accumulate=1)
+    torch.cuda.synchronize()
+    o = oracle_layer(orc, inp)
+    assert np.array_equal(lay.host("counts"), 2 * o["coact"])
+
+
+FULL = ["tiny_fp32", "olmoe_bf16", "mixtral_bf16", "dsv2lite_bf16", "stress_bf16"]
+
+
+def _sample_tokens(cfg, b, n=48, seed=11):
+    rng = np.random.default_rng(seed)
+    tok = set(rng.choice(cfg.T, size=min(n, cfg.T), replace=False).tolist())
+    tok |= {0, cfg.T - 1}
+    # the tokens of the least-loaded non-empty slot (a ragged tile)
+    cnt = np.diff(b["slot_offset"])
+    g = int(np.argmin(np.where(cnt > 0, cnt, cnt.max() + 1)))
+    seg = b["epd_token"][b["slot_offset"][g]:b["slot_offset"][g + 1]]
+    tok |= set(seg[:16].tolist())
+    return np.array(sorted(tok), dtype=np.int32)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_layer_parity(orc, name):
+    """Full batch for routing, BRIMs, dispatch and co-activation; sampled
+    tokens (and all of their EPD/SFD rows) for the expert arithmetic."""
+    cfg = W.CONFIGS[name]
+    say(f"case full {name}: generating inputs")
+    inp = W.make_layer(cfg, seed=0)
+    o_route = oracle_layer(orc, W.LayerInputs(cfg, inp.x, inp.w_router, None, None, None, None,
+                                              inp.slot_expert))
+    tok = _sample_tokens(cfg, o_route["brim"])
+    say(f"case full {name}: oracle on {tok.size} tokens")
+    o = oracle_layer(orc, inp, tokens=tok)
+    g = gpu_layer(inp)
+    compare(g, o, inp, full=False)
+    say(f"case full {name}: S={o['brim']['S']} of T*k={cfg.R}")
