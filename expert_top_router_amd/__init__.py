@@ -39,11 +39,11 @@ class occ_brim(C.Structure):
                                           "sfd_token", "epd_token", "epd_sfd", "epd_w", "S")]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python -m expert_top_router_amd.build`")
-    lib = C.CDLL(LIB_PATH)
+    lib = C.CDLL(path)
     P, I32, SZ = C.c_void_p, C.c_int32, C.c_size_t
     DP, BP = C.POINTER(occ_layer_desc), C.POINTER(occ_brim)
     sig = {

@@ -68,6 +68,14 @@ occ_status check_desc(const occ_layer_desc *p) {
     return fail(OCC_EUNSUP, "rows of %lld bytes exceed 8192", (long long)(L.d * elem_bytes(L)));
   if (L.dtype == OCC_BF16 && (L.d % 64 != 0 || L.I % 64 != 0 || L.I_shared % 64 != 0))
     return fail(OCC_EUNSUP, "bf16 expert GEMMs need d, I, I_shared multiples of 64");
+  if (L.dtype == OCC_BF16) {
+    // the bf16 GEMMs address each operand with 32-bit byte offsets
+    const int64_t R = (int64_t)L.T * L.k, lim = 0xffffffffll;
+    if (R * L.d * 2 > lim || R * L.I * 2 > lim || (int64_t)L.E * 2 * L.I * L.d * 2 > lim ||
+        (int64_t)L.T * L.n_shared * L.I_shared * 2 > lim ||
+        (int64_t)L.n_shared * 2 * L.I_shared * L.d * 2 > lim)
+      return fail(OCC_EUNSUP, "an expert GEMM operand exceeds 4 GiB");
+  }
   return OCC_OK;
 }
 
@@ -129,7 +137,7 @@ size_t occ_ffn_workspace_bytes(const occ_layer_desc *desc) {
   return h_bytes(*desc) + h_sh_bytes(*desc);
 }
 
-occ_status occ_route_topk(const occ_layer_desc *desc, const void *x, const void *w_router,
+occ_status occ_route_topk(const occ_layer_desc *desc, const void *x, const float *w_router,
                           int32_t *topk_idx, float *topk_w, float *logits, hipStream_t stream) {
   OCC_TRY(check_desc(desc));
   const int64_t Td = (int64_t)desc->T * desc->d, Tk = (int64_t)desc->T * desc->k;

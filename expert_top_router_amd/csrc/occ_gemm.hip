@@ -25,9 +25,6 @@
 namespace occ {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 struct GemmArgs {
   const int32_t *row_offset;  // [G+1] on the device (slots); nullptr: one dense group
   int G;
@@ -37,6 +34,8 @@ struct GemmArgs {
   const void *B;
   int64_t ldb;
   int64_t b_group_stride;  // elements between the weights of consecutive experts
+  int64_t a_bytes;         // bytes of the whole A operand (< 4 GiB: buffer loads)
+  int64_t b_bytes;         // bytes of the whole weight operand (< 4 GiB)
   int64_t up_offset;       // SwiGLU: elements from a gate row to its up row
   int nseg;                // output columns per weight segment
   int64_t nseg_stride;     // elements between weight segments along the output
@@ -51,9 +50,20 @@ struct GemmArgs {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 64;
+constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 constexpr int kLdsK = kBK + 8;
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// Raw buffer resource over a whole operand.  Built from kernel arguments
+// only, so it is wave-uniform and lives in SGPRs; tile and lane positions go
+// into the 32-bit per-lane offset, the k position into the scalar offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)(uint32_t)bytes,
+                                           kBufferFlags);
+}
+
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 
 // Wave 0 writes cumulative m-tile counts of the groups into ts[0..G].
 __device__ __forceinline__ void group_tile_scan(const int32_t *row_offset, int G, int BM,
@@ -122,15 +132,24 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs &a, int32_t *ts, Tile
   return true;
 }
 
-template <int BM, int BN, bool SWIGLU>
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// bf16 grouped GEMM.  4 waves in 2 x 2, wave tile (BM/2) x (BN/2) made of
+// 32x32 output blocks of v_mfma_f32_32x32x16_bf16.  Operand layout of that
+// instruction: lane l supplies row (or column) l % 32 and the eight k values
+// 8*(l/32) .. 8*(l/32)+7 of a 16-deep k step; output element i of lane l is
+// row 8*(i/4) + 4*(l/32) + i%4, column l % 32.
+template <int BM, int BN, int PF, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int MI = WM / 16, NI = WN / 16;
-  constexpr int BNO = SWIGLU ? BN / 2 : BN;  // output columns per tile
+  constexpr int MI = WM / 32, NI = WN / 32;
+  constexpr int BNO = SWIGLU ? BN / 2 : BN;        // output columns per tile
   constexpr int A_CH = BM * (kBK / 8) / kThreads;  // 16-byte chunks per thread
   constexpr int B_CH = BN * (kBK / 8) / kThreads;
   constexpr int STAGE = (BM + BN) * kLdsK;          // elements per LDS stage
   constexpr int CLD = BNO + 8;                      // staged output row stride
+  constexpr int KSTEPS = kBK / 16;
   static_assert(BM * CLD <= 2 * STAGE, "output staging must fit in the tile buffers");
   static_assert(!SWIGLU || NI % 2 == 0, "gate and up halves");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
@@ -142,116 +161,166 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave >> 1, wn = wave & 1;
   const int expert = a.expert_of_group[tc.group];
-  const uint16_t *Ab = static_cast<const uint16_t *>(a.A) + (int64_t)tc.row_begin * a.lda;
-  const int nsg = tc.n0 / a.nseg;
-  const uint16_t *Bb = static_cast<const uint16_t *>(a.B) + (int64_t)expert * a.b_group_stride +
-                       (int64_t)nsg * a.nseg_stride + (int64_t)(tc.n0 - nsg * a.nseg) * a.ldb;
-
-  // per-thread global source rows (clamped inside the tile, never out of bounds)
-  const uint16_t *a_src[A_CH];
-  const uint16_t *b_src[B_CH];
+  // Global loads are buffer loads: one resource per operand, a per-thread
+  // 32-bit byte offset fixed for the whole tile, and a scalar k offset, so the
+  // k loop does no vector address arithmetic.  Rows are clamped inside the
+  // tile, so every access is in bounds.
+  const __amdgpu_buffer_rsrc_t a_rsrc = operand_rsrc(a.A, a.a_bytes);
+  const __amdgpu_buffer_rsrc_t b_rsrc = operand_rsrc(a.B, a.b_bytes);
+  const uint32_t a_base = (uint32_t)((int64_t)tc.row_begin * a.lda * 2);
+  const uint32_t b_base = (uint32_t)((int64_t)expert * a.b_group_stride * 2);
+  uint32_t a_off[A_CH], b_off[B_CH];
   int a_dst[A_CH], b_dst[B_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
     const int c = tid + kThreads * i, r = c >> 3, cc = c & 7;
-    a_src[i] = Ab + (int64_t)min(r, tc.rows - 1) * a.lda + cc * 8;
+    a_off[i] = a_base + (uint32_t)(((int64_t)min(r, tc.rows - 1) * a.lda + cc * 8) * 2);
     a_dst[i] = r * kLdsK + cc * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
     const int c = tid + kThreads * i, r = c >> 3, cc = c & 7;
-    int64_t off;
-    if (SWIGLU) {
-      const int rr = r < BN / 2 ? r : r - BN / 2;
-      const int re = min(rr, a.N - 1 - tc.n0);
-      off = (int64_t)re * a.ldb + (r < BN / 2 ? 0 : a.up_offset);
-    } else {
-      off = (int64_t)min(r, a.N - 1 - tc.n0) * a.ldb;
-    }
-    b_src[i] = Bb + off + cc * 8;
+    // output column n of this weight row; a tile may span weight segments
+    const int rr = SWIGLU ? (r < BN / 2 ? r : r - BN / 2) : r;
+    const int n = tc.n0 + min(rr, a.N - 1 - tc.n0);
+    const int sg = n / a.nseg;
+    int64_t off = (int64_t)sg * a.nseg_stride + (int64_t)(n - sg * a.nseg) * a.ldb;
+    if (SWIGLU && r >= BN / 2) off += a.up_offset;
+    b_off[i] = b_base + (uint32_t)((off + cc * 8) * 2);
     b_dst[i] = BM * kLdsK + r * kLdsK + cc * 8;
   }
 
-  f32x4 acc[MI][NI];
+  f32x16 acc[MI][NI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
 
-  u32x4 ra[A_CH], rb[B_CH];
-#define OCC_LOAD_REGS(kt_)                                                          \
-  do {                                                                              \
-    const int k0_ = (kt_) * kBK;                                                    \
-    const int ks_ = k0_ / a.kseg;                                                   \
-    const int64_t bk_ = (int64_t)ks_ * a.kseg_stride + (k0_ - ks_ * a.kseg);        \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) ra[i] =                        \
-        *reinterpret_cast<const u32x4 *>(a_src[i] + k0_);                           \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) rb[i] =                        \
-        *reinterpret_cast<const u32x4 *>(b_src[i] + bk_);                           \
-  } while (0)
-#define OCC_STORE_LDS(buf_)                                                         \
-  do {                                                                              \
-    uint16_t *s_ = smem + (buf_) * STAGE;                                           \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                \
-        *reinterpret_cast<u32x4 *>(s_ + a_dst[i]) = ra[i];                          \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                \
-        *reinterpret_cast<u32x4 *>(s_ + b_dst[i]) = rb[i];                          \
-  } while (0)
-
+  // LDS row of each B fragment: SwiGLU pairs gate block ni with up block ni + NI/2
   int brow[NI];
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
     if (SWIGLU)
-      brow[ni] = ni < NI / 2 ? wn * (WN / 2) + ni * 16 : BN / 2 + wn * (WN / 2) + (ni - NI / 2) * 16;
+      brow[ni] = ni < NI / 2 ? wn * (WN / 2) + ni * 32 : BN / 2 + wn * (WN / 2) + (ni - NI / 2) * 32;
     else
-      brow[ni] = wn * WN + ni * 16;
+      brow[ni] = wn * WN + ni * 32;
   }
-
-  const int nk = a.K / kBK;
-  OCC_LOAD_REGS(0);
-  OCC_STORE_LDS(0);
-  __syncthreads();
-  const int frag_r = lane & 15, frag_k = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) OCC_LOAD_REGS(kt + 1);
-    const uint16_t *As = smem + cur * STAGE;
-    const uint16_t *Bs = As + BM * kLdsK;
+  const int frag_r = lane & 31, frag_k = (lane >> 5) * 8;
+  int a_frag[MI], b_frag[NI];
 #pragma unroll
-    for (int ks = 0; ks < kBK; ks += 32) {
-      bf16x8 af[MI], bfr[NI];
+  for (int mi = 0; mi < MI; ++mi) a_frag[mi] = (wm * WM + mi * 32 + frag_r) * kLdsK + frag_k;
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) b_frag[ni] = BM * kLdsK + (brow[ni] + frag_r) * kLdsK + frag_k;
+
+  // PF k-tiles in flight: a ring of PF register sets; the k loop is unrolled by
+  // PF so that every set index is a compile-time constant
+  u32x4 ra[PF][A_CH], rb[PF][B_CH];
+#define OCC_LOAD_REGS(kt_, set_)                                                    \
+  do {                                                                              \
+    const int k0_ = (kt_) * kBK;                                                    \
+    const int ks_ = k0_ / a.kseg;                                                   \
+    const int64_t bk_ = (int64_t)ks_ * a.kseg_stride + (k0_ - ks_ * a.kseg);        \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) ra[set_][i] = __builtin_bit_cast( \
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[i], k0_ * 2, 0));  \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) rb[set_][i] = __builtin_bit_cast( \
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[i], (int)bk_ * 2, 0)); \
+  } while (0)
+#define OCC_STORE_LDS(buf_, set_)                                                   \
+  do {                                                                              \
+    uint16_t *s_ = smem + (buf_) * STAGE;                                           \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                \
+        *reinterpret_cast<u32x4 *>(s_ + a_dst[i]) = ra[set_][i];                    \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                \
+        *reinterpret_cast<u32x4 *>(s_ + b_dst[i]) = rb[set_][i];                    \
+  } while (0)
+
+  // nk % PF == 0 (the launcher picks PF so); loads past the last tile re-read
+  // the last tile (in bounds, L2-resident), which keeps the loop branch-free.
+  // Step kt multiplies tile kt from one LDS buffer while, k step by k step,
+  // it stores tile kt+1 (register set (u+1) % PF) into the other buffer and
+  // refills those registers with tile kt+1+PF; one barrier per step.
+  constexpr int A_PER = (A_CH + KSTEPS - 1) / KSTEPS;  // chunks per k step
+  constexpr int B_PER = (B_CH + KSTEPS - 1) / KSTEPS;
+  const int nk = a.K / kBK;
+#pragma unroll
+  for (int p = 0; p < PF; ++p) OCC_LOAD_REGS(min(p, nk - 1), p);
+  OCC_STORE_LDS(0, 0);
+  __syncthreads();
+  OCC_LOAD_REGS(min(PF, nk - 1), 0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int kb = 0; kb < nk; kb += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int kt = kb + u;
+      const uint16_t *S = smem + (kt & 1) * STAGE;
+      uint16_t *Wn = smem + ((kt + 1) & 1) * STAGE;
+      const int kn = min(kt + 1 + PF, nk - 1);  // tile refilled in this step
+      const int k0n = kn * kBK;
+      const int ksn = k0n / a.kseg;
+      const int64_t bkn = (int64_t)ksn * a.kseg_stride + (k0n - ksn * a.kseg);
+      bf16x8v af[2][MI], bfr[2][NI];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8 *>(As + (wm * WM + mi * 16 + frag_r) * kLdsK + ks +
-                                                   frag_k);
+        af[0][mi] = *reinterpret_cast<const bf16x8v *>(S + a_frag[mi]);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        bfr[ni] =
-            *reinterpret_cast<const bf16x8 *>(Bs + (brow[ni] + frag_r) * kLdsK + ks + frag_k);
+        bfr[0][ni] = *reinterpret_cast<const bf16x8v *>(S + b_frag[ni]);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int q = ks & 1;
+        if (ks + 1 < KSTEPS) {  // fragments of the next k step while these multiply
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+          for (int mi = 0; mi < MI; ++mi)
+            af[q ^ 1][mi] = *reinterpret_cast<const bf16x8v *>(S + a_frag[mi] + (ks + 1) * 16);
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            bfr[q ^ 1][ni] = *reinterpret_cast<const bf16x8v *>(S + b_frag[ni] + (ks + 1) * 16);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][mi], bfr[q][ni],
+                                                                 acc[mi][ni], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < A_PER; ++j) {
+          const int i = ks * A_PER + j;
+          if (i < A_CH) {
+            *reinterpret_cast<u32x4 *>(Wn + a_dst[i]) = ra[(u + 1) % PF][i];
+            ra[(u + 1) % PF][i] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[i], k0n * 2, 0));
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < B_PER; ++j) {
+          const int i = ks * B_PER + j;
+          if (i < B_CH) {
+            *reinterpret_cast<u32x4 *>(Wn + b_dst[i]) = rb[(u + 1) % PF][i];
+            rb[(u + 1) % PF][i] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[i], (int)bkn * 2, 0));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
     }
-    if (kt + 1 < nk) OCC_STORE_LDS(cur ^ 1);
-    __syncthreads();
   }
 #undef OCC_LOAD_REGS
 #undef OCC_STORE_LDS
 
   // ---- epilogue: (SwiGLU), round to bf16, stage, coalesced row stores -----
   uint16_t *Cs = smem;
-  const int orow = (lane >> 4) * 4, ocol = lane & 15;
+  const int orow = (lane >> 5) * 4, ocol = lane & 31;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int ni = 0; ni < (SWIGLU ? NI / 2 : NI); ++ni) {
-      const int col = SWIGLU ? wn * (WN / 2) + ni * 16 + ocol : wn * WN + ni * 16 + ocol;
+      const int col = SWIGLU ? wn * (WN / 2) + ni * 32 + ocol : wn * WN + ni * 32 + ocol;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * WM + mi * 16 + orow + i;
+      for (int i = 0; i < 16; ++i) {
+        const int row = wm * WM + mi * 32 + (i >> 2) * 8 + orow + (i & 3);
         float v;
         if (SWIGLU) v = silu(acc[mi][ni][i]) * acc[mi][ni + NI / 2][i];
         else v = acc[mi][ni][i];
@@ -304,7 +373,26 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a, int max_
   static_cast<float *>(a.C)[(int64_t)row * a.ldc + col] = v;
 }
 
-constexpr int kBM = 128, kBN = 128;
+// Tile shape of a launch: BM rows x BN weight rows (BN/2 outputs with SwiGLU).
+struct TileShape {
+  int bm, bn, pf;
+};
+
+TileShape pick_tile(const GemmArgs &a, bool swiglu) {
+  (void)a;
+  (void)swiglu;
+  return TileShape{256, 256, 1};
+}
+
+template <int BM, int BN, int PF, bool SWIGLU>
+void launch_bf16(const GemmArgs &a, int max_rows, hipStream_t st) {
+  constexpr int BNO = SWIGLU ? BN / 2 : BN;
+  // worst case over all splits of max_rows rows into the groups
+  const int64_t groups = a.row_offset != nullptr ? a.G : 1;
+  const int64_t mt = (max_rows + groups * (BM - 1)) / BM;
+  const int64_t grid = mt * ((a.N + BNO - 1) / BNO);
+  gemm_bf16_kernel<BM, BN, PF, SWIGLU><<<(unsigned)grid, kThreads, 0, st>>>(a);
+}
 
 template <bool SWIGLU>
 hipError_t run_gemm(const GemmArgs &a, int dtype, int max_rows, hipStream_t st) {
@@ -315,12 +403,13 @@ hipError_t run_gemm(const GemmArgs &a, int dtype, int max_rows, hipStream_t st) 
         a, max_rows);
     return hipGetLastError();
   }
-  constexpr int BNO = SWIGLU ? kBN / 2 : kBN;
-  // worst case over all splits of max_rows rows into G groups
-  const int64_t groups = a.row_offset != nullptr ? a.G : 1;
-  const int64_t mt = (max_rows + groups * (kBM - 1)) / kBM;
-  const int64_t grid = mt * ((a.N + BNO - 1) / BNO);
-  gemm_bf16_kernel<kBM, kBN, SWIGLU><<<(unsigned)grid, kThreads, 0, st>>>(a);
+  TileShape t = pick_tile(a, SWIGLU);
+  if ((a.K / kBK) % t.pf != 0) t.pf = 1;
+  if (t.bm == 256 && t.bn == 256) launch_bf16<256, 256, 1, SWIGLU>(a, max_rows, st);
+  else if (t.bm == 128 && t.bn == 128 && t.pf == 3) launch_bf16<128, 128, 3, SWIGLU>(a, max_rows, st);
+  else if (t.bm == 128 && t.bn == 128 && t.pf == 1) launch_bf16<128, 128, 1, SWIGLU>(a, max_rows, st);
+  else if (t.bm == 128 && t.bn == 256) launch_bf16<128, 256, 2, SWIGLU>(a, max_rows, st);
+  else launch_bf16<128, 128, 2, SWIGLU>(a, max_rows, st);
   return hipGetLastError();
 }
 
@@ -344,6 +433,8 @@ hipError_t launch_expert_up(const occ_layer_desc &L, const void *epd, const int3
   a.B = w_gate_up;
   a.ldb = d;
   a.b_group_stride = 2 * I * d;
+  a.a_bytes = (int64_t)L.T * L.k * d * 2;
+  a.b_bytes = (int64_t)L.E * 2 * I * d * 2;
   a.up_offset = I * d;
   a.nseg = (int)I;
   a.nseg_stride = 0;
@@ -365,6 +456,8 @@ hipError_t launch_expert_up(const occ_layer_desc &L, const void *epd, const int3
   s.B = w_gate_up_sh;
   s.ldb = d;
   s.b_group_stride = 0;
+  s.a_bytes = (int64_t)L.T * d * 2;
+  s.b_bytes = (int64_t)L.n_shared * 2 * Is * d * 2;
   s.up_offset = Is * d;
   s.nseg = (int)Is;
   s.nseg_stride = 2 * Is * d;
@@ -390,6 +483,8 @@ hipError_t launch_expert_down(const occ_layer_desc &L, const int32_t *slot_offse
   a.B = w_down;
   a.ldb = I;
   a.b_group_stride = d * I;
+  a.a_bytes = (int64_t)L.T * L.k * I * 2;
+  a.b_bytes = (int64_t)L.E * d * I * 2;
   a.up_offset = 0;
   a.nseg = (int)d;
   a.nseg_stride = 0;
@@ -411,6 +506,8 @@ hipError_t launch_expert_down(const occ_layer_desc &L, const int32_t *slot_offse
   s.B = w_down_sh;
   s.ldb = Is;
   s.b_group_stride = 0;
+  s.a_bytes = (int64_t)L.T * L.n_shared * Is * 2;
+  s.b_bytes = (int64_t)L.n_shared * d * Is * 2;
   s.up_offset = 0;
   s.nseg = (int)d;
   s.nseg_stride = 0;

@@ -50,13 +50,27 @@ template <> struct Elem<OCC_BF16> {
   static __device__ __forceinline__ float to_f32(T v) { return bf16_to_f32(v); }
 };
 
+// Widen one 16-byte vector of stored elements to fp32 (8 bf16 or 4 fp32).
+template <int DT> __device__ __forceinline__ void widen(const u32x4 &u, float *f);
+template <> __device__ __forceinline__ void widen<OCC_BF16>(const u32x4 &u, float *f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(u[i] << 16);
+    f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+template <> __device__ __forceinline__ void widen<OCC_F32>(const u32x4 &u, float *f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(u[i]);
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & (kWave - 1);
   return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 }
 
 // ---- launchers (each returns hipGetLastError() of its launches) -----------
-hipError_t launch_route_topk(const occ_layer_desc &L, const void *x, const void *wr,
+hipError_t launch_route_topk(const occ_layer_desc &L, const void *x, const float *wr,
                              int32_t *idx, float *w, float *logits, hipStream_t st);
 
 // workspace layout of the BRIM build: counts then scanned offsets

@@ -11,11 +11,15 @@
 // be split over j, so the contraction stays on the fp32 VALU (not MFMA) and
 // the parallelism is over (token, expert) pairs.
 //
-// Mapping: a wave is cut into Q = 64/ESEG segments of ESEG lanes; the lanes
-// of a segment hold the experts (lane el owns experts el + ESEG*i, i < EP)
-// and a segment owns TPL tokens.  The token values of a d-chunk are read
-// from LDS as broadcasts, the router rows as 16-byte per-lane reads, and the
-// softmax/top-k reductions stay inside a segment (xor shuffles below ESEG).
+// Mapping: a wave is cut into Q = 64/ESEG segments of ESEG lanes; lane el of
+// a segment owns experts el + ESEG*i (i < EP) and the segment owns TPL
+// tokens, so a lane keeps TPL*EP independent chains.  The block's 4 waves
+// share one staged d-chunk of X (as fp32) and of the router (fp32, each row
+// read by one lane as 16-byte vectors, conflict-free with a 36-float row
+// stride); X values are segment-wide LDS broadcasts.  Chunks are
+// double-buffered: the next chunk is loaded into registers while the current
+// one is consumed, with one barrier per chunk.  Softmax and top-k then run
+// inside each segment with xor shuffles.
 #include "occ_internal.h"
 
 namespace occ {
@@ -23,7 +27,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kJC = 32;        // d-chunk staged in LDS
-constexpr int kLds = kJC + 4;  // padded fp32 row stride (breaks bank aliasing)
+constexpr int kLds = kJC + 4;  // padded fp32 row stride
 
 struct Best {
   float key;
@@ -32,30 +36,33 @@ struct Best {
 };
 
 __device__ __forceinline__ bool better(float ka, int ea, float kb, int eb) {
-  // (key descending, expert ascending); invalid entries carry e = INT_MAX
+  // (key descending, expert ascending); empty candidates carry e = INT_MAX
   return ka > kb || (ka == kb && ea < eb);
 }
 
 template <int DT, int ESEG, int EP, int TPL>
 __global__ __launch_bounds__(kThreads) void route_topk_kernel(
     int T, int d, int E, int k, int renorm, const typename Elem<DT>::T *__restrict__ x,
-    const typename Elem<DT>::T *__restrict__ wr, int32_t *__restrict__ idx_out,
-    float *__restrict__ w_out, float *__restrict__ logits) {
+    const float *__restrict__ wr, int32_t *__restrict__ idx_out, float *__restrict__ w_out,
+    float *__restrict__ logits) {
   using ET = typename Elem<DT>::T;
   constexpr int Q = kWave / ESEG;
   constexpr int TW = Q * TPL;                  // tokens per wave
   constexpr int TB = TW * (kThreads / kWave);  // tokens per block
   constexpr int EMAX = ESEG * EP;
-  constexpr int VEC = 16 / sizeof(ET);         // elements per 16-byte load
-  constexpr int TPR = kJC / VEC;               // threads per staged row
-  __shared__ __attribute__((aligned(16))) float xs[TB * kLds];
-  __shared__ __attribute__((aligned(16))) float ws[EMAX * kLds];
+  constexpr int XV = 16 / sizeof(ET);          // x elements per 16-byte load
+  constexpr int XLOADS = TB * kJC / XV;        // 16-byte loads of one X chunk
+  constexpr int WLOADS = EMAX * kJC / 4;       // 16-byte loads of one router chunk
+  constexpr int XPT = (XLOADS + kThreads - 1) / kThreads;
+  constexpr int WPT = (WLOADS + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) float xs[2][TB * kLds];
+  __shared__ __attribute__((aligned(16))) float ws[2][EMAX * kLds];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int q = lane / ESEG;   // segment
-  const int el = lane % ESEG;  // lane in segment
+  const int q = lane / ESEG;
+  const int el = lane % ESEG;
   const int t0 = blockIdx.x * TB;
 
   float acc[TPL][EP];
@@ -64,58 +71,95 @@ __global__ __launch_bounds__(kThreads) void route_topk_kernel(
 #pragma unroll
     for (int i = 0; i < EP; ++i) acc[m][i] = 0.0f;
 
-  for (int j0 = 0; j0 < d; j0 += kJC) {
+  u32x4 xr[XPT];
+  float4 wrg[WPT];
+  // global -> registers for the chunk at j0 (rows past T / E and columns past
+  // d are zero and never enter a chain: the compute loop stops at jn)
+#define OCC_ROUTE_LOAD(j0_)                                                           \
+  do {                                                                                \
+    _Pragma("unroll") for (int u = 0; u < XPT; ++u) {                                 \
+      const int c = tid + kThreads * u;                                               \
+      const int r = c / (kJC / XV), cv = (c % (kJC / XV)) * XV;                       \
+      const int t = t0 + r;                                                           \
+      xr[u] = u32x4{0u, 0u, 0u, 0u};                                                  \
+      if (c < XLOADS && t < T && (j0_) + cv < d)                                      \
+        xr[u] = *reinterpret_cast<const u32x4 *>(x + (size_t)t * d + (j0_) + cv);     \
+    }                                                                                 \
+    _Pragma("unroll") for (int u = 0; u < WPT; ++u) {                                 \
+      const int c = tid + kThreads * u;                                               \
+      const int r = c / (kJC / 4), cv = (c % (kJC / 4)) * 4;                          \
+      wrg[u] = make_float4(0.f, 0.f, 0.f, 0.f);                                       \
+      if (c < WLOADS && r < E && (j0_) + cv < d)                                      \
+        wrg[u] = *reinterpret_cast<const float4 *>(wr + (size_t)r * d + (j0_) + cv);  \
+    }                                                                                 \
+  } while (0)
+#define OCC_ROUTE_STORE(buf_)                                                         \
+  do {                                                                                \
+    _Pragma("unroll") for (int u = 0; u < XPT; ++u) {                                 \
+      const int c = tid + kThreads * u;                                               \
+      if (c < XLOADS) {                                                               \
+        const int r = c / (kJC / XV), cv = (c % (kJC / XV)) * XV;                     \
+        float f[XV];                                                                  \
+        widen<DT>(xr[u], f);                                                          \
+        _Pragma("unroll") for (int v = 0; v < XV; v += 4)                             \
+            *reinterpret_cast<float4 *>(&xs[buf_][r * kLds + cv + v]) =               \
+            make_float4(f[v], f[v + 1], f[v + 2], f[v + 3]);                          \
+      }                                                                               \
+    }                                                                                 \
+    _Pragma("unroll") for (int u = 0; u < WPT; ++u) {                                 \
+      const int c = tid + kThreads * u;                                               \
+      if (c < WLOADS) {                                                               \
+        const int r = c / (kJC / 4), cv = (c % (kJC / 4)) * 4;                        \
+        *reinterpret_cast<float4 *>(&ws[buf_][r * kLds + cv]) = wrg[u];               \
+      }                                                                               \
+    }                                                                                 \
+  } while (0)
+
+  const int nch = (d + kJC - 1) / kJC;
+  OCC_ROUTE_LOAD(0);
+  OCC_ROUTE_STORE(0);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    const int cur = ch & 1;
+    const int j0 = ch * kJC;
     const int jn = min(kJC, d - j0);  // multiple of 8 (d % 8 == 0)
-    // stage X[t0 .. t0+TB)[j0 .. j0+jn) and W[0 .. EMAX)[j0 .. j0+jn) as fp32
-    for (int c = tid; c < TB * TPR; c += kThreads) {
-      const int r = c / TPR, cv = (c % TPR) * VEC;
-      const int t = t0 + r;
+    if (ch + 1 < nch) OCC_ROUTE_LOAD(j0 + kJC);
+    const float *xsc = xs[cur];
+    const float *wsc = ws[cur];
 #pragma unroll
-      for (int u = 0; u < VEC; ++u)
-        xs[r * kLds + cv + u] =
-            (t < T && cv + u < jn) ? Elem<DT>::load(x, (size_t)t * d + j0 + cv + u) : 0.0f;
-    }
-    for (int c = tid; c < EMAX * TPR; c += kThreads) {
-      const int r = c / TPR, cv = (c % TPR) * VEC;
-#pragma unroll
-      for (int u = 0; u < VEC; ++u)
-        ws[r * kLds + cv + u] =
-            (r < E && cv + u < jn) ? Elem<DT>::load(wr, (size_t)r * d + j0 + cv + u) : 0.0f;
-    }
-    __syncthreads();
-    if (jn == kJC) {
-#pragma unroll
-      for (int jj = 0; jj < kJC; jj += 4) {
-        float4 wv[EP];
+    for (int jj = 0; jj < kJC; jj += 4) {
+      if (jj < jn) {
+        float4 wv[EP], xv[TPL];
 #pragma unroll
         for (int i = 0; i < EP; ++i)
-          wv[i] = *reinterpret_cast<const float4 *>(&ws[(el + ESEG * i) * kLds + jj]);
+          wv[i] = *reinterpret_cast<const float4 *>(&wsc[(el + ESEG * i) * kLds + jj]);
 #pragma unroll
-        for (int m = 0; m < TPL; ++m) {
-          const float4 xv =
-              *reinterpret_cast<const float4 *>(&xs[(wave * TW + q + Q * m) * kLds + jj]);
+        for (int m = 0; m < TPL; ++m)
+          xv[m] = *reinterpret_cast<const float4 *>(&xsc[(wave * TW + q + Q * m) * kLds + jj]);
+        // j ascending inside every chain; the TPL*EP chains interleave
 #pragma unroll
-          for (int i = 0; i < EP; ++i) {
-            acc[m][i] = __builtin_fmaf(xv.x, wv[i].x, acc[m][i]);
-            acc[m][i] = __builtin_fmaf(xv.y, wv[i].y, acc[m][i]);
-            acc[m][i] = __builtin_fmaf(xv.z, wv[i].z, acc[m][i]);
-            acc[m][i] = __builtin_fmaf(xv.w, wv[i].w, acc[m][i]);
-          }
-        }
-      }
-    } else {
-      for (int jj = 0; jj < jn; ++jj) {
+        for (int m = 0; m < TPL; ++m)
 #pragma unroll
-        for (int m = 0; m < TPL; ++m) {
-          const float xv = xs[(wave * TW + q + Q * m) * kLds + jj];
+          for (int i = 0; i < EP; ++i) acc[m][i] = __builtin_fmaf(xv[m].x, wv[i].x, acc[m][i]);
 #pragma unroll
-          for (int i = 0; i < EP; ++i)
-            acc[m][i] = __builtin_fmaf(xv, ws[(el + ESEG * i) * kLds + jj], acc[m][i]);
-        }
+        for (int m = 0; m < TPL; ++m)
+#pragma unroll
+          for (int i = 0; i < EP; ++i) acc[m][i] = __builtin_fmaf(xv[m].y, wv[i].y, acc[m][i]);
+#pragma unroll
+        for (int m = 0; m < TPL; ++m)
+#pragma unroll
+          for (int i = 0; i < EP; ++i) acc[m][i] = __builtin_fmaf(xv[m].z, wv[i].z, acc[m][i]);
+#pragma unroll
+        for (int m = 0; m < TPL; ++m)
+#pragma unroll
+          for (int i = 0; i < EP; ++i) acc[m][i] = __builtin_fmaf(xv[m].w, wv[i].w, acc[m][i]);
       }
     }
+    if (ch + 1 < nch) OCC_ROUTE_STORE(cur ^ 1);
     __syncthreads();
   }
+#undef OCC_ROUTE_LOAD
+#undef OCC_ROUTE_STORE
 
   // ---- softmax and top-k per token, inside the segment --------------------
 #pragma unroll
@@ -151,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void route_topk_kernel(
     int my_e = -1;
     float my_p = 0.0f, psum = 0.0f;
     for (int j = 0; j < k; ++j) {
-      Best b{-INFINITY, INT_MAX, 0.0f};
+      Best b{-INFINITY, 0x7fffffff, 0.0f};
 #pragma unroll
       for (int i = 0; i < EP; ++i) {
         const int e = el + ESEG * i;
@@ -164,10 +208,9 @@ __global__ __launch_bounds__(kThreads) void route_topk_kernel(
         const float op = __shfl_xor(b.p, off);
         if (better(ok, oe, b.key, b.e)) b = Best{ok, oe, op};
       }
-      // the owner retires the winner
 #pragma unroll
       for (int i = 0; i < EP; ++i)
-        if (el + ESEG * i == b.e) live[i] = false;
+        if (el + ESEG * i == b.e) live[i] = false;  // the owner retires the winner
       psum += b.p;
       if (el == j) {
         my_e = b.e;
@@ -182,33 +225,29 @@ __global__ __launch_bounds__(kThreads) void route_topk_kernel(
 }
 
 template <int DT, int ESEG, int EP>
-hipError_t launch_tpl(const occ_layer_desc &L, const void *x, const void *wr, int32_t *idx,
+hipError_t launch_tpl(const occ_layer_desc &L, const void *x, const float *wr, int32_t *idx,
                       float *w, float *logits, hipStream_t st) {
   using ET = typename Elem<DT>::T;
   constexpr int Q = kWave / ESEG;
-  // enough waves to keep four per SIMD busy, then longer per-lane token lists
-  const long waves_tpl1 = ((long)L.T + Q - 1) / Q;
-  int tpl = 1;
-  if (waves_tpl1 >= 4L * 4096) tpl = 4;
-  else if (waves_tpl1 >= 2L * 4096) tpl = 2;
+  // about one wave per SIMD (1024) before lengthening the per-lane token list
+  const long per = (long)L.T / ((long)Q * 1024);
+  const int tpl = per >= 8 ? 8 : per >= 4 ? 4 : per >= 2 ? 2 : 1;
   const int tb = Q * tpl * (kThreads / kWave);
   const dim3 grid((L.T + tb - 1) / tb);
   const ET *xp = static_cast<const ET *>(x);
-  const ET *wp = static_cast<const ET *>(wr);
-  if (tpl == 4)
-    route_topk_kernel<DT, ESEG, EP, 4><<<grid, kThreads, 0, st>>>(L.T, L.d, L.E, L.k, L.renorm,
-                                                                  xp, wp, idx, w, logits);
-  else if (tpl == 2)
-    route_topk_kernel<DT, ESEG, EP, 2><<<grid, kThreads, 0, st>>>(L.T, L.d, L.E, L.k, L.renorm,
-                                                                  xp, wp, idx, w, logits);
-  else
-    route_topk_kernel<DT, ESEG, EP, 1><<<grid, kThreads, 0, st>>>(L.T, L.d, L.E, L.k, L.renorm,
-                                                                  xp, wp, idx, w, logits);
+#define OCC_ROUTE_LAUNCH(TPL_)                                                    \
+  route_topk_kernel<DT, ESEG, EP, TPL_><<<grid, kThreads, 0, st>>>(               \
+      L.T, L.d, L.E, L.k, L.renorm, xp, wr, idx, w, logits)
+  if (tpl == 8) OCC_ROUTE_LAUNCH(8);
+  else if (tpl == 4) OCC_ROUTE_LAUNCH(4);
+  else if (tpl == 2) OCC_ROUTE_LAUNCH(2);
+  else OCC_ROUTE_LAUNCH(1);
+#undef OCC_ROUTE_LAUNCH
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t launch_dt(const occ_layer_desc &L, const void *x, const void *wr, int32_t *idx,
+hipError_t launch_dt(const occ_layer_desc &L, const void *x, const float *wr, int32_t *idx,
                      float *w, float *logits, hipStream_t st) {
   if (L.E <= 4) return launch_tpl<DT, 4, 1>(L, x, wr, idx, w, logits, st);
   if (L.E <= 8) return launch_tpl<DT, 8, 1>(L, x, wr, idx, w, logits, st);
@@ -220,7 +259,7 @@ hipError_t launch_dt(const occ_layer_desc &L, const void *x, const void *wr, int
 
 }  // namespace
 
-hipError_t launch_route_topk(const occ_layer_desc &L, const void *x, const void *wr,
+hipError_t launch_route_topk(const occ_layer_desc &L, const void *x, const float *wr,
                              int32_t *idx, float *w, float *logits, hipStream_t st) {
   if (L.T == 0) return hipSuccess;
   return L.dtype == OCC_F32 ? launch_dt<OCC_F32>(L, x, wr, idx, w, logits, st)

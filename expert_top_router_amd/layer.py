@@ -165,9 +165,16 @@ class MoELayer:
         return to_host(getattr(self, name))
 
 
+def router_f32(w_router: np.ndarray) -> np.ndarray:
+    """The router in fp32, as occ_route_topk takes it (bf16 widens exactly)."""
+    if w_router.dtype == np.uint16:
+        return (w_router.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return np.ascontiguousarray(w_router, dtype=np.float32)
+
+
 def upload_inputs(inp, device="cuda") -> Weights:
-    """Device copies of ``workloads.LayerInputs``."""
+    """Device copies of ``workloads.LayerInputs`` (router widened to fp32)."""
     def dev(a):
         return None if a is None else to_device(a, device)
-    return Weights(dev(inp.x), dev(inp.w_router), dev(inp.w_gate_up), dev(inp.w_down),
-                   dev(inp.w_gate_up_sh), dev(inp.w_down_sh))
+    return Weights(dev(inp.x), dev(router_f32(inp.w_router)), dev(inp.w_gate_up),
+                   dev(inp.w_down), dev(inp.w_gate_up_sh), dev(inp.w_down_sh))

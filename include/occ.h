@@ -111,7 +111,7 @@ size_t occ_ffn_workspace_bytes(const occ_layer_desc *desc);
 
 /* Routing (Expert Coupling, Abstract: each token goes to k of E experts).
  *   x        dtype [T][d]     ORI tokens
- *   w_router dtype [E][d]     router weights
+ *   w_router float [E][d]     router weights, fp32 whatever the layer dtype
  *   topk_idx int32 [T][k]     chosen experts, by logit descending, lower
  *                             expert index first on equal logits
  *   topk_w   float [T][k]     softmax over all E logits at the chosen
@@ -119,7 +119,7 @@ size_t occ_ffn_workspace_bytes(const occ_layer_desc *desc);
  *   logits   float [T][E]     optional (NULL to skip)
  * Each logit is the fp32 chain acc = fma(x[t][j], w_router[e][j], acc) over
  * j = 0..d-1 in order, from +0: bit-reproducible on any IEEE machine. */
-occ_status occ_route_topk(const occ_layer_desc *desc, const void *x, const void *w_router,
+occ_status occ_route_topk(const occ_layer_desc *desc, const void *x, const float *w_router,
                           int32_t *topk_idx, float *topk_w, float *logits, hipStream_t stream);
 
 /* BRIM construction (Occult, Figure 5 caption; Expert Coupling, Abstract:

@@ -84,12 +84,18 @@ def _check(rc, what):
 
 
 # ---------------------------------------------------------------------------
-def logits(x, wr, dtype):
-    """O1: [T, E] float32 logits, each an in-order fmaf chain over d."""
+def _dt_of(a):
+    """Storage type of an array: float32, or bfloat16 kept as uint16 bits."""
+    return {np.dtype(np.float32): 0, np.dtype(np.uint16): 1}[np.asarray(a).dtype]
+
+
+def logits(x, wr, dtype=None):
+    """O1: [T, E] float32 logits, each an in-order fmaf chain over d.  The
+    storage types of x and wr come from their numpy dtypes."""
     T, d = x.shape
     E = wr.shape[0]
     out = np.empty((T, E), dtype=np.float32)
-    _check(lib().orc_logits(T, d, E, DT[dtype], _p(np.ascontiguousarray(x)),
+    _check(lib().orc_logits(T, d, E, _dt_of(x), _p(np.ascontiguousarray(x)), _dt_of(wr),
                             _p(np.ascontiguousarray(wr)), _p(out)), "logits")
     return out
 

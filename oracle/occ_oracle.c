@@ -76,14 +76,17 @@ static double round_dt(double v, int dt) {
  * [CPL-ABS]: each token is routed to k of the E experts.  Softmax gate over
  * all E experts; selection on the logits (softmax is monotone). */
 
-/* logits[t][e] = fp32 chain acc = fmaf(x[t][j], wr[e][j], acc), j = 0..d-1 */
-int orc_logits(int T, int d, int E, int dt, const void *x, const void *wr, float *logits) {
+/* logits[t][e] = fp32 chain acc = fmaf(x[t][j], wr[e][j], acc), j = 0..d-1;
+ * x stored in dt_x, the router in dt_w (both widened exactly to fp32). */
+int orc_logits(int T, int d, int E, int dt_x, const void *x, int dt_w, const void *wr,
+               float *logits) {
   if (T < 0 || d <= 0 || E <= 0 || !logits) return ORC_EINVAL;
   for (int t = 0; t < T; ++t)
     for (int e = 0; e < E; ++e) {
       float acc = 0.0f;
       for (int j = 0; j < d; ++j)
-        acc = fmaf(load_f32(x, (size_t)t * d + j, dt), load_f32(wr, (size_t)e * d + j, dt), acc);
+        acc = fmaf(load_f32(x, (size_t)t * d + j, dt_x), load_f32(wr, (size_t)e * d + j, dt_w),
+                   acc);
       logits[(size_t)t * E + e] = acc;
     }
   return ORC_OK;
