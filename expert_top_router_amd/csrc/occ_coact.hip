@@ -52,8 +52,8 @@ hipError_t launch_coactivation(const occ_layer_desc &L, const int32_t *idx, int3
   const int n = L.E * L.E;
   if (!accumulate) zero_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, st>>>(counts, n);
   if (L.T > 0) {
-    // about two blocks per CU, at least one wave of tokens per thread block
-    const int tpb = max(kThreads, (L.T + 511) / 512);
+    // about one block per CU, at least 64 tokens per block
+    const int tpb = max(64, (L.T + 255) / 256 + 63) / 64 * 64;
     const int nblk = (L.T + tpb - 1) / tpb;
     const size_t lds = sizeof(int32_t) * n;
     if (lds > 48 * 1024) {
