@@ -11,7 +11,9 @@ clustered tokens).  Prints one JSON line.
 
 The roofline object describes the dominant kernel (the gate/up GEMM with the
 SwiGLU epilogue): achieved = algorithmic flops per launch / its mean launch
-time from HIP events on the stream it runs on.  cpu_baseline times the CPU
+time, from HIP events recorded around it in every timed step on the stream
+it runs on.  The per-stage times come from a second pass of the same steps
+with an event between every two stages.  cpu_baseline times the CPU
 oracle (single thread) on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -45,6 +47,8 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=192)
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many forward steps (for rocprofv3), print nothing else")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="with --profile-steps: first copy 256 MiB twice (counter scale factors)")
     return p.parse_args()
 
 
@@ -69,17 +73,38 @@ def algorithmic(cfg, S):
     }
 
 
-def time_calls(fn, n, torch):
-    """Mean duration (s) of fn() over n back-to-back calls, HIP events on the
-    current stream (the one the library launches on)."""
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(n):
-        fn()
-    stop.record()
-    stop.synchronize()
-    return start.elapsed_time(stop) / 1e3 / n
+def measured_traffic(cfg):
+    """HBM bytes per launch of the gate/up GEMM from the committed counter
+    summary (two rocprofv3 --pmc passes, scaled by a plain copy), or None when
+    the workload differs or the GEMM source changed since they were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{cfg.name}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    h = re.search(r"gemm_source_sha256: ([0-9a-f]+)", text)
+    src = os.path.join(ROOT, "expert_top_router_amd", "csrc", "occ_gemm.hip")
+    if not m or not h or hashlib.sha256(open(src, "rb").read()).hexdigest() != h.group(1):
+        return None
+    return int(m.group(1))
+
+
+STAGES = ("route", "build_brim", "dispatch", "expert_up", "expert_down", "combine")
+
+
+def step(lay, marks=None):
+    """One forward step of the layer, stage by stage (occ_expert_ffn split
+    into its two launches).  With marks (a list of len(STAGES) + 1 events)
+    an event is recorded on the launch stream before every stage and after
+    the last one."""
+    for i, name in enumerate(STAGES):
+        if marks is not None:
+            marks[i].record()
+        getattr(lay, name)()
+    if marks is not None:
+        marks[-1].record()
 
 
 def cpu_baseline(inp, n_tok):
@@ -159,41 +184,65 @@ def main():
     torch.cuda.synchronize()
 
     if args.profile_steps:
+        if args.copy_calibration:
+            # a plain copy of known size: what the traffic counters read for it
+            # scales their readings for the layer's kernels
+            src = torch.ones(256 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            for _ in range(2):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
         for _ in range(args.profile_steps):
-            lay.forward()
+            step(lay)
             lay.coactivation()
         torch.cuda.synchronize()
         print(f"profiled {args.profile_steps} steps of {cfg.name}", flush=True)
         return
 
     for _ in range(args.warmup):
-        lay.forward()
+        step(lay)
     torch.cuda.synchronize()
+    # Timed region: K steps back to back.  The dominant kernel (gate/up GEMM)
+    # is bracketed by HIP events on the launch stream in every step.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        lay.forward()
+    for i in range(args.steps):
+        lay.route()
+        lay.build_brim()
+        lay.dispatch()
+        ev[i][0].record()
+        lay.expert_up()
+        ev[i][1].record()
+        lay.expert_down()
+        lay.combine()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / args.steps * 1e3
     value = cfg.T * args.steps / elapsed
+    up_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
 
-    # per-stage mean launch times (inputs of each stage are valid from the last forward)
+    # Per-stage mean times in the same sequence (separate pass, an event
+    # between every two stages), and the co-activation side output alone.
     n = max(10, min(args.steps, 50))
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+             for _ in range(n)]
+    for i in range(n):
+        step(lay, marks[i])
+    ca = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ca[0].record()
+    for _ in range(n):
+        lay.coactivation()
+    ca[1].record()
+    torch.cuda.synchronize()
+    t = {name: float(np.mean([m[j].elapsed_time(m[j + 1]) for m in marks])) / 1e3
+         for j, name in enumerate(STAGES)}
+    t["coactivation"] = ca[0].elapsed_time(ca[1]) / 1e3 / n
     S = int(lay.host("S")[0])
     alg = algorithmic(cfg, S)
-    t = {
-        "route": time_calls(lay.route, n, torch),
-        "build_brim": time_calls(lay.build_brim, n, torch),
-        "dispatch": time_calls(lay.dispatch, n, torch),
-        "expert_up": time_calls(lay.expert_up, n, torch),
-        "expert_down": time_calls(lay.expert_down, n, torch),
-        "combine": time_calls(lay.combine, n, torch),
-        "coactivation": time_calls(lay.coactivation, n, torch),
-    }
-    lay.forward()
-    torch.cuda.synchronize()
     peak_mfma = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-    up_tf = alg["up_flop"] / t["expert_up"] / 1e12
+    up_tf = alg["up_flop"] / up_s / 1e12
     stages = {
         "route_us": t["route"] * 1e6,
         "route_valu_frac": alg["route_flop"] / t["route"] / 1e12 / 78.6,
@@ -201,7 +250,7 @@ def main():
         "dispatch_us": t["dispatch"] * 1e6,
         "dispatch_hbm_frac": alg["dispatch_bytes"] / t["dispatch"] / 1e9 / PEAK_HBM_GBS,
         "expert_up_us": t["expert_up"] * 1e6,
-        "expert_up_mfma_frac": up_tf / peak_mfma,
+        "expert_up_mfma_frac": alg["up_flop"] / t["expert_up"] / 1e12 / peak_mfma,
         "expert_down_us": t["expert_down"] * 1e6,
         "expert_down_mfma_frac": alg["down_flop"] / t["expert_down"] / 1e12 / peak_mfma,
         "combine_us": t["combine"] * 1e6,
@@ -225,10 +274,10 @@ def main():
                    "k": cfg.k, "D": cfg.D, "n_shared": cfg.n_shared, "I_shared": cfg.I_shared,
                    "placement": args.placement, "sfd_rows": S, "epd_rows": cfg.R,
                    "sfd_over_tk": S / max(cfg.R, 1)},
-        "roofline": {"kernel": "gemm_bf16_kernel<128,128,SwiGLU> (occ_expert_up)",
+        "roofline": {"kernel": "gemm_bf16_kernel, gate/up GEMM with SwiGLU (occ_expert_up)",
                      "bound": "mfma", "achieved": up_tf, "peak": peak_mfma, "unit": "TFLOP/s",
-                     "frac": up_tf / peak_mfma, "traffic": None,
-                     "launch_us": t["expert_up"] * 1e6,
+                     "frac": up_tf / peak_mfma, "traffic": measured_traffic(cfg),
+                     "launch_us": up_s * 1e6,
                      "flop_per_launch": alg["up_flop"]},
         "stages": stages,
     }

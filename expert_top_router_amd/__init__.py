@@ -42,7 +42,7 @@ class occ_brim(C.Structure):
 def _load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
-                          "`python -m expert_top_router_amd.build`")
+                          "`python expert_top_router_amd/build.py`")
     lib = C.CDLL(path)
     P, I32, SZ = C.c_void_p, C.c_int32, C.c_size_t
     DP, BP = C.POINTER(occ_layer_desc), C.POINTER(occ_brim)

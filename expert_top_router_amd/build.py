@@ -1,6 +1,8 @@
 """Compile liboccult.so (HIP C++ for gfx950) in-tree.
 
-    python -m expert_top_router_amd.build
+    python expert_top_router_amd/build.py
+
+(run by path: importing the package loads the library this script builds).
 
 Every source is compiled with hipcc for gfx950 only; packed-fp32 instructions
 are disabled in device code (hipcc's host pass warns that it does not know
@@ -9,6 +11,7 @@ that feature, which is harmless).
 from __future__ import annotations
 
 import concurrent.futures as cf
+import ctypes
 import os
 import subprocess
 import sys
@@ -47,7 +50,11 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    subprocess.check_call([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *objs])
+    subprocess.check_call([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-Wl,-z,defs",
+                           "-o", tmp, *objs])
+    # every symbol must resolve now (a kernel whose host stub was not emitted
+    # shows up here, not at the first launch)
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW)
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -6,20 +6,18 @@
 //   up:   h   = silu(A W_gate^T) * (A W_up^T)    (SwiGLU fused in the epilogue)
 //   down: out = h W_down^T
 // EPD rows of slot g are contiguous ([slot_offset[g], slot_offset[g+1])), so
-// each slot is one dense GEMM with a data-dependent row count: the grid is
-// sized for the worst case and each block decodes its (slot, n-tile, m-tile)
-// from slot_offset on the device, so no host synchronisation is needed.
+// each slot is one dense GEMM with a data-dependent row count.  The tile table
+// (cumulative m-tiles per slot) is built on the device from slot_offset, so
+// no host synchronisation is needed.
 //
-// bf16: 256 threads = 2 x 2 waves, block tile BM x BN x 64, wave tile
-// (BM/2) x (BN/2) of v_mfma_f32_16x16x32_bf16, fp32 accumulators.  Global
-// tiles go through registers into double-buffered, padded LDS (row stride 72
-// elements = 144 bytes, so the 16 rows read by one MFMA operand load fall in
-// distinct banks); one barrier per k-step.  The output tile is staged in LDS
-// and written with 16-byte row stores.
-// Tile order: slot-major, then n-tile, m-tile fastest, with block ids
-// remapped so that each XCD (blocks are dealt round-robin to the 8 XCDs)
-// works on a contiguous range of tiles: the m-tiles of one slot that share a
-// weight panel run together and share that XCD's L2.
+// bf16: persistent blocks, one per CU, each walking a contiguous range of
+// tiles of its XCD.  A block is 2 x 2 waves with a 256 x 256 x 64 tile, wave
+// tile 128 x 128 of v_mfma_f32_32x32x16_bf16, fp32 accumulators.  Global
+// tiles go through registers (raw buffer loads, one k-tile ahead) into
+// double-buffered, padded LDS (row stride 72 elements = 144 bytes, so the 16
+// rows read by one MFMA operand load fall in distinct banks); one barrier per
+// k-tile.  The epilogue applies SwiGLU, rounds to bf16 in hardware, stages
+// the tile in LDS and writes it with 16-byte row stores.
 #include "occ_internal.h"
 
 namespace occ {
@@ -48,7 +46,7 @@ struct GemmArgs {
   int32_t expert_of_group[OCC_MAX_E];
 };
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // fp32 kernel
 constexpr int kBK = 64;
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 constexpr int kLdsK = kBK + 8;
@@ -89,26 +87,26 @@ struct TileCoord {
   int group, row_begin, rows, n0;
 };
 
-// Decodes this block's tile; returns false for blocks beyond the last tile.
+// The tile table of a launch: cumulative m-tiles per group (ts[0..G]) and the
+// group row offsets (ro[0..G]) in LDS; returns the number of tiles.
 template <int BM, int BNO>
-__device__ __forceinline__ bool decode_tile(const GemmArgs &a, int32_t *ts, TileCoord &tc) {
+__device__ __forceinline__ int tile_table(const GemmArgs &a, int32_t *ts, int32_t *ro) {
   const int ntn = (a.N + BNO - 1) / BNO;
-  int total_mt;
+  if (a.row_offset == nullptr) return ((a.dense_rows + BM - 1) / BM) * ntn;
+  if (threadIdx.x < kWave) group_tile_scan(a.row_offset, a.G, BM, ts);
+  for (int g = threadIdx.x; g <= a.G; g += blockDim.x) ro[g] = a.row_offset[g];
+  __syncthreads();
+  return ts[a.G] * ntn;
+}
+
+// Tile number `logical` (slot-major, then n-tile, m-tile fastest).
+template <int BM, int BNO>
+__device__ __forceinline__ TileCoord tile_coord(const GemmArgs &a, const int32_t *ts,
+                                                const int32_t *ro, int logical) {
+  const int ntn = (a.N + BNO - 1) / BNO;
+  TileCoord tc;
   if (a.row_offset != nullptr) {
-    if (threadIdx.x < kWave) group_tile_scan(a.row_offset, a.G, BM, ts);
-    __syncthreads();
-    total_mt = ts[a.G];
-  } else {
-    total_mt = (a.dense_rows + BM - 1) / BM;
-  }
-  const int ntiles = total_mt * ntn;
-  const int bid = blockIdx.x;
-  if (bid >= ntiles) return false;
-  // XCD-aware remap: the blocks of XCD x (bid % 8 == x) take a contiguous range
-  const int xcd = bid % kXcds;
-  const int logical = xcd * (ntiles / kXcds) + min(xcd, ntiles % kXcds) + bid / kXcds;
-  if (a.row_offset != nullptr) {
-    int lo = 0, hi = a.G - 1;
+    int lo = 0, hi = a.G - 1;  // last group whose first tile is <= logical
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (ts[mid] * ntn <= logical) lo = mid;
@@ -117,22 +115,25 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs &a, int32_t *ts, Tile
     const int mtg = ts[lo + 1] - ts[lo];
     const int local = logical - ts[lo] * ntn;
     const int nt = local / mtg, mt = local - nt * mtg;
-    const int r0 = a.row_offset[lo], r1 = a.row_offset[lo + 1];
     tc.group = lo;
-    tc.row_begin = r0 + mt * BM;
-    tc.rows = min(BM, r1 - tc.row_begin);
+    tc.row_begin = ro[lo] + mt * BM;
+    tc.rows = min(BM, ro[lo + 1] - tc.row_begin);
     tc.n0 = nt * BNO;
   } else {
+    const int total_mt = (a.dense_rows + BM - 1) / BM;
     const int nt = logical / total_mt, mt = logical - nt * total_mt;
     tc.group = 0;
     tc.row_begin = mt * BM;
     tc.rows = min(BM, a.dense_rows - tc.row_begin);
     tc.n0 = nt * BNO;
   }
-  return true;
+  return tc;
 }
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // bf16 grouped GEMM.  4 waves in 2 x 2, wave tile (BM/2) x (BN/2) made of
@@ -140,13 +141,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // instruction: lane l supplies row (or column) l % 32 and the eight k values
 // 8*(l/32) .. 8*(l/32)+7 of a 16-deep k step; output element i of lane l is
 // row 8*(i/4) + 4*(l/32) + i%4, column l % 32.
-template <int BM, int BN, int PF, bool SWIGLU>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+template <int BM, int BN, int PF, bool SWIGLU, int NWN>
+__global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int NT = 2 * NWN * kWave;               // 2 x NWN waves
+  constexpr int WM = BM / 2, WN = BN / NWN;
   constexpr int MI = WM / 32, NI = WN / 32;
   constexpr int BNO = SWIGLU ? BN / 2 : BN;        // output columns per tile
-  constexpr int A_CH = BM * (kBK / 8) / kThreads;  // 16-byte chunks per thread
-  constexpr int B_CH = BN * (kBK / 8) / kThreads;
+  constexpr int A_CH = BM * (kBK / 8) / NT;        // 16-byte chunks per thread
+  constexpr int B_CH = BN * (kBK / 8) / NT;
+  static_assert(A_CH * NT == BM * (kBK / 8) && B_CH * NT == BN * (kBK / 8), "whole chunks");
   constexpr int STAGE = (BM + BN) * kLdsK;          // elements per LDS stage
   constexpr int CLD = BNO + 8;                      // staged output row stride
   constexpr int KSTEPS = kBK / 16;
@@ -154,12 +157,25 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   static_assert(!SWIGLU || NI % 2 == 0, "gate and up halves");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
   __shared__ int32_t ts[OCC_MAX_E + 1];
+  __shared__ int32_t ro[OCC_MAX_E + 1];
 
-  TileCoord tc;
-  if (!decode_tile<BM, BNO>(a, ts, tc)) return;
-
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int wm = wave >> 1, wn = wave & 1;
+  // Persistent blocks (one per CU).  Blocks are dealt round-robin to the 8
+  // XCDs; the blocks of XCD x walk a contiguous range of tiles, so the tiles
+  // that share a weight panel run together on one XCD and share its L2.
+  const int ntiles = tile_table<BM, BNO>(a, ts, ro);
+  const int xcd = blockIdx.x % kXcds;
+  const int nbx = gridDim.x / kXcds + (xcd < (int)(gridDim.x % kXcds) ? 1 : 0);
+  const int x0 = xcd * (ntiles / kXcds) + min(xcd, ntiles % kXcds);
+  const int x1 = x0 + ntiles / kXcds + (xcd < ntiles % kXcds ? 1 : 0);
+  for (int logical = x0 + (int)(blockIdx.x / kXcds); logical < x1; logical += nbx) {
+  // The thread index is re-read per tile (opaque to the compiler) so that the
+  // per-thread offsets below are recomputed instead of staying live, and
+  // spilling, across the epilogue.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int wm = wave / NWN, wn = wave % NWN;
+  const TileCoord tc = tile_coord<BM, BNO>(a, ts, ro, logical);
   const int expert = a.expert_of_group[tc.group];
   // Global loads are buffer loads: one resource per operand, a per-thread
   // 32-bit byte offset fixed for the whole tile, and a scalar k offset, so the
@@ -173,13 +189,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   int a_dst[A_CH], b_dst[B_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + kThreads * i, r = c >> 3, cc = c & 7;
+    const int c = tid + NT * i, r = c >> 3, cc = c & 7;
     a_off[i] = a_base + (uint32_t)(((int64_t)min(r, tc.rows - 1) * a.lda + cc * 8) * 2);
     a_dst[i] = r * kLdsK + cc * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + kThreads * i, r = c >> 3, cc = c & 7;
+    const int c = tid + NT * i, r = c >> 3, cc = c & 7;
     // output column n of this weight row; a tile may span weight segments
     const int rr = SWIGLU ? (r < BN / 2 ? r : r - BN / 2) : r;
     const int n = tc.n0 + min(rr, a.N - 1 - tc.n0);
@@ -282,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][mi], bfr[q][ni],
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[q][ni], af[q][mi],
                                                                  acc[mi][ni], 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < A_PER; ++j) {
@@ -311,31 +327,44 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
 #undef OCC_STORE_LDS
 
   // ---- epilogue: (SwiGLU), round to bf16, stage, coalesced row stores -----
+  // The weight fragment is the MFMA's first operand, so a 32 x 32 accumulator
+  // block holds (output column, token) pairs: lane l has token row l % 32 and
+  // the output columns 8q + 4(l / 32) + j (j < 4) in registers 4q + j, i.e.
+  // four runs of 4 adjacent columns.  Each run is rounded to bf16 in hardware
+  // (round to nearest even) and staged with one 8-byte LDS store.
   uint16_t *Cs = smem;
-  const int orow = (lane >> 5) * 4, ocol = lane & 31;
+  const int crow = lane & 31, ccol = (lane >> 5) * 4;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
+    const int row = wm * WM + mi * 32 + crow;
 #pragma unroll
     for (int ni = 0; ni < (SWIGLU ? NI / 2 : NI); ++ni) {
-      const int col = SWIGLU ? wn * (WN / 2) + ni * 32 + ocol : wn * WN + ni * 32 + ocol;
+      const int col = (SWIGLU ? wn * (WN / 2) : wn * WN) + ni * 32 + ccol;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = wm * WM + mi * 32 + (i >> 2) * 8 + orow + (i & 3);
-        float v;
-        if (SWIGLU) v = silu(acc[mi][ni][i]) * acc[mi][ni + NI / 2][i];
-        else v = acc[mi][ni][i];
-        Cs[row * CLD + col] = f32_to_bf16(v);
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (SWIGLU) v[j] = silu(acc[mi][ni][4 * q + j]) * acc[mi][ni + NI / 2][4 * q + j];
+          else v[j] = acc[mi][ni][4 * q + j];
+        }
+        const f32x2v lo = {v[0], v[1]}, hi = {v[2], v[3]};
+        const u32x2 packed = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2v)),
+                              __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2v))};
+        *reinterpret_cast<u32x2 *>(Cs + row * CLD + col + 8 * q) = packed;
       }
     }
   }
   __syncthreads();
   constexpr int RCH = BNO / 8;  // 16-byte chunks per output row
   uint16_t *Cg = static_cast<uint16_t *>(a.C) + (int64_t)tc.row_begin * a.ldc + tc.n0;
-  for (int c = tid; c < BM * RCH; c += kThreads) {
+  for (int c = tid; c < BM * RCH; c += NT) {
     const int r = c / RCH, cc = c - r * RCH;
     if (r < tc.rows && tc.n0 + cc * 8 < a.N)
       *reinterpret_cast<u32x4 *>(Cg + (int64_t)r * a.ldc + cc * 8) =
           *reinterpret_cast<const u32x4 *>(Cs + r * CLD + cc * 8);
+  }
+  __syncthreads();  // the staging area is the next tile's first LDS stage
   }
 }
 
@@ -373,25 +402,16 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a, int max_
   static_cast<float *>(a.C)[(int64_t)row * a.ldc + col] = v;
 }
 
-// Tile shape of a launch: BM rows x BN weight rows (BN/2 outputs with SwiGLU).
-struct TileShape {
-  int bm, bn, pf;
-};
-
-TileShape pick_tile(const GemmArgs &a, bool swiglu) {
-  (void)a;
-  (void)swiglu;
-  return TileShape{256, 256, 1};
-}
-
-template <int BM, int BN, int PF, bool SWIGLU>
-void launch_bf16(const GemmArgs &a, int max_rows, hipStream_t st) {
+template <int BM, int BN, int PF, bool SWIGLU, int NWN>
+void launch_bf16(const GemmArgs &a, int max_rows, int n_cu, hipStream_t st) {
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
   // worst case over all splits of max_rows rows into the groups
   const int64_t groups = a.row_offset != nullptr ? a.G : 1;
   const int64_t mt = (max_rows + groups * (BM - 1)) / BM;
-  const int64_t grid = mt * ((a.N + BNO - 1) / BNO);
-  gemm_bf16_kernel<BM, BN, PF, SWIGLU><<<(unsigned)grid, kThreads, 0, st>>>(a);
+  const int64_t tiles = mt * ((a.N + BNO - 1) / BNO);
+  // one persistent block per CU (a block fills a CU's LDS)
+  const int64_t grid = tiles < n_cu ? tiles : n_cu;
+  gemm_bf16_kernel<BM, BN, PF, SWIGLU, NWN><<<(unsigned)grid, 2 * NWN * kWave, 0, st>>>(a);
 }
 
 template <bool SWIGLU>
@@ -403,13 +423,11 @@ hipError_t run_gemm(const GemmArgs &a, int dtype, int max_rows, hipStream_t st) 
         a, max_rows);
     return hipGetLastError();
   }
-  TileShape t = pick_tile(a, SWIGLU);
-  if ((a.K / kBK) % t.pf != 0) t.pf = 1;
-  if (t.bm == 256 && t.bn == 256) launch_bf16<256, 256, 1, SWIGLU>(a, max_rows, st);
-  else if (t.bm == 128 && t.bn == 128 && t.pf == 3) launch_bf16<128, 128, 3, SWIGLU>(a, max_rows, st);
-  else if (t.bm == 128 && t.bn == 128 && t.pf == 1) launch_bf16<128, 128, 1, SWIGLU>(a, max_rows, st);
-  else if (t.bm == 128 && t.bn == 256) launch_bf16<128, 256, 2, SWIGLU>(a, max_rows, st);
-  else launch_bf16<128, 128, 2, SWIGLU>(a, max_rows, st);
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipGetLastError();
+  launch_bf16<256, 256, 1, SWIGLU, 2>(a, max_rows, n_cu, st);
   return hipGetLastError();
 }
 

@@ -13,21 +13,19 @@
 //
 // Mapping: a wave is cut into Q = 64/ESEG segments of ESEG lanes; lane el of
 // a segment owns experts el + ESEG*i (i < EP) and the segment owns TPL
-// tokens, so a lane keeps TPL*EP independent chains.  The block's 4 waves
-// share one staged d-chunk of X (as fp32) and of the router (fp32, each row
-// read by one lane as 16-byte vectors, conflict-free with a 36-float row
-// stride); X values are segment-wide LDS broadcasts.  Chunks are
-// double-buffered: the next chunk is loaded into registers while the current
-// one is consumed, with one barrier per chunk.  Softmax and top-k then run
-// inside each segment with xor shuffles.
+// tokens, so a lane keeps TPL*EP independent chains.  The block's 4 or 8
+// waves share one staged d-chunk of X (as fp32) and of the router (fp32, each
+// row read by one lane as 16-byte vectors; the row stride of JC + 4 floats
+// puts the 16 rows of a quarter-wave in distinct banks); X values are
+// segment-wide LDS broadcasts.  Chunks of JC = 32..128 columns go through a
+// two-deep register pipeline (chunk c + 2 loads while chunk c is multiplied
+// from LDS and chunk c + 1 waits in registers), one barrier per chunk.
+// Softmax and top-k then run inside each segment with xor shuffles.
 #include "occ_internal.h"
 
 namespace occ {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kJC = 32;        // d-chunk staged in LDS
-constexpr int kLds = kJC + 4;  // padded fp32 row stride
 
 struct Best {
   float key;
@@ -40,16 +38,19 @@ __device__ __forceinline__ bool better(float ka, int ea, float kb, int eb) {
   return ka > kb || (ka == kb && ea < eb);
 }
 
-template <int DT, int ESEG, int EP, int TPL>
-__global__ __launch_bounds__(kThreads) void route_topk_kernel(
+template <int DT, int ESEG, int EP, int TPL, int JC, int THR>
+__global__ __launch_bounds__(THR) void route_topk_kernel(
     int T, int d, int E, int k, int renorm, const typename Elem<DT>::T *__restrict__ x,
     const float *__restrict__ wr, int32_t *__restrict__ idx_out, float *__restrict__ w_out,
     float *__restrict__ logits) {
   using ET = typename Elem<DT>::T;
   constexpr int Q = kWave / ESEG;
   constexpr int TW = Q * TPL;                  // tokens per wave
+  constexpr int kThreads = THR;
   constexpr int TB = TW * (kThreads / kWave);  // tokens per block
   constexpr int EMAX = ESEG * EP;
+  constexpr int kJC = JC;                      // d-chunk staged in LDS
+  constexpr int kLds = kJC + 4;                // padded fp32 row stride
   constexpr int XV = 16 / sizeof(ET);          // x elements per 16-byte load
   constexpr int XLOADS = TB * kJC / XV;        // 16-byte loads of one X chunk
   constexpr int WLOADS = EMAX * kJC / 4;       // 16-byte loads of one router chunk
@@ -71,11 +72,13 @@ __global__ __launch_bounds__(kThreads) void route_topk_kernel(
 #pragma unroll
     for (int i = 0; i < EP; ++i) acc[m][i] = 0.0f;
 
-  u32x4 xr[XPT];
-  float4 wrg[WPT];
+  // Two register sets: the loads of chunk c go into set c % 2 two chunks
+  // before it is stored to LDS, so each load has two chunks of compute to land.
+  u32x4 xr0[XPT], xr1[XPT];
+  float4 wr0[WPT], wr1[WPT];
   // global -> registers for the chunk at j0 (rows past T / E and columns past
   // d are zero and never enter a chain: the compute loop stops at jn)
-#define OCC_ROUTE_LOAD(j0_)                                                           \
+#define OCC_ROUTE_LOAD(xr, wrg, j0_)                                                  \
   do {                                                                                \
     _Pragma("unroll") for (int u = 0; u < XPT; ++u) {                                 \
       const int c = tid + kThreads * u;                                               \
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void route_topk_kernel(
         wrg[u] = *reinterpret_cast<const float4 *>(wr + (size_t)r * d + (j0_) + cv);  \
     }                                                                                 \
   } while (0)
-#define OCC_ROUTE_STORE(buf_)                                                         \
+#define OCC_ROUTE_STORE(xr, wrg, buf_)                                                \
   do {                                                                                \
     _Pragma("unroll") for (int u = 0; u < XPT; ++u) {                                 \
       const int c = tid + kThreads * u;                                               \
@@ -116,48 +119,50 @@ __global__ __launch_bounds__(kThreads) void route_topk_kernel(
   } while (0)
 
   const int nch = (d + kJC - 1) / kJC;
-  OCC_ROUTE_LOAD(0);
-  OCC_ROUTE_STORE(0);
+  // chunk ch is multiplied from LDS buffer ch % 2, chunk ch + 1 waits in
+  // register set (ch + 1) % 2, and chunk ch + 2 is loading into set ch % 2
+  OCC_ROUTE_LOAD(xr0, wr0, 0);
+  if (nch > 1) OCC_ROUTE_LOAD(xr1, wr1, kJC);
+  OCC_ROUTE_STORE(xr0, wr0, 0);
+  if (nch > 2) OCC_ROUTE_LOAD(xr0, wr0, 2 * kJC);
   __syncthreads();
-  for (int ch = 0; ch < nch; ++ch) {
-    const int cur = ch & 1;
-    const int j0 = ch * kJC;
-    const int jn = min(kJC, d - j0);  // multiple of 8 (d % 8 == 0)
-    if (ch + 1 < nch) OCC_ROUTE_LOAD(j0 + kJC);
-    const float *xsc = xs[cur];
-    const float *wsc = ws[cur];
-#pragma unroll
-    for (int jj = 0; jj < kJC; jj += 4) {
-      if (jj < jn) {
-        float4 wv[EP], xv[TPL];
-#pragma unroll
-        for (int i = 0; i < EP; ++i)
-          wv[i] = *reinterpret_cast<const float4 *>(&wsc[(el + ESEG * i) * kLds + jj]);
-#pragma unroll
-        for (int m = 0; m < TPL; ++m)
-          xv[m] = *reinterpret_cast<const float4 *>(&xsc[(wave * TW + q + Q * m) * kLds + jj]);
-        // j ascending inside every chain; the TPL*EP chains interleave
-#pragma unroll
-        for (int m = 0; m < TPL; ++m)
-#pragma unroll
-          for (int i = 0; i < EP; ++i) acc[m][i] = __builtin_fmaf(xv[m].x, wv[i].x, acc[m][i]);
-#pragma unroll
-        for (int m = 0; m < TPL; ++m)
-#pragma unroll
-          for (int i = 0; i < EP; ++i) acc[m][i] = __builtin_fmaf(xv[m].y, wv[i].y, acc[m][i]);
-#pragma unroll
-        for (int m = 0; m < TPL; ++m)
-#pragma unroll
-          for (int i = 0; i < EP; ++i) acc[m][i] = __builtin_fmaf(xv[m].z, wv[i].z, acc[m][i]);
-#pragma unroll
-        for (int m = 0; m < TPL; ++m)
-#pragma unroll
-          for (int i = 0; i < EP; ++i) acc[m][i] = __builtin_fmaf(xv[m].w, wv[i].w, acc[m][i]);
-      }
-    }
-    if (ch + 1 < nch) OCC_ROUTE_STORE(cur ^ 1);
-    __syncthreads();
+#define OCC_ROUTE_CHUNK(ch_, cur_, xn, wn)                                            \
+  do {                                                                                \
+    const int j0 = (ch_) * kJC;                                                       \
+    const int jn = min(kJC, d - j0); /* multiple of 8 (d % 8 == 0) */                 \
+    const float *xsc = xs[cur_];                                                      \
+    const float *wsc = ws[cur_];                                                      \
+    _Pragma("unroll 8") for (int jj = 0; jj < kJC; jj += 4) {                         \
+      if (jj < jn) {                                                                  \
+        float4 wv[EP], xv[TPL];                                                       \
+        _Pragma("unroll") for (int i = 0; i < EP; ++i) wv[i] =                        \
+            *reinterpret_cast<const float4 *>(&wsc[(el + ESEG * i) * kLds + jj]);     \
+        _Pragma("unroll") for (int m = 0; m < TPL; ++m) xv[m] =                       \
+            *reinterpret_cast<const float4 *>(&xsc[(wave * TW + q + Q * m) * kLds + jj]); \
+        /* j ascending inside every chain; the TPL*EP chains interleave */            \
+        _Pragma("unroll") for (int m = 0; m < TPL; ++m)                               \
+        _Pragma("unroll") for (int i = 0; i < EP; ++i)                                \
+            acc[m][i] = __builtin_fmaf(xv[m].x, wv[i].x, acc[m][i]);                  \
+        _Pragma("unroll") for (int m = 0; m < TPL; ++m)                               \
+        _Pragma("unroll") for (int i = 0; i < EP; ++i)                                \
+            acc[m][i] = __builtin_fmaf(xv[m].y, wv[i].y, acc[m][i]);                  \
+        _Pragma("unroll") for (int m = 0; m < TPL; ++m)                               \
+        _Pragma("unroll") for (int i = 0; i < EP; ++i)                                \
+            acc[m][i] = __builtin_fmaf(xv[m].z, wv[i].z, acc[m][i]);                  \
+        _Pragma("unroll") for (int m = 0; m < TPL; ++m)                               \
+        _Pragma("unroll") for (int i = 0; i < EP; ++i)                                \
+            acc[m][i] = __builtin_fmaf(xv[m].w, wv[i].w, acc[m][i]);                  \
+      }                                                                               \
+    }                                                                                 \
+    if ((ch_) + 1 < nch) OCC_ROUTE_STORE(xn, wn, (cur_) ^ 1);                         \
+    if ((ch_) + 3 < nch) OCC_ROUTE_LOAD(xn, wn, ((ch_) + 3) * kJC);                   \
+    __syncthreads();                                                                  \
+  } while (0)
+  for (int ch = 0; ch < nch; ch += 2) {
+    OCC_ROUTE_CHUNK(ch, 0, xr1, wr1);
+    if (ch + 1 < nch) OCC_ROUTE_CHUNK(ch + 1, 1, xr0, wr0);
   }
+#undef OCC_ROUTE_CHUNK
 #undef OCC_ROUTE_LOAD
 #undef OCC_ROUTE_STORE
 
@@ -224,25 +229,40 @@ __global__ __launch_bounds__(kThreads) void route_topk_kernel(
   }
 }
 
+// LDS bytes of one block: double-buffered X and router chunks.
+constexpr int route_lds(int tb, int emax, int jc) { return 2 * (tb + emax) * (jc + 4) * 4; }
+
+template <int DT, int ESEG, int EP, int TPL, int THR>
+void launch_jc(const occ_layer_desc &L, const void *x, const float *wr, int32_t *idx, float *w,
+               float *logits, hipStream_t st) {
+  using ET = typename Elem<DT>::T;
+  constexpr int TB = kWave / ESEG * TPL * (THR / kWave);
+  // The widest d-chunk that leaves room for two waves per SIMD (two 4-wave
+  // blocks, or one 8-wave block, per CU): long chunks mean few barriers.
+  constexpr int kBudget = THR == 512 ? 150 * 1024 : 80 * 1024;
+  constexpr int JC = route_lds(TB, ESEG * EP, 128) <= kBudget  ? 128
+                     : route_lds(TB, ESEG * EP, 64) <= kBudget ? 64
+                                                               : 32;
+  static_assert(route_lds(TB, ESEG * EP, JC) <= 160 * 1024, "LDS");
+  const dim3 grid((L.T + TB - 1) / TB);
+  route_topk_kernel<DT, ESEG, EP, TPL, JC, THR><<<grid, THR, 0, st>>>(
+      L.T, L.d, L.E, L.k, L.renorm, static_cast<const ET *>(x), wr, idx, w, logits);
+}
+
 template <int DT, int ESEG, int EP>
 hipError_t launch_tpl(const occ_layer_desc &L, const void *x, const float *wr, int32_t *idx,
                       float *w, float *logits, hipStream_t st) {
-  using ET = typename Elem<DT>::T;
   constexpr int Q = kWave / ESEG;
-  // about one wave per SIMD (1024) before lengthening the per-lane token list
-  const long per = (long)L.T / ((long)Q * 1024);
-  const int tpl = per >= 8 ? 8 : per >= 4 ? 4 : per >= 2 ? 2 : 1;
-  const int tb = Q * tpl * (kThreads / kWave);
-  const dim3 grid((L.T + tb - 1) / tb);
-  const ET *xp = static_cast<const ET *>(x);
-#define OCC_ROUTE_LAUNCH(TPL_)                                                    \
-  route_topk_kernel<DT, ESEG, EP, TPL_><<<grid, kThreads, 0, st>>>(               \
-      L.T, L.d, L.E, L.k, L.renorm, xp, wr, idx, w, logits)
-  if (tpl == 8) OCC_ROUTE_LAUNCH(8);
-  else if (tpl == 4) OCC_ROUTE_LAUNCH(4);
-  else if (tpl == 2) OCC_ROUTE_LAUNCH(2);
-  else OCC_ROUTE_LAUNCH(1);
-#undef OCC_ROUTE_LAUNCH
+  // About two waves per SIMD (2048) before lengthening the per-lane token
+  // list.  Routers of 33..64 experts use 8-wave blocks: every block re-reads
+  // the whole router, so more tokens per block means less router traffic
+  // (wider routers already carry 8 tokens per lane).
+  constexpr int THR = ESEG == 64 && EP == 1 ? 512 : 256;
+  const long per = (long)L.T / ((long)Q * 2048);
+  if (per >= 8) launch_jc<DT, ESEG, EP, 8, THR>(L, x, wr, idx, w, logits, st);
+  else if (per >= 4) launch_jc<DT, ESEG, EP, 4, THR>(L, x, wr, idx, w, logits, st);
+  else if (per >= 2) launch_jc<DT, ESEG, EP, 2, THR>(L, x, wr, idx, w, logits, st);
+  else launch_jc<DT, ESEG, EP, 1, THR>(L, x, wr, idx, w, logits, st);
   return hipGetLastError();
 }
 
