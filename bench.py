@@ -107,6 +107,44 @@ def step(lay, marks=None):
         marks[-1].record()
 
 
+DIRECT_STAGES = ("route", "build_brim", "dispatch_direct", "expert_up", "expert_down",
+                 "combine_direct")
+
+
+def conventional(lay, cfg, steps, torch):
+    """The conventional per-(token, expert) strategy (Occult, Figure 2) on
+    the same BRIMs: EPD straight from ORI, combine with no pre-reduction.
+    Times K whole steps, then each stage with events between stages, and
+    states the rows and bytes each strategy would send between devices."""
+    for _ in range(3):
+        for name in DIRECT_STAGES:
+            getattr(lay, name)()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for name in DIRECT_STAGES:
+            getattr(lay, name)()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    n = max(10, min(steps, 50))
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(DIRECT_STAGES) + 1)]
+             for _ in range(n)]
+    for i in range(n):
+        for j, name in enumerate(DIRECT_STAGES):
+            marks[i][j].record()
+            getattr(lay, name)()
+        marks[i][-1].record()
+    torch.cuda.synchronize()
+    t = {name: float(np.mean([m[j].elapsed_time(m[j + 1]) for m in marks])) * 1e3
+         for j, name in enumerate(DIRECT_STAGES)}
+    S = int(lay.host("S")[0])
+    rowb = cfg.d * elem_bytes(cfg)
+    return {"ms_per_step": elapsed / steps * 1e3, "tokens_per_s": cfg.T * steps / elapsed,
+            "dispatch_us": t["dispatch_direct"], "combine_us": t["combine_direct"],
+            "rows_sent": cfg.R, "occult_rows_sent": S, "row_saving": 1.0 - S / max(cfg.R, 1),
+            "send_bytes": cfg.R * rowb, "occult_send_bytes": S * rowb}
+
+
 def cpu_baseline(inp, n_tok):
     """The oracle as it stands, one thread: routing and BRIMs on the full
     batch, expert FFN and combine on a seeded sample of tokens; tokens/s
@@ -281,6 +319,7 @@ def main():
                      "flop_per_launch": alg["up_flop"]},
         "stages": stages,
     }
+    out["conventional"] = conventional(lay, cfg, args.steps, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

@@ -56,6 +56,8 @@ def _load(path: str = LIB_PATH):
         "occ_expert_up": (I32, [DP, P, BP, P, P, P, SZ, P, P, P]),
         "occ_expert_down": (I32, [DP, BP, P, P, P, SZ, P, P, P, P]),
         "occ_combine": (I32, [DP, P, BP, P, P, P, P]),
+        "occ_dispatch_direct": (I32, [DP, P, BP, P, P]),
+        "occ_combine_direct": (I32, [DP, P, BP, P, P, P]),
         "occ_coactivation": (I32, [DP, P, P, I32, P]),
         "occ_place_greedy": (I32, [I32, I32, P, P]),
         "occ_last_error": (C.c_char_p, []),
@@ -72,7 +74,8 @@ _lib = _load()
 # Every symbol the C header declares (checked by the tests).
 EXPORTED = ("occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk", "occ_build_brim",
             "occ_dispatch", "occ_expert_ffn", "occ_expert_up", "occ_expert_down", "occ_combine",
-            "occ_coactivation", "occ_place_greedy", "occ_last_error")
+            "occ_dispatch_direct", "occ_combine_direct", "occ_coactivation", "occ_place_greedy",
+            "occ_last_error")
 
 
 def lib():
@@ -187,6 +190,16 @@ def occ_combine(desc, out_epd, brim: occ_brim, shared_out, out_sfd, y, stream=No
                             _ptr(out_sfd), _ptr(y), _stream(stream)), "occ_combine")
 
 
+def occ_dispatch_direct(desc, x, brim: occ_brim, epd, stream=None):
+    _check(_lib.occ_dispatch_direct(C.byref(desc), _ptr(x), C.byref(brim), _ptr(epd),
+                                    _stream(stream)), "occ_dispatch_direct")
+
+
+def occ_combine_direct(desc, out_epd, brim: occ_brim, shared_out, y, stream=None):
+    _check(_lib.occ_combine_direct(C.byref(desc), _ptr(out_epd), C.byref(brim), _ptr(shared_out),
+                                   _ptr(y), _stream(stream)), "occ_combine_direct")
+
+
 def occ_coactivation(desc, topk_idx, counts, accumulate=0, stream=None):
     _check(_lib.occ_coactivation(C.byref(desc), _ptr(topk_idx), _ptr(counts), int(accumulate),
                                  _stream(stream)), "occ_coactivation")
@@ -206,5 +219,5 @@ from .layer import MoELayer  # noqa: E402  (buffers + the call sequence)
 __all__ = ["MoELayer", "OccError", "occ_layer_desc", "occ_brim", "make_desc", "desc_of",
            "make_brim", "occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk",
            "occ_build_brim", "occ_dispatch", "occ_expert_ffn", "occ_expert_up",
-           "occ_expert_down", "occ_combine", "occ_coactivation", "occ_place_greedy",
-           "last_error"]
+           "occ_expert_down", "occ_combine", "occ_dispatch_direct", "occ_combine_direct",
+           "occ_coactivation", "occ_place_greedy", "last_error"]

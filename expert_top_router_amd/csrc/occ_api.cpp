@@ -175,6 +175,17 @@ occ_status occ_dispatch(const occ_layer_desc *desc, const void *x, const occ_bri
   return hip_status(occ::launch_dispatch(*desc, x, *brim, sfd, epd, stream), "occ_dispatch");
 }
 
+occ_status occ_dispatch_direct(const occ_layer_desc *desc, const void *x, const occ_brim *brim,
+                               void *epd, hipStream_t stream) {
+  OCC_TRY(check_desc(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const int64_t Td = (int64_t)desc->T * desc->d;
+  if (missing(x, Td) || missing(epd, Td * desc->k))
+    return fail(OCC_EINVAL, "x and epd must be set");
+  return hip_status(occ::launch_dispatch(*desc, x, *brim, nullptr, epd, stream),
+                    "occ_dispatch_direct");
+}
+
 // Shared-expert pointers: all set when n_shared > 0, all NULL otherwise.
 static occ_status check_shared_args(const occ_layer_desc &L, std::initializer_list<const void *> ps,
                                     const char *names) {
@@ -270,6 +281,19 @@ occ_status occ_combine(const occ_layer_desc *desc, const void *out_epd, const oc
     return fail(OCC_EINVAL, "out_epd, out_sfd and y must be set");
   return hip_status(occ::launch_combine(*desc, out_epd, *brim, shared_out, out_sfd, y, stream),
                     "occ_combine");
+}
+
+occ_status occ_combine_direct(const occ_layer_desc *desc, const void *out_epd, const occ_brim *brim,
+                              const void *shared_out, void *y, hipStream_t stream) {
+  OCC_TRY(check_desc(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const int64_t Td = (int64_t)desc->T * desc->d;
+  if (missing(brim->epd_w, (int64_t)desc->T * desc->k))
+    return fail(OCC_EINVAL, "brim->epd_w must be set");
+  if (missing(out_epd, Td * desc->k) || missing(y, Td))
+    return fail(OCC_EINVAL, "out_epd and y must be set");
+  return hip_status(occ::launch_combine(*desc, out_epd, *brim, shared_out, nullptr, y, stream),
+                    "occ_combine_direct");
 }
 
 occ_status occ_coactivation(const occ_layer_desc *desc, const int32_t *topk_idx,

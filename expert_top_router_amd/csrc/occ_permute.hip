@@ -10,6 +10,11 @@
 //             device's experts (local index ascending) in fp32, store that
 //             pre-reduced row to out_SFD (the return payload) and add it, as
 //             stored, into y[t].
+// The conventional strategy of Occult, Figure 2 (one row per (token, expert)
+// pair, no deduplication) is the same walk without the SFD stage: dispatch
+// writes only the EPD rows, and combine sums w * out_EPD over all of the
+// token's rows (device, then local expert ascending) into y in fp32 with a
+// single rounding, storing no pre-reduced payload.
 // Index lookups are lane-parallel: lane p of a pass holds pair (device
 // p / L, local expert p % L); ballots then walk the present rows in
 // ascending (device, local) order.  Rows move as 16-byte per-lane chunks,
@@ -22,7 +27,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTokPerBlock = kThreads / kWave;
 
-template <int NCH>
+template <int NCH, bool SFD>
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     int T, int D, int L, int ld, int row16, const u32x4 *__restrict__ x,
     const int32_t *__restrict__ brim0, const int32_t *__restrict__ brim1,
@@ -48,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
       first = l == 0;
       if (s >= 0) r = brim1[(size_t)l * ld + s];
     }
-    uint64_t ms = __ballot(first && s >= 0);
+    uint64_t ms = SFD ? __ballot(first && s >= 0) : 0;
     uint64_t mr = __ballot(r >= 0);
     while (ms) {
       const int b = __ffsll((long long)ms) - 1;
@@ -112,7 +117,7 @@ template <> struct Chunk<OCC_F32> {
   static __device__ __forceinline__ float stored(float f) { return f; }
 };
 
-template <int DT, int NCH>
+template <int DT, int NCH, bool PRE>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     int T, int D, int L, int ld, int row16, const u32x4 *__restrict__ out_epd,
     const int32_t *__restrict__ brim0, const int32_t *__restrict__ brim1,
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
       const int b = __ffsll((long long)mr) - 1;
       mr &= mr - 1;
       const int dv = (p0 + b) / L;
-      if (dv != cur_dev) {
+      if (PRE && dv != cur_dev) {
         if (cur_dev >= 0) finish_device();
         cur_dev = dv;
         cur_s = __builtin_amdgcn_readlane(s, b);
@@ -189,12 +194,15 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
           float f[VE];
           CK::unpack(srcp[i], f);
 #pragma unroll
-          for (int u = 0; u < VE; ++u) acc[c][u] = __builtin_fmaf(wb, f[u], acc[c][u]);
+          for (int u = 0; u < VE; ++u) {
+            if (PRE) acc[c][u] = __builtin_fmaf(wb, f[u], acc[c][u]);
+            else yacc[c][u] = __builtin_fmaf(wb, f[u], yacc[c][u]);
+          }
         }
       }
     }
   }
-  if (cur_dev >= 0) finish_device();
+  if (PRE && cur_dev >= 0) finish_device();
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int i = lane + kWave * c;
@@ -208,6 +216,7 @@ int chunks_per_lane(int row16) { return (row16 + kWave - 1) / kWave; }
 
 hipError_t launch_dispatch(const occ_layer_desc &Ld, const void *x, const occ_brim &b, void *sfd,
                            void *epd, hipStream_t st) {
+  // sfd == nullptr: the conventional dispatch (EPD rows only)
   if (Ld.T == 0) return hipSuccess;
   const int es = Ld.dtype == OCC_F32 ? 4 : 2;
   const int row16 = Ld.d * es / 16;
@@ -218,9 +227,15 @@ hipError_t launch_dispatch(const occ_layer_desc &Ld, const void *x, const occ_br
   u32x4 *sp = static_cast<u32x4 *>(sfd);
   u32x4 *ep = static_cast<u32x4 *>(epd);
   const int nch = chunks_per_lane(row16);
-#define OCC_DISPATCH(N)                                                                       \
-  dispatch_kernel<N><<<grid, kThreads, 0, st>>>(Ld.T, Ld.D, L, ld, row16, xp, b.brim0, b.brim1, \
-                                                sp, ep)
+#define OCC_DISPATCH(N)                                                                     \
+  do {                                                                                      \
+    if (sp != nullptr)                                                                      \
+      dispatch_kernel<N, true><<<grid, kThreads, 0, st>>>(Ld.T, Ld.D, L, ld, row16, xp,     \
+                                                          b.brim0, b.brim1, sp, ep);        \
+    else                                                                                    \
+      dispatch_kernel<N, false><<<grid, kThreads, 0, st>>>(Ld.T, Ld.D, L, ld, row16, xp,    \
+                                                           b.brim0, b.brim1, sp, ep);       \
+  } while (0)
   if (nch <= 1) OCC_DISPATCH(1);
   else if (nch <= 2) OCC_DISPATCH(2);
   else if (nch <= 4) OCC_DISPATCH(4);
@@ -243,9 +258,17 @@ static hipError_t combine_dt(const occ_layer_desc &Ld, const void *out_epd, cons
   u32x4 *os = static_cast<u32x4 *>(out_sfd);
   u32x4 *yp = static_cast<u32x4 *>(y);
   const int nch = chunks_per_lane(row16);
-#define OCC_COMBINE(N)                                                                         \
-  combine_kernel<DT, N><<<grid, kThreads, 0, st>>>(Ld.T, Ld.D, L, ld, row16, oe, b.brim0,      \
-                                                   b.brim1, b.epd_w, sh, os, yp)
+#define OCC_COMBINE(N)                                                                    \
+  do {                                                                                    \
+    if (os != nullptr)                                                                    \
+      combine_kernel<DT, N, true><<<grid, kThreads, 0, st>>>(Ld.T, Ld.D, L, ld, row16, oe, \
+                                                             b.brim0, b.brim1, b.epd_w, sh, \
+                                                             os, yp);                       \
+    else                                                                                  \
+      combine_kernel<DT, N, false><<<grid, kThreads, 0, st>>>(Ld.T, Ld.D, L, ld, row16,    \
+                                                              oe, b.brim0, b.brim1,        \
+                                                              b.epd_w, sh, os, yp);        \
+  } while (0)
   if (nch <= 1) OCC_COMBINE(1);
   else if (nch <= 2) OCC_COMBINE(2);
   else if (nch <= 4) OCC_COMBINE(4);
@@ -255,6 +278,7 @@ static hipError_t combine_dt(const occ_layer_desc &Ld, const void *out_epd, cons
   return hipGetLastError();
 }
 
+// out_sfd == nullptr: the conventional combine (no pre-reduction)
 hipError_t launch_combine(const occ_layer_desc &Ld, const void *out_epd, const occ_brim &b,
                           const void *shared_out, void *out_sfd, void *y, hipStream_t st) {
   if (Ld.T == 0) return hipSuccess;

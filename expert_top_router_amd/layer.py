@@ -12,9 +12,10 @@ from typing import Optional
 
 import numpy as np
 
-from . import (desc_of, make_brim, occ_build_brim, occ_coactivation, occ_combine, occ_dispatch,
-               occ_expert_down, occ_expert_ffn, occ_expert_up, occ_ffn_workspace_bytes,
-               occ_route_topk, occ_workspace_bytes)
+from . import (desc_of, make_brim, occ_build_brim, occ_coactivation, occ_combine,
+               occ_combine_direct, occ_dispatch, occ_dispatch_direct, occ_expert_down,
+               occ_expert_ffn, occ_expert_up, occ_ffn_workspace_bytes, occ_route_topk,
+               occ_workspace_bytes)
 
 
 def _torch():
@@ -142,6 +143,20 @@ class MoELayer:
         self.dispatch(stream)
         self.expert_ffn(stream)
         self.combine(stream)
+
+    # ---- the conventional per-(token, expert) strategy ------------------------
+    def dispatch_direct(self, stream=None):
+        occ_dispatch_direct(self.desc, self.w.x, self.brim, self.epd, stream)
+
+    def combine_direct(self, stream=None):
+        occ_combine_direct(self.desc, self.out_epd, self.brim, self.shared_out, self.y, stream)
+
+    def forward_direct(self, stream=None):
+        self.route(stream)
+        self.build_brim(stream)
+        self.dispatch_direct(stream)
+        self.expert_ffn(stream)
+        self.combine_direct(stream)
 
     def coactivation(self, accumulate=0, stream=None):
         occ_coactivation(self.desc, self.topk_idx, self.counts, accumulate, stream)

@@ -178,6 +178,23 @@ occ_status occ_expert_down(const occ_layer_desc *desc, const occ_brim *brim,
 occ_status occ_combine(const occ_layer_desc *desc, const void *out_epd, const occ_brim *brim,
                        const void *shared_out, void *out_sfd, void *y, hipStream_t stream);
 
+/* Conventional per-(token, expert) dispatch and combine: the standard
+ * strategy that Occult, Figure 2 contrasts with, where every (token, expert)
+ * pair is one row of the send buffer and comes back unreduced.  Same
+ * occ_build_brim outputs, no SFD stage:
+ *   occ_dispatch_direct: epd[r] = x[epd_token[r]]   (dtype [R][d]; the EPD,
+ *                        grouped by slot and so by device, is the send buffer)
+ *   occ_combine_direct:  y[t] = shared_out[t] + sum over the token's rows r
+ *                        (device, then local expert ascending) of
+ *                        epd_w[r] * out_epd[r]      (dtype [T][d])
+ *                        fp32 accumulation, one rounding to dtype (ties to
+ *                        even); shared_out may be NULL.
+ * EINVAL on a NULL x / epd / out_epd / y or brim array (T > 0). */
+occ_status occ_dispatch_direct(const occ_layer_desc *desc, const void *x, const occ_brim *brim,
+                               void *epd, hipStream_t stream);
+occ_status occ_combine_direct(const occ_layer_desc *desc, const void *out_epd, const occ_brim *brim,
+                              const void *shared_out, void *y, hipStream_t stream);
+
 /* Co-activation (collaboration) counts (Occult, Abstract):
  *   counts int32 [E][E]: counts[i][j] += #tokens choosing both i and j
  *   (diagonal: tokens per expert).  accumulate = 0 zeroes counts first.

@@ -190,6 +190,19 @@ def combine(tok, b, T, D, L, d, dtype, out_epd, epd_row=None, shared=None, want_
     return y, osfd
 
 
+def combine_direct(tok, b, T, D, L, d, dtype, out_epd, epd_row=None, shared=None):
+    """O10': the conventional combine (no pre-reduction) for the tokens ``tok``."""
+    tok = _i32(tok)
+    n = tok.size
+    y = np.empty((n, d), np.float32)
+    rc = lib().orc_combine_direct(n, _p(tok), T, D, L, b["ld"], d, DT[dtype], _p(b["brim0"]),
+                                  _p(b["brim1"]), _p(b["epd_w"]), _p(_f32(out_epd)),
+                                  _p(None if epd_row is None else _i32(epd_row)),
+                                  _p(None if shared is None else _f32(shared)), _p(y))
+    _check(rc, "combine_direct")
+    return y
+
+
 def bruteforce(tok, x, idx, w, wgu, wdn, dtype, shared=None):
     """O13: the standard MoE layer with no SFD/EPD, for the tokens ``tok``."""
     tok = _i32(tok)
@@ -270,7 +283,8 @@ def layer(inp, tokens=None, with_bruteforce=False):
     if cfg.n_shared:
         shared = shared_rows(inp.x, tok, inp.w_gate_up_sh, inp.w_down_sh, cfg.dtype)
     y, osfd = combine(tok, b, T, D, L, d, cfg.dtype, out_rows, epd_row, shared, want_sfd=True)
-    res.update(tokens=tok, epd_rows=rows, out_epd_rows=out_rows, shared=shared, y=y, out_sfd=osfd)
+    res.update(tokens=tok, epd_rows=rows, out_epd_rows=out_rows, shared=shared, y=y, out_sfd=osfd,
+               y_direct=combine_direct(tok, b, T, D, L, d, cfg.dtype, out_rows, epd_row, shared))
     if with_bruteforce:
         res["y_bf"] = bruteforce(tok, inp.x, idx, w, inp.w_gate_up, inp.w_down, cfg.dtype, shared)
     return res

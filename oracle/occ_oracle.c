@@ -19,6 +19,9 @@
  *  [OCC-FIG5]   same page, Figure 5 caption: BRIM_0 is [EP devices] x
  *               [ORI tokens]; BRIM_1 is [local experts per device] x
  *               [SFD tokens].
+ *  [OCC-FIG2]   same page, Figure 2 caption: MoE workflows under three
+ *               all-to-all strategies across expert-parallel devices (the
+ *               plain one sends one row per (token, expert) pair).
  *  [CPL-ABS]    "Expert Coupling in MoE Pretraining" (readsearch.ai page),
  *               Abstract: each token is routed to k of E experts; a
  *               dispatcher that sends each token to each GPU once;
@@ -337,6 +340,42 @@ int orc_bruteforce(int ntok, const int32_t *tok, int d, int I, int k, int dt, co
   free(o);
   free(yt);
   return ORC_OK;
+}
+
+/* ---- O10': conventional combine (no deduplication) ------------------------
+ * [OCC-FIG2]: the plain strategy returns every (token, expert) row unreduced
+ * and the source sums them.  For each requested token, in the same walk as
+ * orc_combine (devices ascending, local experts ascending, rows found through
+ * BRIM_0 and BRIM_1) but with no per-device rounding:
+ *   y[t] = round_dtype(shared[t] + sum_r w[r] * out_epd[r])   (fp64 sum) */
+int orc_combine_direct(int ntok, const int32_t *tok, int T, int D, int L, int ld, int d, int dt,
+                       const int32_t *brim0, const int32_t *brim1, const float *epd_w,
+                       const float *out_epd, const int32_t *epd_row, const float *shared,
+                       float *y) {
+  if (ntok < 0 || d <= 0 || D <= 0 || L <= 0) return ORC_EINVAL;
+  double *yt = (double *)malloc(sizeof(double) * (size_t)d);
+  if (!yt) return ORC_EINVAL;
+  int rc = ORC_OK;
+  for (int q = 0; q < ntok && rc == ORC_OK; ++q) {
+    int t = tok[q];
+    if (t < 0 || t >= T) { rc = ORC_EINVAL; break; }
+    for (int c = 0; c < d; ++c) yt[c] = shared ? (double)shared[(size_t)q * d + c] : 0.0;
+    for (int dv = 0; dv < D && rc == ORC_OK; ++dv) {
+      int32_t s = brim0[(size_t)dv * T + t];
+      if (s < 0) continue;
+      for (int l = 0; l < L; ++l) {
+        int32_t r = brim1[(size_t)l * ld + s];
+        if (r < 0) continue;
+        int32_t row = epd_row ? epd_row[r] : r;
+        if (row < 0) { rc = ORC_ECHECK; break; }
+        double wr = (double)epd_w[r];
+        for (int c = 0; c < d; ++c) yt[c] += wr * (double)out_epd[(size_t)row * d + c];
+      }
+    }
+    for (int c = 0; c < d; ++c) y[(size_t)q * d + c] = (float)round_dt(yt[c], dt);
+  }
+  free(yt);
+  return rc;
 }
 
 /* ---- O12: co-activation (collaboration) counts ---------------------------

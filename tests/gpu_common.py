@@ -69,7 +69,9 @@ def oracle_layer(orc, inp, tokens=None):
         shared = orc.shared_rows(inp.x, tok, inp.w_gate_up_sh, inp.w_down_sh, cfg.dtype)
     y, osfd = orc.combine(tok, b, T, D, L, cfg.d, cfg.dtype, out_rows, epd_row, shared,
                           want_sfd=True)
-    res.update(tokens=tok, epd_rows=rows, out_epd_rows=out_rows, shared=shared, y=y, out_sfd=osfd)
+    y_direct = orc.combine_direct(tok, b, T, D, L, cfg.d, cfg.dtype, out_rows, epd_row, shared)
+    res.update(tokens=tok, epd_rows=rows, out_epd_rows=out_rows, shared=shared, y=y, out_sfd=osfd,
+               y_direct=y_direct)
     return res
 
 
@@ -91,7 +93,18 @@ def gpu_layer(inp, runs=1, poison=True):
         names = ["logits", "topk_idx", "topk_w", "brim0", "brim1", "sfd_offset", "slot_offset",
                  "sfd_token", "epd_token", "epd_sfd", "epd_w", "S", "sfd", "epd", "out_epd",
                  "out_sfd", "y", "counts"] + (["shared_out"] if cfg.n_shared else [])
-        outs.append({n: lay.host(n) for n in names})
+        out = {n: lay.host(n) for n in names}
+        # the conventional strategy on the same BRIMs: EPD straight from ORI,
+        # combine without pre-reduction
+        for t in (lay.epd, lay.out_epd, lay.y):
+            t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).fill_(-1)
+        lay.dispatch_direct()
+        lay.expert_ffn()
+        lay.combine_direct()
+        torch.cuda.synchronize()
+        out["epd_direct"] = lay.host("epd")
+        out["y_direct"] = lay.host("y")
+        outs.append(out)
     del lay
     torch.cuda.empty_cache()
     return outs if runs > 1 else outs[0]
@@ -142,6 +155,9 @@ def compare(g, o, inp, full=True):
     srows = np.unique(b["brim0"][:, tok][b["brim0"][:, tok] >= 0])
     assert_close(as_f32(g["out_sfd"][srows], dt), o["out_sfd"][srows], dt, "out_sfd")
     assert_close(as_f32(g["y"][tok], dt), o["y"], dt, "y")
+    if "y_direct" in g:
+        assert np.array_equal(g["epd_direct"], xs[b["epd_token"]]), "epd (direct dispatch)"
+        assert_close(as_f32(g["y_direct"][tok], dt), o["y_direct"], dt, "y (direct combine)")
 
 
 def _flat_pos(idx, b, slot_expert, k):

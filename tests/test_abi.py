@@ -14,8 +14,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 @pytest.fixture(scope="module")
 def occ():
     if not os.path.exists(os.path.join(ROOT, "expert_top_router_amd", "liboccult.so")):
-        from expert_top_router_amd import build
-        build.build()
+        import __graft_entry__
+        __graft_entry__._hip_build_module().build()
     import expert_top_router_amd as occ
     return occ
 
@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(occ):
     names = declared_symbols()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     lib = C.CDLL(occ.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -87,6 +87,21 @@ def test_null_pointers_and_workspace(occ):
     rc = lib.occ_build_brim(C.byref(d), FAKE, FAKE, se.ctypes.data, C.byref(partial), FAKE,
                             need, None)
     assert rc == -1
+
+
+def test_direct_mode_arguments_are_checked(occ):
+    lib = occ.lib()
+    d = _desc(occ)
+    brim = occ.make_brim(brim0=FAKE, brim1=FAKE, slot_offset=FAKE, epd_w=FAKE)
+    assert lib.occ_dispatch_direct(C.byref(d), None, C.byref(brim), FAKE, None) == -1
+    assert lib.occ_dispatch_direct(C.byref(d), FAKE, C.byref(brim), None, None) == -1
+    assert lib.occ_combine_direct(C.byref(d), None, C.byref(brim), None, FAKE, None) == -1
+    assert lib.occ_combine_direct(C.byref(d), FAKE, C.byref(brim), None, None, None) == -1
+    nw = occ.make_brim(brim0=FAKE, brim1=FAKE, slot_offset=FAKE)
+    rc = lib.occ_combine_direct(C.byref(d), FAKE, C.byref(nw), None, FAKE, None)
+    assert rc == -1 and "epd_w" in occ.last_error()
+    bad = _desc(occ, E=10, D=4)
+    assert lib.occ_dispatch_direct(C.byref(bad), FAKE, C.byref(brim), FAKE, None) == -1
 
 
 def test_shared_expert_arguments_are_checked(occ):

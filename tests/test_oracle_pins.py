@@ -311,10 +311,13 @@ def test_identity_expert_combine(orc, renorm):
     b = orc.brim(idx, w, np.arange(E, dtype=np.int32), E, D)
     epd = orc.gather(orc.gather(x, b["sfd_token"][:b["S"]]), b["epd_sfd"])
     y, _ = orc.combine(np.arange(T), b, T, D, E // D, d, "f32", epd)
+    yd = orc.combine_direct(np.arange(T), b, T, D, E // D, d, "f32", epd)
     want = x.astype(np.float64) * w.sum(1, dtype=np.float64)[:, None]
     assert rel_err(y, want) <= 1e-6
+    assert rel_err(yd, want) <= 1e-6
     if renorm:
         assert rel_err(y, x) <= 1e-6
+        assert rel_err(yd, x) <= 1e-6
 
 
 def test_combine_invariant_under_placement(orc):
@@ -325,6 +328,54 @@ def test_combine_invariant_under_placement(orc):
     moved = orc.layer(inp)
     assert np.array_equal(moved["idx"], base["idx"])
     assert rel_err(moved["y"], base["y"]) <= 1e-6
+
+
+# ---------------------------------------------------------------------------
+# O10' the conventional strategy (one row per (token, expert) pair, Occult
+# Figure 2 caption): EPD straight from ORI, combine without pre-reduction
+# ---------------------------------------------------------------------------
+def test_direct_dispatch_is_the_two_stage_gather(orc):
+    """x[epd_token] is bit for bit the ORI -> SFD -> EPD result."""
+    rng = np.random.default_rng(20)
+    T, E, k, D, d = 70, 12, 3, 3, 10
+    x = _f32(rng.standard_normal((T, d)))
+    _, idx, w = orc.route(x, _f32(rng.standard_normal((E, d))), k, 0, "f32")
+    b = orc.brim(idx, w, rng.permutation(E).astype(np.int32), E, D)
+    two = orc.gather(orc.gather(x, b["sfd_token"][:b["S"]]), b["epd_sfd"])
+    one = orc.gather(x, b["epd_token"])
+    assert np.array_equal(one.view(np.uint32), two.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_direct_combine_matches_bruteforce(orc, dtype):
+    """The conventional combine is the standard layer itself: both round one
+    fp64 sum of the same exact products (fp32 weight x dtype output), only
+    the order differs."""
+    cfg = W.CONFIGS["olmoe_bf16"].replace(T=96, d=64, E=16, I=32, D=4, k=4, dtype=dtype)
+    inp = W.make_layer(cfg)
+    r = orc.layer(inp, with_bruteforce=True)
+    if dtype == "bf16":
+        assert np.array_equal(r["y_direct"], r["y_bf"])
+    else:
+        assert rel_err(r["y_direct"], r["y_bf"]) <= 1e-6
+    assert r["S"] < cfg.R  # the Occult path deduplicated; the direct one did not need to
+
+
+def test_direct_combine_drops_no_row(orc):
+    """With out_EPD = 1 in every element and shared = 0, y_direct = sum of
+    the token's k weights (and with renormalised weights exactly 1)."""
+    rng = np.random.default_rng(21)
+    T, E, k, D, d = 40, 8, 3, 2, 4
+    x = _f32(rng.standard_normal((T, d)))
+    for renorm in (0, 1):
+        _, idx, w = orc.route(x, _f32(rng.standard_normal((E, d))), k, renorm, "f32")
+        b = orc.brim(idx, w, np.arange(E, dtype=np.int32), E, D)
+        ones = np.ones((T * k, d), np.float32)
+        y = orc.combine_direct(np.arange(T), b, T, D, E // D, d, "f32", ones)
+        want = np.repeat(w.sum(1, dtype=np.float64)[:, None], d, 1)
+        assert rel_err(y, want) <= 1e-6
+        if renorm:
+            assert np.allclose(y, 1.0, rtol=0, atol=4e-7)
 
 
 # ---------------------------------------------------------------------------
