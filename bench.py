@@ -145,6 +145,28 @@ def conventional(lay, cfg, steps, torch):
             "send_bytes": cfg.R * rowb, "occult_send_bytes": S * rowb}
 
 
+def pruned(cfg, weights, slot_expert, budget, steps, torch):
+    """The layer under collaboration pruning with an all-to-all budget of
+    `budget` devices per token (kept weights rescaled): rows that would be
+    sent and the step time."""
+    from expert_top_router_amd.layer import MoELayer
+    lay = MoELayer(cfg, weights, slot_expert, budget=budget, rescale=1)
+    for _ in range(3):
+        step(lay)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(lay)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    S = int(lay.host("S")[0])
+    Rp = int(lay.host("slot_offset")[cfg.E])
+    del lay
+    return {"budget": budget, "rescale": 1, "sfd_rows": S, "epd_rows": Rp,
+            "sfd_over_tk": S / max(cfg.R, 1), "ms_per_step": elapsed / steps * 1e3,
+            "tokens_per_s": cfg.T * steps / elapsed}
+
+
 def cpu_baseline(inp, n_tok):
     """The oracle as it stands, one thread: routing and BRIMs on the full
     batch, expert FFN and combine on a seeded sample of tokens; tokens/s
@@ -320,6 +342,8 @@ def main():
         "stages": stages,
     }
     out["conventional"] = conventional(lay, cfg, args.steps, torch)
+    if cfg.D >= 4:
+        out["pruned"] = pruned(cfg, lay.w, inp.slot_expert, max(1, cfg.D // 4), args.steps, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

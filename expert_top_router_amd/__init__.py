@@ -51,6 +51,7 @@ def _load(path: str = LIB_PATH):
         "occ_ffn_workspace_bytes": (SZ, [DP]),
         "occ_route_topk": (I32, [DP, P, P, P, P, P, P]),
         "occ_build_brim": (I32, [DP, P, P, P, BP, P, SZ, P]),
+        "occ_build_brim_pruned": (I32, [DP, P, P, P, I32, I32, BP, P, SZ, P]),
         "occ_dispatch": (I32, [DP, P, BP, P, P, P]),
         "occ_expert_ffn": (I32, [DP, P, BP, P, P, P, P, SZ, P, P, P, P, P, P]),
         "occ_expert_up": (I32, [DP, P, BP, P, P, P, SZ, P, P, P]),
@@ -73,6 +74,7 @@ _lib = _load()
 
 # Every symbol the C header declares (checked by the tests).
 EXPORTED = ("occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk", "occ_build_brim",
+            "occ_build_brim_pruned",
             "occ_dispatch", "occ_expert_ffn", "occ_expert_up", "occ_expert_down", "occ_combine",
             "occ_dispatch_direct", "occ_combine_direct", "occ_coactivation", "occ_place_greedy",
             "occ_last_error")
@@ -151,6 +153,16 @@ def occ_build_brim(desc, topk_idx, topk_w, slot_expert_host, brim: occ_brim, ws,
            "occ_build_brim")
 
 
+def occ_build_brim_pruned(desc, topk_idx, topk_w, slot_expert_host, budget, rescale,
+                          brim: occ_brim, ws, ws_bytes, stream=None):
+    import numpy as np
+    se = np.ascontiguousarray(slot_expert_host, dtype=np.int32)
+    _check(_lib.occ_build_brim_pruned(C.byref(desc), _ptr(topk_idx), _ptr(topk_w),
+                                      se.ctypes.data, int(budget), int(rescale), C.byref(brim),
+                                      _ptr(ws), ws_bytes, _stream(stream)),
+           "occ_build_brim_pruned")
+
+
 def occ_dispatch(desc, x, brim: occ_brim, sfd, epd, stream=None):
     _check(_lib.occ_dispatch(C.byref(desc), _ptr(x), C.byref(brim), _ptr(sfd), _ptr(epd),
                              _stream(stream)), "occ_dispatch")
@@ -218,6 +230,6 @@ from .layer import MoELayer  # noqa: E402  (buffers + the call sequence)
 
 __all__ = ["MoELayer", "OccError", "occ_layer_desc", "occ_brim", "make_desc", "desc_of",
            "make_brim", "occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk",
-           "occ_build_brim", "occ_dispatch", "occ_expert_ffn", "occ_expert_up",
+           "occ_build_brim", "occ_build_brim_pruned", "occ_dispatch", "occ_expert_ffn", "occ_expert_up",
            "occ_expert_down", "occ_combine", "occ_dispatch_direct", "occ_combine_direct",
            "occ_coactivation", "occ_place_greedy", "last_error"]

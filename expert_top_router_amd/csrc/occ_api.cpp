@@ -147,9 +147,11 @@ occ_status occ_route_topk(const occ_layer_desc *desc, const void *x, const float
                     "occ_route_topk");
 }
 
-occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *topk_idx,
-                          const float *topk_w, const int32_t *slot_expert_host,
-                          const occ_brim *brim, void *ws, size_t ws_bytes, hipStream_t stream) {
+static occ_status build_brim(const char *name, const occ_layer_desc *desc,
+                             const int32_t *topk_idx, const float *topk_w,
+                             const int32_t *slot_expert_host, const occ_brim *brim, void *ws,
+                             size_t ws_bytes, hipStream_t stream, int32_t budget,
+                             int32_t rescale) {
   OCC_TRY(check_desc(desc));
   OCC_TRY(check_brim(*desc, brim, true));
   const int64_t Tk = (int64_t)desc->T * desc->k;
@@ -161,8 +163,27 @@ occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *topk_idx,
   if (ws == nullptr) return fail(OCC_EINVAL, "workspace is NULL");
   if (ws_bytes < need)
     return fail(OCC_ENOSPC, "workspace of %zu bytes < %zu required", ws_bytes, need);
-  return hip_status(occ::launch_build_brim(*desc, topk_idx, topk_w, pl, *brim, ws, stream),
-                    "occ_build_brim");
+  return hip_status(occ::launch_build_brim(*desc, topk_idx, topk_w, pl, *brim, ws, stream,
+                                           budget, rescale),
+                    name);
+}
+
+occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *topk_idx,
+                          const float *topk_w, const int32_t *slot_expert_host,
+                          const occ_brim *brim, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return build_brim("occ_build_brim", desc, topk_idx, topk_w, slot_expert_host, brim, ws,
+                    ws_bytes, stream, OCC_MAX_D, 0);
+}
+
+occ_status occ_build_brim_pruned(const occ_layer_desc *desc, const int32_t *topk_idx,
+                                 const float *topk_w, const int32_t *slot_expert_host,
+                                 int32_t budget, int32_t rescale, const occ_brim *brim, void *ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  if (desc != nullptr && (budget < 1 || budget > desc->D))
+    return fail(OCC_EINVAL, "budget %d outside 1..D", budget);
+  if (rescale != 0 && rescale != 1) return fail(OCC_EINVAL, "rescale must be 0 or 1");
+  return build_brim("occ_build_brim_pruned", desc, topk_idx, topk_w, slot_expert_host, brim, ws,
+                    ws_bytes, stream, budget, rescale);
 }
 
 occ_status occ_dispatch(const occ_layer_desc *desc, const void *x, const occ_brim *brim,

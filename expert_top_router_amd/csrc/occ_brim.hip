@@ -14,6 +14,16 @@
 //            wave's earlier lanes (ballot) -> BRIM_0, sfd_token, BRIM_1,
 //            epd_token, epd_sfd, epd_w; block 0 writes the offsets and S
 // No atomics, so every output is deterministic.
+//
+// Collaboration pruning under an all-to-all budget (Occult, TL;DR:
+// routing-score-based pruning to minimise the budget C_T): with budget < D a
+// token keeps at most `budget` devices, those with the largest summed routing
+// weight of its selected experts (fp32 sums in top-k order; lower device
+// index on equal sums); its experts on other devices are dropped, and with
+// `rescale` the kept weights are scaled by (sum of all its weights) / (sum of
+// the kept ones) so the token's total gate mass is unchanged.  Counting and
+// filling apply the same rule, so the layouts stay consistent, and EPD then
+// holds fewer than T*k rows (slot_offset[E]).
 #include "occ_internal.h"
 
 namespace occ {
@@ -36,26 +46,83 @@ __device__ __forceinline__ bool slot_bit(const TokenKeys<KMAX> &tk, int g) {
   return (word >> (g & 63)) & 1ull;
 }
 
+struct Prune {
+  int budget;   // devices kept per token (>= D: no pruning)
+  int rescale;  // 1: keep each token's total weight
+};
+
 template <int KMAX>
 __device__ __forceinline__ TokenKeys<KMAX> load_keys(int t, int T, int k, int L,
                                                      const int32_t *idx, const float *w,
-                                                     const Placement &pl) {
+                                                     const Placement &pl, const Prune &pr) {
   TokenKeys<KMAX> tk{};
+  int dev[KMAX];
+  float wt[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     tk.slot[j] = -1;
     tk.w[j] = 0.0f;
+    dev[j] = -1;
+    wt[j] = 0.0f;
     // ids outside [0, OCC_MAX_E) or of no slot are skipped, never used as addresses
     const int e = (t < T && j < k) ? idx[(size_t)t * k + j] : -1;
     const int g = (unsigned)e < (unsigned)OCC_MAX_E ? pl.slot_of[e] : -1;
     if (g >= 0) {
       tk.slot[j] = g;
-      tk.w[j] = w != nullptr ? w[(size_t)t * k + j] : 0.0f;
-      tk.dmask |= 1u << (g / L);
-      const uint64_t bit = 1ull << (g & 63);
-      if (g < 64) tk.slo |= bit;
-      else tk.shi |= bit;
+      dev[j] = g / L;
+      wt[j] = w != nullptr ? w[(size_t)t * k + j] : 0.0f;
     }
+  }
+  float scale = 1.0f;
+  if (pr.budget < OCC_MAX_D) {
+    // score of each pick's device: fp32 sum of the token's weights on it, in pick order
+    float score[KMAX];
+    bool first[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      float sc = 0.0f;
+      bool f = dev[j] >= 0;
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        if (dev[i] == dev[j]) sc += wt[i];
+        if (i < j && dev[i] == dev[j]) f = false;
+      }
+      score[j] = sc;
+      first[j] = f;  // the first pick on its device stands for the device
+    }
+    float total = 0.0f, kept = 0.0f;
+    bool keep[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      keep[j] = false;
+      if (dev[j] < 0) continue;
+      int rank = 0;  // devices ahead of this pick's device
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i)
+        if (first[i] && dev[i] != dev[j] &&
+            (score[i] > score[j] || (score[i] == score[j] && dev[i] < dev[j])))
+          ++rank;
+      keep[j] = rank < pr.budget;
+      total += wt[j];
+      if (keep[j]) kept += wt[j];
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (!keep[j]) dev[j] = -1;  // dropped (or no pick)
+    if (pr.rescale && kept > 0.0f) scale = total / kept;
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (dev[j] < 0) {
+      tk.slot[j] = -1;
+      continue;
+    }
+    const int g = tk.slot[j];
+    tk.w[j] = pr.rescale && pr.budget < OCC_MAX_D ? wt[j] * scale : wt[j];
+    tk.dmask |= 1u << dev[j];
+    const uint64_t bit = 1ull << (g & 63);
+    if (g < 64) tk.slo |= bit;
+    else tk.shi |= bit;
   }
   return tk;
 }
@@ -64,10 +131,13 @@ __device__ __forceinline__ TokenKeys<KMAX> load_keys(int t, int T, int k, int L,
 template <int KMAX>
 __global__ __launch_bounds__(kTB) void brim_count_kernel(int T, int k, int D, int E, int L,
                                                          int nblk, const int32_t *idx,
-                                                         Placement pl, int32_t *cnt) {
+                                                         const float *w, Placement pl, Prune pr,
+                                                         int32_t *cnt) {
   const int lane = threadIdx.x;
   const int t = blockIdx.x * kTB + lane;
-  const TokenKeys<KMAX> tk = load_keys<KMAX>(t, T, k, L, idx, nullptr, pl);
+  // the weights matter for counting only when pruning decides by them
+  const TokenKeys<KMAX> tk =
+      load_keys<KMAX>(t, T, k, L, idx, pr.budget < OCC_MAX_D ? w : nullptr, pl, pr);
   for (int dv = 0; dv < D; ++dv) {
     const uint64_t b = __ballot((tk.dmask >> dv) & 1u);
     if (lane == 0) cnt[(size_t)dv * nblk + blockIdx.x] = __popcll(b);
@@ -128,7 +198,8 @@ __device__ __forceinline__ int32_t wave_exclusive(const int32_t *tot, int n, int
 template <int KMAX>
 __global__ __launch_bounds__(kTB) void brim_fill_kernel(
     int T, int k, int D, int E, int L, int nblk, int ld, const int32_t *idx, const float *w,
-    Placement pl, const int32_t *within, const int32_t *tot, int32_t *brim0, int32_t *brim1,
+    Placement pl, Prune pr, const int32_t *within, const int32_t *tot, int32_t *brim0,
+    int32_t *brim1,
     int32_t *sfd_token, int32_t *epd_token, int32_t *epd_sfd, float *epd_w, int32_t *sfd_offset,
     int32_t *slot_offset, int32_t *S_out) {
   __shared__ int32_t base[OCC_MAX_D + OCC_MAX_E];
@@ -147,7 +218,7 @@ __global__ __launch_bounds__(kTB) void brim_fill_kernel(
   __syncthreads();
   const int t = blockIdx.x * kTB + lane;
   const bool live = t < T;
-  const TokenKeys<KMAX> tk = load_keys<KMAX>(t, T, k, L, idx, w, pl);
+  const TokenKeys<KMAX> tk = load_keys<KMAX>(t, T, k, L, idx, w, pl, pr);
   const uint64_t lt = lanemask_lt();
   for (int dv = 0; dv < D; ++dv) {
     const bool hasd = live && ((tk.dmask >> dv) & 1u);
@@ -186,17 +257,17 @@ size_t brim_count_elems(int T, int D, int E) {
 
 template <int KMAX>
 void launch_kmax(int T, int k, int D, int E, int L, int nblk, int ld, const int32_t *idx,
-                 const float *w, const Placement &pl, const occ_brim &b, int32_t *cnt,
-                 int32_t *tot, hipStream_t st) {
+                 const float *w, const Placement &pl, const Prune &pr, const occ_brim &b,
+                 int32_t *cnt, int32_t *tot, hipStream_t st) {
   if (nblk > 0) {
-    brim_count_kernel<KMAX><<<nblk, kTB, 0, st>>>(T, k, D, E, L, nblk, idx, pl, cnt);
+    brim_count_kernel<KMAX><<<nblk, kTB, 0, st>>>(T, k, D, E, L, nblk, idx, w, pl, pr, cnt);
     brim_keyscan_kernel<<<D + E, kTB, 0, st>>>(nblk, cnt, tot);
   } else {
     // no tokens: every key total is zero
     brim_zero_kernel<<<1, kTB, 0, st>>>(tot, D + E);
   }
   brim_fill_kernel<KMAX><<<nblk > 0 ? nblk : 1, kTB, 0, st>>>(
-      T, k, D, E, L, nblk, ld, idx, w, pl, cnt, tot, b.brim0, b.brim1, b.sfd_token, b.epd_token,
+      T, k, D, E, L, nblk, ld, idx, w, pl, pr, cnt, tot, b.brim0, b.brim1, b.sfd_token, b.epd_token,
       b.epd_sfd, b.epd_w, b.sfd_offset, b.slot_offset, b.S);
 }
 
@@ -207,16 +278,19 @@ size_t brim_workspace_bytes(int T, int D, int E) {
 }
 
 hipError_t launch_build_brim(const occ_layer_desc &Ld, const int32_t *idx, const float *w,
-                             const Placement &pl, const occ_brim &b, void *ws, hipStream_t st) {
+                             const Placement &pl, const occ_brim &b, void *ws, hipStream_t st,
+                             int budget, int rescale) {
   const int T = Ld.T, k = Ld.k, D = Ld.D, E = Ld.E, L = E / D;
   const int nblk = (T + kTB - 1) / kTB;
   const int ld = T * (k < D ? k : D);
   int32_t *cnt = static_cast<int32_t *>(ws);
   int32_t *tot = cnt + brim_count_elems(T, D, E);
-  if (k <= 2) launch_kmax<2>(T, k, D, E, L, nblk, ld, idx, w, pl, b, cnt, tot, st);
-  else if (k <= 4) launch_kmax<4>(T, k, D, E, L, nblk, ld, idx, w, pl, b, cnt, tot, st);
-  else if (k <= 8) launch_kmax<8>(T, k, D, E, L, nblk, ld, idx, w, pl, b, cnt, tot, st);
-  else launch_kmax<16>(T, k, D, E, L, nblk, ld, idx, w, pl, b, cnt, tot, st);
+  // a budget of D or more keeps every device: the unpruned layouts
+  const Prune pr{budget < D ? budget : OCC_MAX_D, rescale};
+  if (k <= 2) launch_kmax<2>(T, k, D, E, L, nblk, ld, idx, w, pl, pr, b, cnt, tot, st);
+  else if (k <= 4) launch_kmax<4>(T, k, D, E, L, nblk, ld, idx, w, pl, pr, b, cnt, tot, st);
+  else if (k <= 8) launch_kmax<8>(T, k, D, E, L, nblk, ld, idx, w, pl, pr, b, cnt, tot, st);
+  else launch_kmax<16>(T, k, D, E, L, nblk, ld, idx, w, pl, pr, b, cnt, tot, st);
   return hipGetLastError();
 }
 

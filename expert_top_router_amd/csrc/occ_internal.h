@@ -75,8 +75,11 @@ hipError_t launch_route_topk(const occ_layer_desc &L, const void *x, const float
 
 // workspace layout of the BRIM build: counts then scanned offsets
 size_t brim_workspace_bytes(int T, int D, int E);
+// budget >= D: the plain layouts; budget < D: collaboration pruning (at most
+// `budget` devices per token, kept weights rescaled when `rescale` is 1)
 hipError_t launch_build_brim(const occ_layer_desc &L, const int32_t *idx, const float *w,
-                             const Placement &pl, const occ_brim &b, void *ws, hipStream_t st);
+                             const Placement &pl, const occ_brim &b, void *ws, hipStream_t st,
+                             int budget, int rescale);
 
 hipError_t launch_dispatch(const occ_layer_desc &L, const void *x, const occ_brim &b, void *sfd,
                            void *epd, hipStream_t st);

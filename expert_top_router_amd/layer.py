@@ -12,7 +12,8 @@ from typing import Optional
 
 import numpy as np
 
-from . import (desc_of, make_brim, occ_build_brim, occ_coactivation, occ_combine,
+from . import (desc_of, make_brim, occ_build_brim, occ_build_brim_pruned, occ_coactivation,
+               occ_combine,
                occ_combine_direct, occ_dispatch, occ_dispatch_direct, occ_expert_down,
                occ_expert_ffn, occ_expert_up, occ_ffn_workspace_bytes, occ_route_topk,
                occ_workspace_bytes)
@@ -54,9 +55,14 @@ class MoELayer:
     """All device buffers of one layer configuration (duck-typed ``cfg`` with
     T, d, E, I, k, D, dtype, renorm, n_shared, I_shared)."""
 
-    def __init__(self, cfg, weights: Weights, slot_expert, with_logits=False, device="cuda"):
+    def __init__(self, cfg, weights: Weights, slot_expert, with_logits=False, device="cuda",
+                 budget=None, rescale=1):
+        """budget: None for the exact layer, else the all-to-all budget of
+        collaboration pruning (devices kept per token, occ_build_brim_pruned)."""
         torch = _torch()
         self.cfg = cfg
+        self.budget = budget
+        self.rescale = rescale
         self.desc = desc_of(cfg)
         self.slot_expert = np.ascontiguousarray(slot_expert, dtype=np.int32)
         self.w = weights
@@ -106,8 +112,13 @@ class MoELayer:
                        self.logits, stream)
 
     def build_brim(self, stream=None):
-        occ_build_brim(self.desc, self.topk_idx, self.topk_w, self.slot_expert, self.brim,
-                       self.ws, self.ws_bytes, stream)
+        if self.budget is None:
+            occ_build_brim(self.desc, self.topk_idx, self.topk_w, self.slot_expert, self.brim,
+                           self.ws, self.ws_bytes, stream)
+        else:
+            occ_build_brim_pruned(self.desc, self.topk_idx, self.topk_w, self.slot_expert,
+                                  self.budget, self.rescale, self.brim, self.ws, self.ws_bytes,
+                                  stream)
 
     def dispatch(self, stream=None):
         occ_dispatch(self.desc, self.w.x, self.brim, self.sfd, self.epd, stream)

@@ -134,6 +134,24 @@ occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *topk_idx,
                           const float *topk_w, const int32_t *slot_expert_host,
                           const occ_brim *brim, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* BRIM build under an all-to-all budget: routing-score-based collaboration
+ * pruning (Occult, TL;DR: pruning by routing score to minimise the budget
+ * C_T).  The pages give no exact rule; this one is used: each token keeps at
+ * most `budget` devices (1 <= budget <= D), those with the largest summed
+ * routing weight of the token's selected experts (fp32 sums in top-k order,
+ * lower device index on equal sums); its selections on the other devices are
+ * dropped.  rescale = 1 multiplies each kept weight by (sum of the token's
+ * weights) / (sum of its kept weights), both fp32 sums in top-k order;
+ * rescale = 0 keeps the weights.  Outputs as occ_build_brim, except that EPD
+ * holds R' = slot_offset[E] <= T*k rows (epd_token, epd_sfd, epd_w valid
+ * below R'); budget = D gives exactly occ_build_brim's result.  Every later
+ * call works on the pruned layouts unchanged.  EINVAL for a budget outside
+ * 1..D or rescale outside {0, 1}. */
+occ_status occ_build_brim_pruned(const occ_layer_desc *desc, const int32_t *topk_idx,
+                                 const float *topk_w, const int32_t *slot_expert_host,
+                                 int32_t budget, int32_t rescale, const occ_brim *brim, void *ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
 /* Dispatch ORI -> SFD -> EPD (Occult, Figure 4 caption): bit copies
  *   sfd[s] = x[sfd_token[s]]  (dtype [S_max][d], rows < S written): the
  *            all-to-all send buffer, grouped by device

@@ -116,8 +116,21 @@ def route(x, wr, k, renorm, dtype):
     return lg, idx, w
 
 
+def prune(idx, w, slot_expert, E, D, budget, rescale):
+    """O5': routing-score-based pruning to at most ``budget`` devices per
+    token; dropped selections come back as idx -1, w 0."""
+    T, k = idx.shape
+    io = np.empty((T, k), np.int32)
+    wo = np.empty((T, k), np.float32)
+    _check(lib().orc_prune(T, k, E, D, _p(_i32(slot_expert)), int(budget), int(rescale),
+                           _p(_i32(idx)), _p(_f32(w)), _p(io), _p(wo)), "prune")
+    return io, wo
+
+
 def brim(idx, w, slot_expert, E, D):
-    """O4-O6: BRIM_0, BRIM_1 (ld = T*min(k, D)), offsets, SFD/EPD index arrays."""
+    """O4-O6: BRIM_0, BRIM_1 (ld = T*min(k, D)), offsets, SFD/EPD index arrays.
+    idx entries of -1 (pairs dropped by pruning) are skipped; EPD then has
+    R' = slot_offset[E] rows."""
     T, k = idx.shape
     L = E // D
     ld = T * min(k, D)
@@ -135,9 +148,11 @@ def brim(idx, w, slot_expert, E, D):
     _check(rc, "brim")
     out["S"] = int(S[0])
     out["ld"] = ld
-    out["epd_token"] = out["epd_token"][:R]
-    out["epd_sfd"] = out["epd_sfd"][:R]
-    out["epd_w"] = out["epd_w"][:R]
+    Rp = int(out["slot_offset"][E])
+    out["R"] = Rp
+    out["epd_token"] = out["epd_token"][:Rp]
+    out["epd_sfd"] = out["epd_sfd"][:Rp]
+    out["epd_w"] = out["epd_w"][:Rp]
     return out
 
 
@@ -248,7 +263,7 @@ def intra_share(Cm, slot_expert, D):
 
 
 # ---------------------------------------------------------------------------
-def layer(inp, tokens=None, with_bruteforce=False):
+def layer(inp, tokens=None, with_bruteforce=False, budget=None, rescale=1):
     """Whole layer on the inputs of ``workloads.make_layer`` (duck-typed).
 
     Routing, BRIMs, gathers and co-activation always run on the full batch.
@@ -258,9 +273,12 @@ def layer(inp, tokens=None, with_bruteforce=False):
     T, d, E, k, D = cfg.T, cfg.d, cfg.E, cfg.k, cfg.D
     L = E // D
     lg, idx, w = route(inp.x, inp.w_router, k, cfg.renorm, cfg.dtype)
+    res = dict(logits=lg, idx=idx, w=w, coact=coactivation(idx, E))
+    if budget is not None:  # collaboration pruning: the layer runs on the kept pairs
+        idx, w = prune(idx, w, inp.slot_expert, E, D, budget, rescale)
+        res.update(idx_kept=idx, w_kept=w)
     b = brim(idx, w, inp.slot_expert, E, D)
-    res = dict(logits=lg, idx=idx, w=w, brim=b, S=b["S"],
-               coact=coactivation(idx, E))
+    res.update(brim=b, S=b["S"])
     if inp.w_gate_up is None:
         return res
     tok = np.arange(T, dtype=np.int32) if tokens is None else _i32(tokens)

@@ -165,7 +165,10 @@ int orc_brim(int T, int k, int E, int D, const int32_t *idx, const float *w,
     sfd_offset[dv] = s;
     for (int t = 0; t < T; ++t) {
       int hit = 0;
-      for (int j = 0; j < k; ++j) if (dev_of[idx[(size_t)t * k + j]] == dv) hit = 1;
+      for (int j = 0; j < k; ++j) {
+        int e = idx[(size_t)t * k + j];
+        if (e >= 0 && dev_of[e] == dv) hit = 1;  /* e < 0: a pair dropped by pruning */
+      }
       if (hit) {
         brim0[(size_t)dv * T + t] = s;
         sfd_token[s] = t;
@@ -199,7 +202,75 @@ int orc_brim(int T, int k, int E, int D, const int32_t *idx, const float *w,
   }
   slot_offset[E] = r;
   free(dev_of);
-  return r == T * k ? ORC_OK : ORC_ECHECK; /* dropless: exactly T*k EPD rows */
+  /* dropless: one EPD row per selected pair, T*k unless pruning dropped some */
+  int32_t pairs = 0;
+  for (size_t q = 0; q < (size_t)T * k; ++q) pairs += idx[q] >= 0;
+  return r == pairs ? ORC_OK : ORC_ECHECK;
+}
+
+/* ---- O5': routing-score-based collaboration pruning ------------------------
+ * [OCC-TLDR]: pruning by routing score to minimise the all-to-all budget C_T.
+ * The pages give no exact rule; the reading: each token is sent to at most
+ * `budget` devices.  A device's score is the fp32 sum, in top-k order, of
+ * the token's routing weights on experts it holds; devices are ranked by
+ * score (descending, lower device index first) and the first `budget` kept.
+ * Selections on other devices become idx = -1, w = 0.  With rescale, each
+ * kept weight is multiplied by total / kept (fp32 sums in top-k order of all
+ * and of the kept weights), so the token's gate mass is unchanged. */
+int orc_prune(int T, int k, int E, int D, const int32_t *slot_expert, int budget, int rescale,
+              const int32_t *idx, const float *w, int32_t *idx_out, float *w_out) {
+  if (T < 0 || k <= 0 || E <= 0 || D <= 0 || E % D != 0 || budget < 1) return ORC_EINVAL;
+  const int L = E / D;
+  int32_t *dev_of = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+  float *score = (float *)malloc(sizeof(float) * (size_t)D);
+  int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)D);
+  int32_t *keep = (int32_t *)malloc(sizeof(int32_t) * (size_t)D);
+  if (!dev_of || !score || !order || !keep) {
+    free(dev_of); free(score); free(order); free(keep);
+    return ORC_EINVAL;
+  }
+  for (int g = 0; g < E; ++g) dev_of[slot_expert[g]] = g / L;
+  for (int t = 0; t < T; ++t) {
+    const int32_t *it = idx + (size_t)t * k;
+    const float *wt = w + (size_t)t * k;
+    int n = 0; /* the token's devices, in first-pick order */
+    for (int dv = 0; dv < D; ++dv) { score[dv] = 0.0f; keep[dv] = 0; }
+    for (int j = 0; j < k; ++j) {
+      int dv = dev_of[it[j]];
+      int seen = 0;
+      for (int q = 0; q < n; ++q) if (order[q] == dv) seen = 1;
+      if (!seen) order[n++] = dv;
+      score[dv] = score[dv] + wt[j];
+    }
+    /* selection of the best `budget` devices: (score desc, device asc) */
+    for (int c = 0; c < budget && c < n; ++c) {
+      int best = -1;
+      for (int q = 0; q < n; ++q) {
+        int dv = order[q];
+        if (keep[dv]) continue;
+        if (best < 0 || score[dv] > score[best] || (score[dv] == score[best] && dv < best))
+          best = dv;
+      }
+      keep[best] = 1;
+    }
+    float total = 0.0f, kept = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      total = total + wt[j];
+      if (keep[dev_of[it[j]]]) kept = kept + wt[j];
+    }
+    float scale = (rescale && kept > 0.0f) ? total / kept : 1.0f;
+    for (int j = 0; j < k; ++j) {
+      if (keep[dev_of[it[j]]]) {
+        idx_out[(size_t)t * k + j] = it[j];
+        w_out[(size_t)t * k + j] = rescale ? wt[j] * scale : wt[j];
+      } else {
+        idx_out[(size_t)t * k + j] = -1;
+        w_out[(size_t)t * k + j] = 0.0f;
+      }
+    }
+  }
+  free(dev_of); free(score); free(order); free(keep);
+  return ORC_OK;
 }
 
 /* ---- O8-O9: expert networks ---------------------------------------------
@@ -331,6 +402,7 @@ int orc_bruteforce(int ntok, const int32_t *tok, int d, int I, int k, int dt, co
     for (int c = 0; c < d; ++c) yt[c] = shared ? (double)shared[(size_t)q * d + c] : 0.0;
     for (int j = 0; j < k; ++j) {
       int32_t e = idx[(size_t)t * k + j];
+      if (e < 0) continue; /* a selection dropped by pruning */
       orc_expert_rows(1, &tok[q], &e, d, I, dt, x, wgu, wdn, o);
       double wj = (double)w[(size_t)t * k + j];
       for (int c = 0; c < d; ++c) yt[c] += wj * (double)o[c];

@@ -37,16 +37,26 @@ def oracle_expert_rows_parallel(orc, x, tok, ex, wgu, wdn, dtype, parts=16):
                                                                             np.float32)
 
 
-def oracle_layer(orc, inp, tokens=None):
+def oracle_layer(orc, inp, tokens=None, budget=None, rescale=1, w_route=None):
     """Oracle results; routing, BRIMs and counts on the full batch, expert
-    arithmetic for ``tokens`` (all by default) and their EPD rows."""
+    arithmetic for ``tokens`` (all by default) and their EPD rows.  With a
+    budget the BRIMs are built from the pruned selections.  Pruning decides
+    by fp32 sums of the routing weights, so ``w_route`` (the GPU's own
+    weights, checked against the oracle's softmax separately) is what both
+    sides prune from."""
     cfg = inp.cfg
     T, E, k, D = cfg.T, cfg.E, cfg.k, cfg.D
     L = E // D
     lg = oracle_logits_parallel(orc, inp.x, inp.w_router, cfg.dtype)
     idx, w = orc.topk(lg, k, cfg.renorm)
-    b = orc.brim(idx, w, inp.slot_expert, E, D)
-    res = dict(logits=lg, idx=idx, w=w, brim=b, coact=orc.coactivation(idx, E))
+    res = dict(logits=lg, idx=idx, w=w, coact=orc.coactivation(idx, E), budget=budget)
+    if budget is None:
+        b = orc.brim(idx, w, inp.slot_expert, E, D)
+    else:
+        ik, wk = orc.prune(idx, w if w_route is None else w_route, inp.slot_expert, E, D,
+                           budget, rescale)
+        b = orc.brim(ik, wk, inp.slot_expert, E, D)
+    res["brim"] = b
     if inp.w_gate_up is None:
         return res
     tok = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
@@ -75,12 +85,13 @@ def oracle_layer(orc, inp, tokens=None):
     return res
 
 
-def gpu_layer(inp, runs=1, poison=True):
+def gpu_layer(inp, runs=1, poison=True, budget=None, rescale=1):
     """Run the HIP layer (forward + co-activation) and fetch every buffer."""
     import torch
     from expert_top_router_amd.layer import MoELayer, upload_inputs
     cfg = inp.cfg
-    lay = MoELayer(cfg, upload_inputs(inp), inp.slot_expert, with_logits=True)
+    lay = MoELayer(cfg, upload_inputs(inp), inp.slot_expert, with_logits=True, budget=budget,
+                   rescale=rescale)
     outs = []
     for _ in range(runs):
         if poison:
@@ -124,26 +135,32 @@ def compare(g, o, inp, full=True):
     assert np.array_equal(g["topk_idx"], o["idx"]), "topk_idx"
     assert_close(g["topk_w"], o["w"], "f32", "topk_w")
     b = o["brim"]
-    S = b["S"]
+    S, Rp = b["S"], b["R"]
+    pruned = o.get("budget") is not None
     assert int(g["S"][0]) == S, ("S", int(g["S"][0]), S)
     for name in ("brim0", "sfd_offset", "slot_offset"):
         assert np.array_equal(g[name], b[name]), name
     assert np.array_equal(g["brim1"][:, :S], b["brim1"][:, :S]), "brim1"
     assert np.array_equal(g["sfd_token"][:S], b["sfd_token"][:S]), "sfd_token"
-    assert np.array_equal(g["epd_token"], b["epd_token"]), "epd_token"
-    assert np.array_equal(g["epd_sfd"], b["epd_sfd"]), "epd_sfd"
-    # epd_w is a copy of the GPU's own routing weights
-    assert np.array_equal(g["epd_w"], g["topk_w"].reshape(-1)[
-        _flat_pos(g["topk_idx"], b, inp.slot_expert, k)]), "epd_w copy"
+    assert np.array_equal(g["epd_token"][:Rp], b["epd_token"]), "epd_token"
+    assert np.array_equal(g["epd_sfd"][:Rp], b["epd_sfd"]), "epd_sfd"
+    if pruned:
+        # the same fp32 scores and rescaling on both sides: bit for bit
+        assert np.array_equal(g["epd_w"][:Rp].view(np.uint32), b["epd_w"].view(np.uint32)), \
+            "epd_w (pruned)"
+    else:
+        # epd_w is a copy of the GPU's own routing weights
+        assert np.array_equal(g["epd_w"], g["topk_w"].reshape(-1)[
+            _flat_pos(g["topk_idx"], b, inp.slot_expert, k)]), "epd_w copy"
     assert np.array_equal(g["counts"], o["coact"]), "coactivation"
     # dispatch: bit copies
     xs = inp.x
     assert np.array_equal(g["sfd"][:S], xs[b["sfd_token"][:S]]), "sfd"
-    assert np.array_equal(g["epd"], xs[b["epd_token"]]), "epd"
+    assert np.array_equal(g["epd"][:Rp], xs[b["epd_token"]]), "epd"
     gb = dict(brim0=g["brim0"], brim1=g["brim1"], sfd_offset=g["sfd_offset"],
               slot_offset=g["slot_offset"], sfd_token=g["sfd_token"], epd_token=g["epd_token"],
               epd_sfd=g["epd_sfd"], epd_w=g["epd_w"], S=S)
-    if full:
+    if full and not pruned:
         check_brim_invariants(gb, g["topk_idx"], g["topk_w"], inp.slot_expert, E, D)
     if "y" not in o:
         return
@@ -156,7 +173,7 @@ def compare(g, o, inp, full=True):
     assert_close(as_f32(g["out_sfd"][srows], dt), o["out_sfd"][srows], dt, "out_sfd")
     assert_close(as_f32(g["y"][tok], dt), o["y"], dt, "y")
     if "y_direct" in g:
-        assert np.array_equal(g["epd_direct"], xs[b["epd_token"]]), "epd (direct dispatch)"
+        assert np.array_equal(g["epd_direct"][:Rp], xs[b["epd_token"]]), "epd (direct dispatch)"
         assert_close(as_f32(g["y_direct"][tok], dt), o["y_direct"], dt, "y (direct combine)")
 
 

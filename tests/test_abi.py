@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(occ):
     names = declared_symbols()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     lib = C.CDLL(occ.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -87,6 +87,22 @@ def test_null_pointers_and_workspace(occ):
     rc = lib.occ_build_brim(C.byref(d), FAKE, FAKE, se.ctypes.data, C.byref(partial), FAKE,
                             need, None)
     assert rc == -1
+
+
+def test_pruned_brim_arguments_are_checked(occ):
+    lib = occ.lib()
+    d = _desc(occ)  # D = 2
+    brim = occ.make_brim(brim0=FAKE, brim1=FAKE, sfd_offset=FAKE, slot_offset=FAKE,
+                         sfd_token=FAKE, epd_token=FAKE, epd_sfd=FAKE, epd_w=FAKE, S=FAKE)
+    se = np.arange(8, dtype=np.int32)
+    need = occ.occ_workspace_bytes(d)
+    for budget, rescale in [(0, 1), (3, 1), (-1, 0), (1, 2)]:
+        rc = lib.occ_build_brim_pruned(C.byref(d), FAKE, FAKE, se.ctypes.data, budget, rescale,
+                                       C.byref(brim), FAKE, need, None)
+        assert rc == -1, (budget, rescale)
+    rc = lib.occ_build_brim_pruned(C.byref(d), FAKE, FAKE, se.ctypes.data, 1, 1, C.byref(brim),
+                                   FAKE, need - 1, None)
+    assert rc == -3
 
 
 def test_direct_mode_arguments_are_checked(occ):

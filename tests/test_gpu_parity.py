@@ -90,6 +90,22 @@ def test_coactivation_accumulates(orc):
     assert np.array_equal(lay.host("counts"), 2 * o["coact"])
 
 
+@pytest.mark.parametrize("name,budget,rescale", [
+    ("bf16_ragged", 1, 1), ("bf16_ragged", 2, 0), ("bf16_ragged", 3, 1),
+    ("bf16_e128_pairs", 2, 1), ("f32_e12", 1, 1), ("bf16_shared", 1, 1),
+])
+def test_pruned_layer_parity(orc, name, budget, rescale):
+    """Collaboration pruning under an all-to-all budget: the pruned BRIMs and
+    rescaled weights bit for bit, the layer (both strategies) by tolerance."""
+    cfg = SMALL[name]
+    say(f"case pruned {name} budget={budget} rescale={rescale}")
+    inp = W.make_layer(cfg, seed=7)
+    g = gpu_layer(inp, budget=budget, rescale=rescale)
+    o = oracle_layer(orc, inp, budget=budget, rescale=rescale, w_route=g["topk_w"])
+    assert o["brim"]["R"] < cfg.R  # pairs were dropped
+    compare(g, o, inp)
+
+
 FULL = ["tiny_fp32", "olmoe_bf16", "mixtral_bf16", "dsv2lite_bf16", "stress_bf16"]
 
 
@@ -120,3 +136,17 @@ def test_full_size_layer_parity(orc, name):
     g = gpu_layer(inp)
     compare(g, o, inp, full=False)
     say(f"case full {name}: S={o['brim']['S']} of T*k={cfg.R}")
+
+
+def test_full_size_pruned_layer_parity(orc):
+    """The OLMoE-shaped layer under a budget of 2 of its 8 devices."""
+    cfg = W.CONFIGS["olmoe_bf16"]
+    say("case full pruned olmoe_bf16 budget=2: generating inputs")
+    inp = W.make_layer(cfg, seed=0)
+    g = gpu_layer(inp, budget=2)
+    o_route = oracle_layer(orc, W.LayerInputs(cfg, inp.x, inp.w_router, None, None, None, None,
+                                              inp.slot_expert), budget=2, w_route=g["topk_w"])
+    tok = _sample_tokens(cfg, o_route["brim"])
+    o = oracle_layer(orc, inp, tokens=tok, budget=2, w_route=g["topk_w"])
+    compare(g, o, inp, full=False)
+    say(f"case full pruned: S={o['brim']['S']}, R'={o['brim']['R']} of T*k={cfg.R}")

@@ -379,6 +379,86 @@ def test_direct_combine_drops_no_row(orc):
 
 
 # ---------------------------------------------------------------------------
+# O5' routing-score-based collaboration pruning (Occult TL;DR, budget C_T)
+# ---------------------------------------------------------------------------
+def test_prune_hand_worked(orc):
+    from fractions import Fraction
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "prune_budget.json")))
+    idx = np.array(g["idx"], np.int32)
+    w = np.array(g["w"], np.float32)
+    se = np.array(g["slot_expert"], np.int32)
+    for case in g["cases"]:
+        io, wo = orc.prune(idx, w, se, g["E"], g["D"], case["budget"], case["rescale"])
+        assert np.array_equal(io, np.array(case["idx"], np.int32)), case
+        want = np.array([[float(Fraction(v)) for v in row] for row in case["w"]])
+        assert np.allclose(wo, want, rtol=1e-6, atol=0), case
+        b = orc.brim(io, wo, se, g["E"], g["D"])
+        assert b["S"] == case["S"] and b["R"] == case["R"], case
+        check_brim_invariants_pruned(b, io, g["D"], g["E"], se)
+
+
+def check_brim_invariants_pruned(b, io, D, E, se):
+    """Every kept (token, device) pair has one SFD row and every kept
+    (token, expert) pair one EPD row; dropped pairs have none."""
+    T, k = io.shape
+    L = E // D
+    dev_of = np.empty(E, np.int64)
+    dev_of[se] = np.arange(E) // L
+    for t in range(T):
+        kept = io[t][io[t] >= 0]
+        devs = set(dev_of[kept].tolist())
+        for dv in range(D):
+            assert (b["brim0"][dv, t] >= 0) == (dv in devs)
+    pairs = sorted((int(t), int(e)) for t in range(T) for e in io[t] if e >= 0)
+    ex_of_row = np.repeat(se, np.diff(b["slot_offset"]))
+    got = sorted(zip(b["epd_token"].tolist(), ex_of_row.tolist()))
+    assert got == pairs
+
+
+def test_prune_keeps_the_heaviest_devices_brute_force(orc):
+    """The kept devices carry the largest summed weight of any device subset
+    of the budget's size (checked over all subsets), and rescaling keeps the
+    token's total weight."""
+    rng = np.random.default_rng(30)
+    for E, D, k, budget in [(8, 4, 3, 1), (12, 4, 4, 2), (16, 8, 6, 3), (6, 3, 3, 2)]:
+        T = 60
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        w = _f32(rng.dirichlet(np.ones(k), size=T))
+        se = rng.permutation(E).astype(np.int32)
+        io, wo = orc.prune(idx, w, se, E, D, budget, 1)
+        L = E // D
+        dev_of = np.empty(E, np.int64)
+        dev_of[se] = np.arange(E) // L
+        for t in range(T):
+            sums = {}
+            for e, wt in zip(idx[t], w[t].astype(np.float64)):
+                sums[int(dev_of[e])] = sums.get(int(dev_of[e]), 0.0) + wt
+            m = min(budget, len(sums))
+            best = max(sum(sums[dv] for dv in c) for c in itertools.combinations(sums, m))
+            kept = {int(dev_of[e]) for e in io[t] if e >= 0}
+            assert len(kept) == m
+            assert abs(sum(sums[dv] for dv in kept) - best) <= 1e-6
+            assert abs(float(wo[t].sum(dtype=np.float64)) - float(w[t].sum(dtype=np.float64))) <= 1e-6
+            assert np.all(wo[t][io[t] < 0] == 0)
+        # a budget of D changes nothing
+        io_d, wo_d = orc.prune(idx, w, se, E, D, D, 1)
+        assert np.array_equal(io_d, idx) and np.array_equal(wo_d, w)
+
+
+def test_pruned_layer_is_the_standard_layer_on_the_kept_pairs(orc):
+    cfg = W.CONFIGS["olmoe_bf16"].replace(T=96, d=64, E=16, I=32, D=4, k=4, dtype="f32")
+    inp = W.make_layer(cfg)
+    full = orc.layer(inp)
+    for budget in (1, 2, 3):
+        r = orc.layer(inp, with_bruteforce=True, budget=budget)
+        assert rel_err(r["y"], r["y_bf"]) <= 1e-6
+        assert rel_err(r["y_direct"], r["y_bf"]) <= 1e-6
+        assert r["S"] <= budget * cfg.T and r["S"] <= full["S"]
+        assert r["brim"]["R"] < cfg.R
+        assert (r["brim"]["brim0"] >= 0).sum(0).max() <= budget
+
+
+# ---------------------------------------------------------------------------
 # O12 co-activation and placement
 # ---------------------------------------------------------------------------
 def test_coactivation_brute_force_and_sums(orc):
