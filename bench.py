@@ -167,6 +167,56 @@ def pruned(cfg, weights, slot_expert, budget, steps, torch):
             "tokens_per_s": cfg.T * steps / elapsed}
 
 
+def affinity(cfg, lay, torch):
+    """Cross-layer affinity on a synthetic two-layer stack (the layer's tokens
+    through a second, independently drawn router): counts from a calibration
+    batch (token seed 1), then the share of the next layer's assignments
+    served on the token's device, for plain sharding (t * D / T) and for the
+    predicted home devices, and the time of each call."""
+    import expert_top_router_amd as occ
+    import workloads as W
+    from expert_top_router_amd.layer import router_f32, to_device
+    T, E, k, D = cfg.T, cfg.E, cfg.k, cfg.D
+    dsc = occ.desc_of(cfg)
+    routers = [to_device(router_f32(W.make_router(cfg, seed=0, layer=l))) for l in (0, 1)]
+    batches = [lay.w.x, to_device(W.make_tokens(cfg, seed=0, token_seed=1))]
+    idx = {}
+    for b, xb in enumerate(batches):
+        for l in (0, 1):
+            i = torch.empty((T, k), dtype=torch.int32, device="cuda")
+            wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+            occ.occ_route_topk(dsc, xb, routers[l], i, wt)
+            idx[(b, l)] = i
+    A = torch.empty((E, E), dtype=torch.int32, device="cuda")
+    home = torch.empty(T, dtype=torch.int32, device="cuda")
+    hits = torch.empty(1, dtype=torch.int32, device="cuda")
+    shard = (torch.arange(T, device="cuda", dtype=torch.int64) * D // T).to(torch.int32)
+    se2 = np.asarray(W.contiguous_placement(cfg), dtype=np.int32)
+    calls = {
+        "cross_coactivation": lambda: occ.occ_cross_coactivation(T, k, E, idx[(1, 0)], k, E,
+                                                                 idx[(1, 1)], A),
+        "home_device": lambda: occ.occ_home_device(T, k, E, idx[(0, 0)], E, D, se2, A, home),
+        "local_hits": lambda: occ.occ_local_hits(T, k, E, idx[(0, 1)], D, se2, home, hits),
+    }
+    us = {}
+    for name, fn in calls.items():
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(10):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        us[name + "_us"] = ev[0].elapsed_time(ev[1]) * 1e3 / 10
+    predicted = int(hits.cpu()[0])
+    occ.occ_local_hits(T, k, E, idx[(0, 1)], D, se2, shard, hits)
+    torch.cuda.synchronize()
+    sharded = int(hits.cpu()[0])
+    return {"layers": 2, "calibration": "token seed 1", "placement": "contiguous",
+            "sharded_local_share": sharded / (T * k), "predicted_local_share": predicted / (T * k),
+            **us}
+
+
 def cpu_baseline(inp, n_tok):
     """The oracle as it stands, one thread: routing and BRIMs on the full
     batch, expert FFN and combine on a seeded sample of tokens; tokens/s
@@ -344,6 +394,7 @@ def main():
     out["conventional"] = conventional(lay, cfg, args.steps, torch)
     if cfg.D >= 4:
         out["pruned"] = pruned(cfg, lay.w, inp.slot_expert, max(1, cfg.D // 4), args.steps, torch)
+    out["affinity"] = affinity(cfg, lay, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

@@ -60,6 +60,9 @@ def _load(path: str = LIB_PATH):
         "occ_dispatch_direct": (I32, [DP, P, BP, P, P]),
         "occ_combine_direct": (I32, [DP, P, BP, P, P, P]),
         "occ_coactivation": (I32, [DP, P, P, I32, P]),
+        "occ_cross_coactivation": (I32, [I32, I32, I32, P, I32, I32, P, P, I32, P]),
+        "occ_home_device": (I32, [I32, I32, I32, P, I32, I32, P, P, P, P]),
+        "occ_local_hits": (I32, [I32, I32, I32, P, I32, P, P, P, I32, P]),
         "occ_place_greedy": (I32, [I32, I32, P, P]),
         "occ_last_error": (C.c_char_p, []),
     }
@@ -76,7 +79,8 @@ _lib = _load()
 EXPORTED = ("occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk", "occ_build_brim",
             "occ_build_brim_pruned",
             "occ_dispatch", "occ_expert_ffn", "occ_expert_up", "occ_expert_down", "occ_combine",
-            "occ_dispatch_direct", "occ_combine_direct", "occ_coactivation", "occ_place_greedy",
+            "occ_dispatch_direct", "occ_combine_direct", "occ_coactivation",
+            "occ_cross_coactivation", "occ_home_device", "occ_local_hits", "occ_place_greedy",
             "occ_last_error")
 
 
@@ -217,6 +221,27 @@ def occ_coactivation(desc, topk_idx, counts, accumulate=0, stream=None):
                                  _stream(stream)), "occ_coactivation")
 
 
+def occ_cross_coactivation(T, k1, E1, idx1, k2, E2, idx2, counts, accumulate=0, stream=None):
+    _check(_lib.occ_cross_coactivation(T, k1, E1, _ptr(idx1), k2, E2, _ptr(idx2), _ptr(counts),
+                                       int(accumulate), _stream(stream)),
+           "occ_cross_coactivation")
+
+
+def occ_home_device(T, k1, E1, idx1, E2, D, slot_expert2_host, affinity, home, stream=None):
+    import numpy as np
+    se = np.ascontiguousarray(slot_expert2_host, dtype=np.int32)
+    _check(_lib.occ_home_device(T, k1, E1, _ptr(idx1), E2, D, se.ctypes.data, _ptr(affinity),
+                                _ptr(home), _stream(stream)), "occ_home_device")
+
+
+def occ_local_hits(T, k2, E2, idx2, D, slot_expert2_host, home, hits, accumulate=0,
+                   stream=None):
+    import numpy as np
+    se = np.ascontiguousarray(slot_expert2_host, dtype=np.int32)
+    _check(_lib.occ_local_hits(T, k2, E2, _ptr(idx2), D, se.ctypes.data, _ptr(home), _ptr(hits),
+                               int(accumulate), _stream(stream)), "occ_local_hits")
+
+
 def occ_place_greedy(E: int, D: int, counts_host):
     """Host greedy placement: returns slot_expert (numpy int32 [E])."""
     import numpy as np
@@ -232,4 +257,5 @@ __all__ = ["MoELayer", "OccError", "occ_layer_desc", "occ_brim", "make_desc", "d
            "make_brim", "occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk",
            "occ_build_brim", "occ_build_brim_pruned", "occ_dispatch", "occ_expert_ffn", "occ_expert_up",
            "occ_expert_down", "occ_combine", "occ_dispatch_direct", "occ_combine_direct",
-           "occ_coactivation", "occ_place_greedy", "last_error"]
+           "occ_coactivation", "occ_cross_coactivation", "occ_home_device", "occ_local_hits",
+           "occ_place_greedy", "last_error"]

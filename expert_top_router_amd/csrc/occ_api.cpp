@@ -327,6 +327,72 @@ occ_status occ_coactivation(const occ_layer_desc *desc, const int32_t *topk_idx,
                     "occ_coactivation");
 }
 
+// ---- cross-layer affinity -------------------------------------------------
+static occ_status check_routing(const char *what, int32_t T, int32_t k, int32_t E,
+                                const int32_t *idx) {
+  if (T < 0 || k < 1 || E < 1 || k > E) return fail(OCC_EINVAL, "%s: bad T=%d k=%d E=%d", what, T, k, E);
+  if (E > OCC_MAX_E || k > OCC_MAX_K)
+    return fail(OCC_EUNSUP, "%s: E=%d or k=%d beyond the supported maximum", what, E, k);
+  if ((int64_t)T * k > INT32_MAX) return fail(OCC_EUNSUP, "%s: T*k beyond int32", what);
+  if (T > 0 && idx == nullptr) return fail(OCC_EINVAL, "%s: selections are NULL", what);
+  return OCC_OK;
+}
+
+static occ_status make_device_of(int32_t E, int32_t D, const int32_t *slot_expert_host,
+                                 occ::DeviceOf &dv) {
+  if (D < 1 || E % D != 0) return fail(OCC_EINVAL, "bad E=%d D=%d", E, D);
+  if (D > OCC_MAX_D) return fail(OCC_EUNSUP, "D=%d beyond %d", D, OCC_MAX_D);
+  if (slot_expert_host == nullptr) return fail(OCC_EINVAL, "slot_expert_host is NULL");
+  const int L = E / D;
+  for (int i = 0; i < OCC_MAX_E; ++i) dv.dev[i] = -1;
+  for (int g = 0; g < E; ++g) {
+    const int e = slot_expert_host[g];
+    if (e < 0 || e >= E || dv.dev[e] != -1)
+      return fail(OCC_EINVAL, "slot_expert is not a permutation of 0..%d (slot %d -> %d)",
+                  E - 1, g, e);
+    dv.dev[e] = (int8_t)(g / L);
+  }
+  return OCC_OK;
+}
+
+occ_status occ_cross_coactivation(int32_t T, int32_t k1, int32_t E1, const int32_t *idx1,
+                                  int32_t k2, int32_t E2, const int32_t *idx2, int32_t *counts,
+                                  int32_t accumulate, hipStream_t stream) {
+  OCC_TRY(check_routing("first layer", T, k1, E1, idx1));
+  OCC_TRY(check_routing("second layer", T, k2, E2, idx2));
+  if (counts == nullptr) return fail(OCC_EINVAL, "counts is NULL");
+  if (accumulate != 0 && accumulate != 1) return fail(OCC_EINVAL, "accumulate must be 0 or 1");
+  return hip_status(occ::launch_cross_coactivation(T, k1, E1, idx1, k2, E2, idx2, counts,
+                                                   accumulate, stream),
+                    "occ_cross_coactivation");
+}
+
+occ_status occ_home_device(int32_t T, int32_t k1, int32_t E1, const int32_t *idx1, int32_t E2,
+                           int32_t D, const int32_t *slot_expert2_host, const int32_t *affinity,
+                           int32_t *home, hipStream_t stream) {
+  OCC_TRY(check_routing("first layer", T, k1, E1, idx1));
+  if (E2 < 1 || E2 > OCC_MAX_E) return fail(E2 < 1 ? OCC_EINVAL : OCC_EUNSUP, "bad E2=%d", E2);
+  occ::DeviceOf dv;
+  OCC_TRY(make_device_of(E2, D, slot_expert2_host, dv));
+  if (affinity == nullptr || (T > 0 && home == nullptr))
+    return fail(OCC_EINVAL, "affinity and home must be set");
+  return hip_status(occ::launch_home_device(T, k1, E1, idx1, E2, D, dv, affinity, home, stream),
+                    "occ_home_device");
+}
+
+occ_status occ_local_hits(int32_t T, int32_t k2, int32_t E2, const int32_t *idx2, int32_t D,
+                          const int32_t *slot_expert2_host, const int32_t *home, int32_t *hits,
+                          int32_t accumulate, hipStream_t stream) {
+  OCC_TRY(check_routing("second layer", T, k2, E2, idx2));
+  occ::DeviceOf dv;
+  OCC_TRY(make_device_of(E2, D, slot_expert2_host, dv));
+  if (hits == nullptr || (T > 0 && home == nullptr))
+    return fail(OCC_EINVAL, "home and hits must be set");
+  if (accumulate != 0 && accumulate != 1) return fail(OCC_EINVAL, "accumulate must be 0 or 1");
+  return hip_status(occ::launch_local_hits(T, k2, E2, idx2, dv, home, hits, accumulate, stream),
+                    "occ_local_hits");
+}
+
 occ_status occ_place_greedy(int32_t E, int32_t D, const int32_t *counts_host,
                             int32_t *slot_expert_host) {
   if (E <= 0 || D <= 0 || E % D != 0) return fail(OCC_EINVAL, "bad E=%d D=%d", E, D);

@@ -89,6 +89,20 @@ hipError_t launch_combine(const occ_layer_desc &L, const void *out_epd, const oc
 
 hipError_t launch_coactivation(const occ_layer_desc &L, const int32_t *idx, int32_t *counts,
                                int accumulate, hipStream_t st);
+hipError_t launch_cross_coactivation(int T, int k1, int E1, const int32_t *idx1, int k2, int E2,
+                                     const int32_t *idx2, int32_t *counts, int accumulate,
+                                     hipStream_t st);
+
+// Token shuffling toward the next layer's experts.  dev_of: device of each
+// next-layer expert id (E2 entries, placement validated on the host).
+struct DeviceOf {
+  int8_t dev[OCC_MAX_E];
+};
+hipError_t launch_home_device(int T, int k1, int E1, const int32_t *idx1, int E2, int D,
+                              const DeviceOf &dv, const int32_t *affinity, int32_t *home,
+                              hipStream_t st);
+hipError_t launch_local_hits(int T, int k2, int E2, const int32_t *idx2, const DeviceOf &dv,
+                             const int32_t *home, int32_t *hits, int accumulate, hipStream_t st);
 
 // Expert GEMMs.  up: h = swiglu(A W_gu^T); down: out = h W_dn^T.
 hipError_t launch_expert_up(const occ_layer_desc &L, const void *epd, const int32_t *slot_offset,

@@ -220,6 +220,39 @@ occ_status occ_combine_direct(const occ_layer_desc *desc, const void *out_epd, c
 occ_status occ_coactivation(const occ_layer_desc *desc, const int32_t *topk_idx,
                             int32_t *counts, int32_t accumulate, hipStream_t stream);
 
+/* Cross-layer co-activation (Expert Coupling in MoE Pretraining, Abstract:
+ * the experts a token selects at one layer predict those it selects at the
+ * next; ExFlow, Abstract: inter-layer expert affinity):
+ *   counts int32 [E1][E2]: counts[i][j] += #tokens t with i among
+ *   idx1[t][0..k1) and j among idx2[t][0..k2).  accumulate = 0 zeroes first.
+ *   idx1 int32 [T][k1], idx2 int32 [T][k2] (device), ids outside 0..E-1
+ *   skipped.  Integer atomics only (order-free). */
+occ_status occ_cross_coactivation(int32_t T, int32_t k1, int32_t E1, const int32_t *idx1,
+                                  int32_t k2, int32_t E2, const int32_t *idx2, int32_t *counts,
+                                  int32_t accumulate, hipStream_t stream);
+
+/* Home device of each token for the next layer (token shuffling, Expert
+ * Coupling, Abstract: move each token to the GPU predicted to hold its
+ * next-layer experts).  With affinity int32 [E1][E2] (occ_cross_coactivation
+ * of a calibration batch) and the next layer's placement (slot_expert2_host,
+ * int32 [E2] host, a permutation; D devices of E2/D experts):
+ *   home[t] = argmax over d of sum over i in idx1[t] of sum over the experts
+ *             j on device d of affinity[i][j]   (int64, lower d on ties)
+ *   home int32 [T] (device). */
+occ_status occ_home_device(int32_t T, int32_t k1, int32_t E1, const int32_t *idx1, int32_t E2,
+                           int32_t D, const int32_t *slot_expert2_host, const int32_t *affinity,
+                           int32_t *home, hipStream_t stream);
+
+/* Assignments served on the token's own device (Expert Coupling, Abstract:
+ * the share of token-expert assignments served on the token's GPU):
+ *   hits[0] += #(t, q) with device(idx2[t][q]) == home[t]
+ * for any home assignment home int32 [T] (device): the predicted one of
+ * occ_home_device, or a plain sharding such as t * D / T.  hits is a device
+ * int32 scalar; accumulate = 0 zeroes it first. */
+occ_status occ_local_hits(int32_t T, int32_t k2, int32_t E2, const int32_t *idx2, int32_t D,
+                          const int32_t *slot_expert2_host, const int32_t *home, int32_t *hits,
+                          int32_t accumulate, hipStream_t stream);
+
 /* Greedy correlated placement on the host (Expert Coupling, Abstract:
  * experts often selected together go on one GPU; Occult, TL;DR: placement
  * rescheduling).  For each device in turn: take the unplaced expert with the

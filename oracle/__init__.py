@@ -243,6 +243,38 @@ def coactivation(idx, E, base=None):
     return Cm
 
 
+def cross_coactivation(idx1, E1, idx2, E2):
+    """O12': E1 x E2 counts of tokens choosing i at one layer and j at the next."""
+    idx1, idx2 = _i32(idx1), _i32(idx2)
+    T, k1 = idx1.shape
+    k2 = idx2.shape[1]
+    A = np.empty((E1, E2), np.int32)
+    _check(lib().orc_cross_coactivation(T, k1, E1, _p(idx1), k2, E2, _p(idx2), _p(A)),
+           "cross_coactivation")
+    return A
+
+
+def home_device(idx1, E1, A, slot_expert2, D):
+    """O12': predicted next-layer home device of every token."""
+    idx1 = _i32(idx1)
+    T, k1 = idx1.shape
+    E2 = A.shape[1]
+    home = np.empty(T, np.int32)
+    _check(lib().orc_home_device(T, k1, E1, _p(idx1), E2, D, _p(_i32(slot_expert2)), _p(_i32(A)),
+                                 _p(home)), "home_device")
+    return home
+
+
+def local_hits(idx2, E2, slot_expert2, D, home):
+    """O12': number of next-layer assignments served on the token's home device."""
+    idx2 = _i32(idx2)
+    T, k2 = idx2.shape
+    h = np.zeros(1, np.int64)
+    _check(lib().orc_local_hits(T, k2, E2, _p(idx2), D, _p(_i32(slot_expert2)), _p(_i32(home)),
+                                _p(h)), "local_hits")
+    return int(h[0])
+
+
 def greedy_placement(Cm, D):
     """O-P: slot_expert [E] from co-activation counts."""
     Cm = _i32(Cm)

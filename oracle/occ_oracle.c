@@ -22,6 +22,9 @@
  *  [OCC-FIG2]   same page, Figure 2 caption: MoE workflows under three
  *               all-to-all strategies across expert-parallel devices (the
  *               plain one sends one row per (token, expert) pair).
+ *  [EXF-ABS]    ExFlow (arXiv 2210.17223, bohrium.dp.tech page), Abstract:
+ *               inter-layer expert affinity from the conditional statistics
+ *               of a token's routing across layers.
  *  [CPL-ABS]    "Expert Coupling in MoE Pretraining" (readsearch.ai page),
  *               Abstract: each token is routed to k of E experts; a
  *               dispatcher that sends each token to each GPU once;
@@ -461,6 +464,62 @@ int orc_coactivation(int T, int k, int E, const int32_t *idx, int32_t *C, int ac
     for (int a = 0; a < k; ++a)
       for (int b = 0; b < k; ++b)
         C[(size_t)idx[(size_t)t * k + a] * E + idx[(size_t)t * k + b]] += 1;
+  return ORC_OK;
+}
+
+/* ---- O12': cross-layer co-activation, home devices, local hits ------------
+ * [CPL-ABS]: the experts a token selects at one layer predict those at the
+ * next; token shuffling moves each token to the GPU predicted to hold its
+ * next-layer experts and raises the share of assignments served on the
+ * token's GPU.  [EXF-ABS]: inter-layer expert affinity.
+ *   A[i][j]  = #tokens choosing i at the first layer and j at the second
+ *   home[t]  = argmax_d sum_{i in idx1[t]} sum_{j on device d} A[i][j]
+ *              (lower d on equal sums)
+ *   hits     = #(t, q) with device(idx2[t][q]) == home[t] */
+int orc_cross_coactivation(int T, int k1, int E1, const int32_t *idx1, int k2, int E2,
+                           const int32_t *idx2, int32_t *A) {
+  if (T < 0 || k1 <= 0 || k2 <= 0 || E1 <= 0 || E2 <= 0) return ORC_EINVAL;
+  memset(A, 0, sizeof(int32_t) * (size_t)E1 * E2);
+  for (int t = 0; t < T; ++t)
+    for (int a = 0; a < k1; ++a)
+      for (int b = 0; b < k2; ++b)
+        A[(size_t)idx1[(size_t)t * k1 + a] * E2 + idx2[(size_t)t * k2 + b]] += 1;
+  return ORC_OK;
+}
+
+int orc_home_device(int T, int k1, int E1, const int32_t *idx1, int E2, int D,
+                    const int32_t *slot_expert2, const int32_t *A, int32_t *home) {
+  if (T < 0 || k1 <= 0 || E1 <= 0 || E2 <= 0 || D <= 0 || E2 % D != 0) return ORC_EINVAL;
+  const int L = E2 / D;
+  for (int t = 0; t < T; ++t) {
+    int best = 0;
+    long long best_sum = -1;
+    for (int d = 0; d < D; ++d) {
+      long long sum = 0;
+      for (int l = 0; l < L; ++l) {
+        int j = slot_expert2[d * L + l];
+        for (int a = 0; a < k1; ++a) sum += A[(size_t)idx1[(size_t)t * k1 + a] * E2 + j];
+      }
+      if (sum > best_sum) { best_sum = sum; best = d; }
+    }
+    home[t] = best;
+  }
+  return ORC_OK;
+}
+
+int orc_local_hits(int T, int k2, int E2, const int32_t *idx2, int D, const int32_t *slot_expert2,
+                   const int32_t *home, int64_t *hits) {
+  if (T < 0 || k2 <= 0 || E2 <= 0 || D <= 0 || E2 % D != 0) return ORC_EINVAL;
+  const int L = E2 / D;
+  int64_t h = 0;
+  for (int t = 0; t < T; ++t)
+    for (int q = 0; q < k2; ++q) {
+      int j = idx2[(size_t)t * k2 + q];
+      int g = 0;
+      while (slot_expert2[g] != j) ++g;
+      if (g / L == home[t]) ++h;
+    }
+  *hits = h;
   return ORC_OK;
 }
 

@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(occ):
     names = declared_symbols()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     lib = C.CDLL(occ.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -103,6 +103,21 @@ def test_pruned_brim_arguments_are_checked(occ):
     rc = lib.occ_build_brim_pruned(C.byref(d), FAKE, FAKE, se.ctypes.data, 1, 1, C.byref(brim),
                                    FAKE, need - 1, None)
     assert rc == -3
+
+
+def test_affinity_arguments_are_checked(occ):
+    lib = occ.lib()
+    se = np.arange(8, dtype=np.int32)
+    bad = np.array([0, 1, 2, 3, 4, 5, 6, 6], np.int32)
+    assert lib.occ_cross_coactivation(10, 2, 8, FAKE, 9, 8, FAKE, FAKE, 0, None) == -1  # k > E
+    assert lib.occ_cross_coactivation(10, 2, 8, None, 2, 8, FAKE, FAKE, 0, None) == -1
+    assert lib.occ_cross_coactivation(10, 2, 256, FAKE, 2, 8, FAKE, FAKE, 0, None) == -2
+    assert lib.occ_cross_coactivation(10, 2, 8, FAKE, 2, 8, FAKE, FAKE, 3, None) == -1
+    assert lib.occ_home_device(10, 2, 8, FAKE, 8, 3, se.ctypes.data, FAKE, FAKE, None) == -1
+    assert lib.occ_home_device(10, 2, 8, FAKE, 8, 2, bad.ctypes.data, FAKE, FAKE, None) == -1
+    assert lib.occ_home_device(10, 2, 8, FAKE, 8, 2, se.ctypes.data, None, FAKE, None) == -1
+    assert lib.occ_local_hits(10, 2, 8, FAKE, 2, se.ctypes.data, FAKE, None, 0, None) == -1
+    assert lib.occ_local_hits(10, 2, 8, FAKE, 2, None, FAKE, FAKE, 0, None) == -1
 
 
 def test_direct_mode_arguments_are_checked(occ):

@@ -106,6 +106,54 @@ def test_pruned_layer_parity(orc, name, budget, rescale):
     compare(g, o, inp)
 
 
+def _two_layer_routing(orc, cfg, token_seed=None):
+    """Oracle routing of a synthetic two-layer stack: the same clustered
+    tokens through two independently drawn routers."""
+    from tests.gpu_common import oracle_logits_parallel
+    x = W.make_tokens(cfg, seed=0, token_seed=token_seed)
+    out = []
+    for layer in (0, 1):
+        wr = W.make_router(cfg, seed=0, layer=layer)
+        lg = oracle_logits_parallel(orc, x, wr, cfg.dtype)
+        out.append(orc.topk(lg, cfg.k, cfg.renorm)[0])
+    return out
+
+
+@pytest.mark.parametrize("name", ["bf16_ragged", "bf16_e128_pairs", "olmoe_bf16"])
+def test_cross_layer_affinity_parity(orc, name):
+    """Cross-layer counts (calibration batch), predicted home devices and
+    local hits (test batch), bit for bit against the oracle."""
+    import torch
+    import expert_top_router_amd as occ
+    cfg = SMALL[name] if name in SMALL else W.CONFIGS[name]
+    say(f"case affinity {name}")
+    c1, c2 = _two_layer_routing(orc, cfg, token_seed=1)
+    i1, i2 = _two_layer_routing(orc, cfg)
+    T, E, k, D = cfg.T, cfg.E, cfg.k, cfg.D
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    A = torch.empty((E, E), dtype=torch.int32, device="cuda")
+    occ.occ_cross_coactivation(T, k, E, dev(c1), k, E, dev(c2), A, accumulate=0)
+    occ.occ_cross_coactivation(T, k, E, dev(c1), k, E, dev(c2), A, accumulate=1)
+    torch.cuda.synchronize()
+    A_o = orc.cross_coactivation(c1, E, c2, E)
+    assert np.array_equal(A.cpu().numpy(), 2 * A_o), "cross-layer counts (accumulated twice)"
+    occ.occ_cross_coactivation(T, k, E, dev(c1), k, E, dev(c2), A, accumulate=0)
+    se2 = np.random.default_rng(12).permutation(E).astype(np.int32)
+    home = torch.empty(T, dtype=torch.int32, device="cuda")
+    occ.occ_home_device(T, k, E, dev(i1), E, D, se2, A, home)
+    torch.cuda.synchronize()
+    home_o = orc.home_device(i1, E, A_o, se2, D)
+    assert np.array_equal(home.cpu().numpy(), home_o), "home devices"
+    hits = torch.empty(1, dtype=torch.int32, device="cuda")
+    shard = dev((np.arange(T) * D // T).astype(np.int32))
+    for h_dev, h_host in [(home, home_o), (shard, shard.cpu().numpy())]:
+        occ.occ_local_hits(T, k, E, dev(i2), D, se2, h_dev, hits)
+        torch.cuda.synchronize()
+        assert int(hits.cpu()[0]) == orc.local_hits(i2, E, se2, D, h_host), "local hits"
+    say(f"  local share: predicted {orc.local_hits(i2, E, se2, D, home_o) / (T * k):.3f}, "
+        f"sharded {orc.local_hits(i2, E, se2, D, shard.cpu().numpy()) / (T * k):.3f}")
+
+
 FULL = ["tiny_fp32", "olmoe_bf16", "mixtral_bf16", "dsv2lite_bf16", "stress_bf16"]
 
 

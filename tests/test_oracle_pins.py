@@ -491,6 +491,63 @@ def test_k2_closed_form_for_sfd_rows(orc):
     assert b["S"] == 2 * T - intra
 
 
+def _onehot(idx, E):
+    oh = np.zeros((idx.shape[0], E), np.int64)
+    for q in range(idx.shape[1]):
+        oh[np.arange(idx.shape[0]), idx[:, q]] += 1
+    return oh
+
+
+def test_cross_layer_counts_are_a_one_hot_product(orc):
+    rng = np.random.default_rng(40)
+    for T, E1, k1, E2, k2 in [(50, 8, 2, 8, 2), (120, 16, 4, 12, 3), (64, 64, 8, 32, 6)]:
+        idx1 = np.stack([rng.permutation(E1)[:k1] for _ in range(T)]).astype(np.int32)
+        idx2 = np.stack([rng.permutation(E2)[:k2] for _ in range(T)]).astype(np.int32)
+        A = orc.cross_coactivation(idx1, E1, idx2, E2)
+        assert np.array_equal(A, _onehot(idx1, E1).T @ _onehot(idx2, E2))
+        assert A.sum() == T * k1 * k2
+    # one layer against itself is the plain co-activation
+    assert np.array_equal(orc.cross_coactivation(idx1, E1, idx1, E1), orc.coactivation(idx1, E1))
+
+
+def test_home_device_and_local_hits(orc):
+    rng = np.random.default_rng(41)
+    T, E1, k1, E2, k2, D = 200, 16, 4, 16, 3, 4
+    L = E2 // D
+    idx1 = np.stack([rng.permutation(E1)[:k1] for _ in range(T)]).astype(np.int32)
+    idx2 = np.stack([rng.permutation(E2)[:k2] for _ in range(T)]).astype(np.int32)
+    A = rng.integers(0, 50, size=(E1, E2)).astype(np.int32)
+    A[3, :] = 7  # equal sums on every device for tokens that only see expert 3's row
+    se2 = rng.permutation(E2).astype(np.int32)
+    member = np.zeros((E2, D), np.int64)
+    member[se2, np.arange(E2) // L] = 1
+    scores = _onehot(idx1, E1) @ A.astype(np.int64) @ member
+    home = orc.home_device(idx1, E1, A, se2, D)
+    assert np.array_equal(home, np.argmax(scores, axis=1))  # argmax: first (lowest) on ties
+    dev2 = np.empty(E2, np.int64)
+    dev2[se2] = np.arange(E2) // L
+    assert orc.local_hits(idx2, E2, se2, D, home) == int((dev2[idx2] == home[:, None]).sum())
+    # the best possible home (knowing the next layer) serves at least as many
+    best = np.argmax(_onehot(dev2[idx2], D), axis=1)
+    assert orc.local_hits(idx2, E2, se2, D, best) >= orc.local_hits(idx2, E2, se2, D, home)
+
+
+def test_planted_affinity_is_served_locally(orc):
+    """Next-layer choice = a fixed permutation of this layer's (k = 1): the
+    affinity is that permutation and every assignment lands on its home."""
+    rng = np.random.default_rng(42)
+    T, E, D = 300, 16, 4
+    perm = rng.permutation(E).astype(np.int32)
+    idx1 = rng.integers(0, E, size=(T, 1)).astype(np.int32)
+    idx2 = perm[idx1]
+    A = orc.cross_coactivation(idx1, E, idx2, E)
+    se2 = rng.permutation(E).astype(np.int32)
+    home = orc.home_device(idx1, E, A, se2, D)
+    assert orc.local_hits(idx2, E, se2, D, home) == T
+    shard = (np.arange(T) * D // T).astype(np.int32)
+    assert orc.local_hits(idx2, E, se2, D, shard) < T
+
+
 def test_greedy_recovers_planted_blocks(orc):
     rng = np.random.default_rng(13)
     E, D = 32, 8

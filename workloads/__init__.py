@@ -250,11 +250,15 @@ def make_tokens(cfg: LayerConfig, seed: int = 0, token_seed: Optional[int] = Non
     return out
 
 
-def make_router(cfg: LayerConfig, seed: int = 0, alpha: Optional[float] = None) -> np.ndarray:
+def make_router(cfg: LayerConfig, seed: int = 0, alpha: Optional[float] = None,
+                layer: int = 0) -> np.ndarray:
     """Router W_r [E, d]: N(0, 1/d), plus for the skewed workload
-    alpha * sum over the clusters c mapped to e's hot group of c_c/|c_c|^2."""
+    alpha * sum over the clusters c mapped to e's hot group of c_c/|c_c|^2.
+    `layer` > 0 draws the router of a further layer of a stack (its own
+    stream; the same tokens feed every layer of a synthetic stack)."""
     a = cfg.alpha if alpha is None else alpha
-    w = normal(seed, "router", (cfg.E, cfg.d), 1.0 / math.sqrt(cfg.d))
+    name = "router" if layer == 0 else f"router{layer}"
+    w = normal(seed, name, (cfg.E, cfg.d), 1.0 / math.sqrt(cfg.d))
     if cfg.skew_groups > 0 and a != 0.0:
         centres = cluster_centres(cfg, seed)
         groups = skew_groups(cfg, seed)
