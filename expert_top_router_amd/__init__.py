@@ -60,6 +60,11 @@ def _load(path: str = LIB_PATH):
         "occ_dispatch_direct": (I32, [DP, P, BP, P, P]),
         "occ_combine_direct": (I32, [DP, P, BP, P, P, P]),
         "occ_coactivation": (I32, [DP, P, P, I32, P]),
+        "occ_backward_workspace_bytes": (SZ, [DP]),
+        "occ_grad_combine": (I32, [DP, P, BP, P, P, P, P, P]),
+        "occ_expert_backward": (I32, [DP, P, BP, P, P, P, P, SZ, P, P, SZ, P, P, P, P]),
+        "occ_router_backward": (I32, [DP, P, P, P, P, P, P, BP, P, P, P, P, P]),
+        "occ_grad_dispatch": (I32, [DP, P, BP, P, P, P, P]),
         "occ_cross_coactivation": (I32, [I32, I32, I32, P, I32, I32, P, P, I32, P]),
         "occ_home_device": (I32, [I32, I32, I32, P, I32, I32, P, P, P, P]),
         "occ_local_hits": (I32, [I32, I32, I32, P, I32, P, P, P, I32, P]),
@@ -79,7 +84,9 @@ _lib = _load()
 EXPORTED = ("occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk", "occ_build_brim",
             "occ_build_brim_pruned",
             "occ_dispatch", "occ_expert_ffn", "occ_expert_up", "occ_expert_down", "occ_combine",
-            "occ_dispatch_direct", "occ_combine_direct", "occ_coactivation",
+            "occ_dispatch_direct", "occ_combine_direct", "occ_backward_workspace_bytes",
+            "occ_grad_combine", "occ_expert_backward", "occ_router_backward",
+            "occ_grad_dispatch", "occ_coactivation",
             "occ_cross_coactivation", "occ_home_device", "occ_local_hits", "occ_place_greedy",
             "occ_last_error")
 
@@ -221,6 +228,44 @@ def occ_coactivation(desc, topk_idx, counts, accumulate=0, stream=None):
                                  _stream(stream)), "occ_coactivation")
 
 
+def occ_backward_workspace_bytes(desc: occ_layer_desc) -> int:
+    return _lib.occ_backward_workspace_bytes(C.byref(desc))
+
+
+def occ_grad_combine(desc, dy, brim: occ_brim, out_epd, d_out_sfd, d_out_epd, dw_epd,
+                     stream=None):
+    _check(_lib.occ_grad_combine(C.byref(desc), _ptr(dy), C.byref(brim), _ptr(out_epd),
+                                 _ptr(d_out_sfd), _ptr(d_out_epd), _ptr(dw_epd), _stream(stream)),
+           "occ_grad_combine")
+
+
+def occ_expert_backward(desc, epd, brim: occ_brim, slot_expert_host, w_gate_up, w_down, h_ws,
+                        h_ws_bytes, d_out_epd, bwd_ws, bwd_ws_bytes, d_epd, dw_gate_up, dw_down,
+                        stream=None):
+    import numpy as np
+    se = np.ascontiguousarray(slot_expert_host, dtype=np.int32)
+    _check(_lib.occ_expert_backward(C.byref(desc), _ptr(epd), C.byref(brim), se.ctypes.data,
+                                    _ptr(w_gate_up), _ptr(w_down), _ptr(h_ws), h_ws_bytes,
+                                    _ptr(d_out_epd), _ptr(bwd_ws), bwd_ws_bytes, _ptr(d_epd),
+                                    _ptr(dw_gate_up), _ptr(dw_down), _stream(stream)),
+           "occ_expert_backward")
+
+
+def occ_router_backward(desc, x, w_router, logits, topk_idx, topk_w, slot_expert_host,
+                        brim: occ_brim, dw_epd, dlogits, dx_router, dw_router, stream=None):
+    import numpy as np
+    se = np.ascontiguousarray(slot_expert_host, dtype=np.int32)
+    _check(_lib.occ_router_backward(C.byref(desc), _ptr(x), _ptr(w_router), _ptr(logits),
+                                    _ptr(topk_idx), _ptr(topk_w), se.ctypes.data, C.byref(brim),
+                                    _ptr(dw_epd), _ptr(dlogits), _ptr(dx_router),
+                                    _ptr(dw_router), _stream(stream)), "occ_router_backward")
+
+
+def occ_grad_dispatch(desc, d_epd, brim: occ_brim, dx_router, d_sfd, dx, stream=None):
+    _check(_lib.occ_grad_dispatch(C.byref(desc), _ptr(d_epd), C.byref(brim), _ptr(dx_router),
+                                  _ptr(d_sfd), _ptr(dx), _stream(stream)), "occ_grad_dispatch")
+
+
 def occ_cross_coactivation(T, k1, E1, idx1, k2, E2, idx2, counts, accumulate=0, stream=None):
     _check(_lib.occ_cross_coactivation(T, k1, E1, _ptr(idx1), k2, E2, _ptr(idx2), _ptr(counts),
                                        int(accumulate), _stream(stream)),
@@ -257,5 +302,7 @@ __all__ = ["MoELayer", "OccError", "occ_layer_desc", "occ_brim", "make_desc", "d
            "make_brim", "occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk",
            "occ_build_brim", "occ_build_brim_pruned", "occ_dispatch", "occ_expert_ffn", "occ_expert_up",
            "occ_expert_down", "occ_combine", "occ_dispatch_direct", "occ_combine_direct",
+           "occ_backward_workspace_bytes", "occ_grad_combine", "occ_expert_backward",
+           "occ_router_backward", "occ_grad_dispatch",
            "occ_coactivation", "occ_cross_coactivation", "occ_home_device", "occ_local_hits",
            "occ_place_greedy", "last_error"]

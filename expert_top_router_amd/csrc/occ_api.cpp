@@ -327,6 +327,97 @@ occ_status occ_coactivation(const occ_layer_desc *desc, const int32_t *topk_idx,
                     "occ_coactivation");
 }
 
+// ---- backward -------------------------------------------------------------
+static occ_status check_backward(const occ_layer_desc *desc) {
+  OCC_TRY(check_desc(desc));
+  if (desc->dtype != OCC_BF16) return fail(OCC_EUNSUP, "the backward pass is for bf16 layers");
+  if (desc->n_shared != 0) return fail(OCC_EUNSUP, "the backward pass has no shared experts");
+  return OCC_OK;
+}
+
+static size_t gu_bytes(const occ_layer_desc &L) {
+  return align256((size_t)L.T * L.k * 2 * L.I * 2);
+}
+
+size_t occ_backward_workspace_bytes(const occ_layer_desc *desc) {
+  if (check_backward(desc) != OCC_OK) return 0;
+  return 2 * gu_bytes(*desc);
+}
+
+occ_status occ_grad_combine(const occ_layer_desc *desc, const void *dy, const occ_brim *brim,
+                            const void *out_epd, void *d_out_sfd, void *d_out_epd, float *dw_epd,
+                            hipStream_t stream) {
+  OCC_TRY(check_backward(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const int64_t Td = (int64_t)desc->T * desc->d, Rk = (int64_t)desc->T * desc->k;
+  if (missing(brim->epd_w, Rk)) return fail(OCC_EINVAL, "brim->epd_w must be set");
+  if (missing(dy, Td) || missing(out_epd, Td * desc->k) || missing(d_out_epd, Td * desc->k) ||
+      missing(dw_epd, Rk))
+    return fail(OCC_EINVAL, "dy, out_epd, d_out_epd and dw_epd must be set");
+  return hip_status(occ::launch_grad_combine(*desc, dy, *brim, out_epd, d_out_sfd, d_out_epd,
+                                             dw_epd, stream),
+                    "occ_grad_combine");
+}
+
+occ_status occ_expert_backward(const occ_layer_desc *desc, const void *epd, const occ_brim *brim,
+                               const int32_t *slot_expert_host, const void *w_gate_up,
+                               const void *w_down, const void *h_ws, size_t h_ws_bytes,
+                               const void *d_out_epd, void *bwd_ws, size_t bwd_ws_bytes,
+                               void *d_epd, float *dw_gate_up, float *dw_down,
+                               hipStream_t stream) {
+  OCC_TRY(check_backward(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const occ_layer_desc &L = *desc;
+  const int64_t Rd = (int64_t)L.T * L.k * L.d;
+  if (missing(epd, Rd) || !w_gate_up || !w_down || missing(d_out_epd, Rd) || missing(d_epd, Rd) ||
+      !dw_gate_up || !dw_down || missing(h_ws, (int64_t)h_bytes(L)) ||
+      missing(bwd_ws, (int64_t)(2 * gu_bytes(L))))
+    return fail(OCC_EINVAL, "expert backward: an operand is NULL");
+  if (h_ws_bytes < h_bytes(L))
+    return fail(OCC_ENOSPC, "h workspace of %zu bytes < %zu", h_ws_bytes, h_bytes(L));
+  if (bwd_ws_bytes < 2 * gu_bytes(L))
+    return fail(OCC_ENOSPC, "backward workspace of %zu bytes < %zu", bwd_ws_bytes,
+                2 * gu_bytes(L));
+  occ::Placement pl;
+  OCC_TRY(make_placement(L, slot_expert_host, pl));
+  char *ws = static_cast<char *>(bwd_ws);
+  return hip_status(occ::launch_expert_backward(L, brim->slot_offset, pl, epd, w_gate_up, w_down,
+                                                h_ws, d_out_epd, ws, ws + gu_bytes(L), d_epd,
+                                                dw_gate_up, dw_down, stream),
+                    "occ_expert_backward");
+}
+
+occ_status occ_router_backward(const occ_layer_desc *desc, const void *x, const float *w_router,
+                               const float *logits, const int32_t *topk_idx,
+                               const float *topk_w, const int32_t *slot_expert_host,
+                               const occ_brim *brim, const float *dw_epd, float *dlogits,
+                               float *dx_router, float *dw_router, hipStream_t stream) {
+  OCC_TRY(check_backward(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const occ_layer_desc &L = *desc;
+  const int64_t T = L.T, Tk = T * L.k;
+  if (missing(x, T * L.d) || !w_router || missing(logits, T * L.E) || missing(topk_idx, Tk) ||
+      missing(topk_w, Tk) || missing(dw_epd, Tk) || missing(dlogits, T * L.E) ||
+      missing(dx_router, T * L.d) || !dw_router)
+    return fail(OCC_EINVAL, "router backward: an operand is NULL");
+  occ::Placement pl;
+  OCC_TRY(make_placement(L, slot_expert_host, pl));
+  return hip_status(occ::launch_router_backward(L, pl, x, w_router, logits, topk_idx, topk_w, *brim,
+                                                dw_epd, dlogits, dx_router, dw_router, stream),
+                    "occ_router_backward");
+}
+
+occ_status occ_grad_dispatch(const occ_layer_desc *desc, const void *d_epd, const occ_brim *brim,
+                             const float *dx_router, void *d_sfd, void *dx, hipStream_t stream) {
+  OCC_TRY(check_backward(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const int64_t Td = (int64_t)desc->T * desc->d;
+  if (missing(d_epd, Td * desc->k) || missing(d_sfd, s_max(*desc)) || missing(dx, Td))
+    return fail(OCC_EINVAL, "d_epd, d_sfd and dx must be set");
+  return hip_status(occ::launch_grad_dispatch(*desc, d_epd, *brim, dx_router, d_sfd, dx, stream),
+                    "occ_grad_dispatch");
+}
+
 // ---- cross-layer affinity -------------------------------------------------
 static occ_status check_routing(const char *what, int32_t T, int32_t k, int32_t E,
                                 const int32_t *idx) {

@@ -87,6 +87,18 @@ hipError_t launch_dispatch(const occ_layer_desc &L, const void *x, const occ_bri
 hipError_t launch_combine(const occ_layer_desc &L, const void *out_epd, const occ_brim &b,
                           const void *shared_out, void *out_sfd, void *y, hipStream_t st);
 
+// Backward (bf16): grad-combine, grad-dispatch and the router gradient.
+hipError_t launch_grad_combine(const occ_layer_desc &L, const void *dy, const occ_brim &b,
+                               const void *out_epd, void *d_out_sfd, void *d_out_epd, float *dw,
+                               hipStream_t st);
+hipError_t launch_grad_dispatch(const occ_layer_desc &L, const void *d_epd, const occ_brim &b,
+                                const float *add32, void *d_sfd, void *dx, hipStream_t st);
+hipError_t launch_router_backward(const occ_layer_desc &L, const Placement &pl, const void *x,
+                                  const float *w_router, const float *logits,
+                                  const int32_t *idx, const float *topk_w, const occ_brim &b,
+                                  const float *dw, float *dlogit, float *dx_router,
+                                  float *dw_router, hipStream_t st);
+
 hipError_t launch_coactivation(const occ_layer_desc &L, const int32_t *idx, int32_t *counts,
                                int accumulate, hipStream_t st);
 hipError_t launch_cross_coactivation(int T, int k1, int E1, const int32_t *idx1, int k2, int E2,
@@ -105,6 +117,14 @@ hipError_t launch_local_hits(int T, int k2, int E2, const int32_t *idx2, const D
                              const int32_t *home, int32_t *hits, int accumulate, hipStream_t st);
 
 // Expert GEMMs.  up: h = swiglu(A W_gu^T); down: out = h W_dn^T.
+// Expert backward (bf16): recomputes [G | U] into gu ([R][2I]), writes
+// [dG | dU] into dgu ([R][2I]) and dEPD ([R][d]), and the fp32 weight
+// gradients dW_gate_up [E][2I][d] and dW_down [E][d][I].
+hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_offset,
+                                  const Placement &pl, const void *epd, const void *w_gate_up,
+                                  const void *w_down, const void *h, const void *d_out_epd,
+                                  void *gu, void *dgu, void *d_epd, float *dw_gate_up,
+                                  float *dw_down, hipStream_t st);
 hipError_t launch_expert_up(const occ_layer_desc &L, const void *epd, const int32_t *slot_offset,
                             const Placement &pl, const void *w_gate_up, void *h,
                             const void *x, const void *w_gate_up_sh, void *h_sh,

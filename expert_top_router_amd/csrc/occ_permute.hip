@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     int T, int D, int L, int ld, int row16, const u32x4 *__restrict__ out_epd,
     const int32_t *__restrict__ brim0, const int32_t *__restrict__ brim1,
     const float *__restrict__ epd_w, const u32x4 *__restrict__ shared, u32x4 *__restrict__ out_sfd,
-    u32x4 *__restrict__ y) {
+    u32x4 *__restrict__ y, const float *__restrict__ add32) {
   using CK = Chunk<DT>;
   constexpr int VE = CK::N;
   const int lane = threadIdx.x & (kWave - 1);
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
       s = brim0[(size_t)dv * T + t];
       if (s >= 0) {
         r = brim1[(size_t)l * ld + s];
-        if (r >= 0) wr = epd_w[r];
+        if (r >= 0) wr = epd_w != nullptr ? epd_w[r] : 1.0f;
       }
     }
     uint64_t mr = __ballot(r >= 0);
@@ -206,6 +206,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int i = lane + kWave * c;
+    if (add32 != nullptr && i < row16) {  // an fp32 term added before the final rounding
+      const float *ap = add32 + ((size_t)t * row16 + i) * VE;
+#pragma unroll
+      for (int u = 0; u < VE; ++u) yacc[c][u] += ap[u];
+    }
     if (i < row16) y[(size_t)t * row16 + i] = CK::pack(yacc[c]);
   }
 }
@@ -247,7 +252,8 @@ hipError_t launch_dispatch(const occ_layer_desc &Ld, const void *x, const occ_br
 
 template <int DT>
 static hipError_t combine_dt(const occ_layer_desc &Ld, const void *out_epd, const occ_brim &b,
-                             const void *shared_out, void *out_sfd, void *y, hipStream_t st) {
+                             const void *shared_out, void *out_sfd, void *y, hipStream_t st,
+                             const float *ew, const float *add32) {
   const int es = DT == OCC_F32 ? 4 : 2;
   const int row16 = Ld.d * es / 16;
   const int L = Ld.E / Ld.D;
@@ -262,12 +268,12 @@ static hipError_t combine_dt(const occ_layer_desc &Ld, const void *out_epd, cons
   do {                                                                                    \
     if (os != nullptr)                                                                    \
       combine_kernel<DT, N, true><<<grid, kThreads, 0, st>>>(Ld.T, Ld.D, L, ld, row16, oe, \
-                                                             b.brim0, b.brim1, b.epd_w, sh, \
-                                                             os, yp);                       \
+                                                             b.brim0, b.brim1, ew, sh, os, \
+                                                             yp, add32);                   \
     else                                                                                  \
       combine_kernel<DT, N, false><<<grid, kThreads, 0, st>>>(Ld.T, Ld.D, L, ld, row16,    \
-                                                              oe, b.brim0, b.brim1,        \
-                                                              b.epd_w, sh, os, yp);        \
+                                                              oe, b.brim0, b.brim1, ew,    \
+                                                              sh, os, yp, add32);          \
   } while (0)
   if (nch <= 1) OCC_COMBINE(1);
   else if (nch <= 2) OCC_COMBINE(2);
@@ -282,8 +288,19 @@ static hipError_t combine_dt(const occ_layer_desc &Ld, const void *out_epd, cons
 hipError_t launch_combine(const occ_layer_desc &Ld, const void *out_epd, const occ_brim &b,
                           const void *shared_out, void *out_sfd, void *y, hipStream_t st) {
   if (Ld.T == 0) return hipSuccess;
-  return Ld.dtype == OCC_F32 ? combine_dt<OCC_F32>(Ld, out_epd, b, shared_out, out_sfd, y, st)
-                             : combine_dt<OCC_BF16>(Ld, out_epd, b, shared_out, out_sfd, y, st);
+  return Ld.dtype == OCC_F32
+             ? combine_dt<OCC_F32>(Ld, out_epd, b, shared_out, out_sfd, y, st, b.epd_w, nullptr)
+             : combine_dt<OCC_BF16>(Ld, out_epd, b, shared_out, out_sfd, y, st, b.epd_w, nullptr);
+}
+
+// Gradient of the dispatch (the same walk, unit weights): d_sfd[s] = sum over
+// l of d_epd[r], dx[t] = sum over devices of d_sfd[s] + add32[t] (fp32).
+hipError_t launch_grad_dispatch(const occ_layer_desc &Ld, const void *d_epd, const occ_brim &b,
+                                const float *add32, void *d_sfd, void *dx, hipStream_t st) {
+  if (Ld.T == 0) return hipSuccess;
+  return Ld.dtype == OCC_F32
+             ? combine_dt<OCC_F32>(Ld, d_epd, b, nullptr, d_sfd, dx, st, nullptr, add32)
+             : combine_dt<OCC_BF16>(Ld, d_epd, b, nullptr, d_sfd, dx, st, nullptr, add32);
 }
 
 }  // namespace occ

@@ -12,8 +12,9 @@ from typing import Optional
 
 import numpy as np
 
-from . import (desc_of, make_brim, occ_build_brim, occ_build_brim_pruned, occ_coactivation,
-               occ_combine,
+from . import (desc_of, make_brim, occ_backward_workspace_bytes, occ_build_brim,
+               occ_build_brim_pruned, occ_coactivation, occ_combine, occ_expert_backward,
+               occ_grad_combine, occ_grad_dispatch, occ_router_backward,
                occ_combine_direct, occ_dispatch, occ_dispatch_direct, occ_expert_down,
                occ_expert_ffn, occ_expert_up, occ_ffn_workspace_bytes, occ_route_topk,
                occ_workspace_bytes)
@@ -61,6 +62,7 @@ class MoELayer:
         collaboration pruning (devices kept per token, occ_build_brim_pruned)."""
         torch = _torch()
         self.cfg = cfg
+        self.device = device
         self.budget = budget
         self.rescale = rescale
         self.desc = desc_of(cfg)
@@ -168,6 +170,72 @@ class MoELayer:
         self.dispatch_direct(stream)
         self.expert_ffn(stream)
         self.combine_direct(stream)
+
+    # ---- backward (bf16, no shared experts) -------------------------------
+    def _grad_buffers(self):
+        if getattr(self, "dy", None) is not None:
+            return
+        torch = _torch()
+        cfg = self.cfg
+        T, d, E, k, D = cfg.T, cfg.d, cfg.E, cfg.k, cfg.D
+        S_max, R = T * min(k, D), T * k
+        el = torch.bfloat16
+        f32 = torch.float32
+
+        def buf(shape, dt):
+            n = int(np.prod(shape))
+            return torch.empty(max(n, 1), dtype=dt, device=self.device)[:n].view(*shape)
+
+        if self.logits is None:
+            self.logits = buf((T, E), f32)
+        self.dy = buf((T, d), el)
+        self.d_out_sfd = buf((S_max, d), el)
+        self.d_out_epd = buf((R, d), el)
+        self.dw_epd = buf((R,), f32)
+        self.bwd_bytes = occ_backward_workspace_bytes(self.desc)
+        self.bwd_ws = buf((self.bwd_bytes,), torch.uint8)
+        self.d_epd = buf((R, d), el)
+        self.dw_gate_up = buf((E, 2 * cfg.I, d), f32)
+        self.dw_down = buf((E, d, cfg.I), f32)
+        self.dlogits = buf((T, E), f32)
+        self.dx_router = buf((T, d), f32)
+        self.dw_router = buf((E, d), f32)
+        self.d_sfd = buf((S_max, d), el)
+        self.dx = buf((T, d), el)
+
+    def grad_combine(self, stream=None):
+        occ_grad_combine(self.desc, self.dy, self.brim, self.out_epd, self.d_out_sfd,
+                         self.d_out_epd, self.dw_epd, stream)
+
+    def expert_backward(self, stream=None):
+        occ_expert_backward(self.desc, self.epd, self.brim, self.slot_expert, self.w.w_gate_up,
+                            self.w.w_down, self.h_ws, self.h_bytes, self.d_out_epd, self.bwd_ws,
+                            self.bwd_bytes, self.d_epd, self.dw_gate_up, self.dw_down, stream)
+
+    def router_backward(self, stream=None):
+        occ_router_backward(self.desc, self.w.x, self.w.w_router, self.logits, self.topk_idx,
+                            self.topk_w, self.slot_expert, self.brim, self.dw_epd, self.dlogits,
+                            self.dx_router, self.dw_router, stream)
+
+    def grad_dispatch(self, stream=None):
+        occ_grad_dispatch(self.desc, self.d_epd, self.brim, self.dx_router, self.d_sfd, self.dx,
+                          stream)
+
+    def backward(self, dy=None, stream=None):
+        """Gradients of the last forward (which must have kept its logits:
+        construct with with_logits=True, or call prepare_backward() first)
+        for the upstream gradient dy (bf16 [T, d]; self.dy when None)."""
+        self._grad_buffers()
+        if dy is not None:
+            self.dy.copy_(dy)
+        self.grad_combine(stream)
+        self.expert_backward(stream)
+        self.router_backward(stream)
+        self.grad_dispatch(stream)
+
+    def prepare_backward(self):
+        """Allocate the gradient buffers (and the logits the router gradient needs)."""
+        self._grad_buffers()
 
     def coactivation(self, accumulate=0, stream=None):
         occ_coactivation(self.desc, self.topk_idx, self.counts, accumulate, stream)

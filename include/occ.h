@@ -220,6 +220,68 @@ occ_status occ_combine_direct(const occ_layer_desc *desc, const void *out_epd, c
 occ_status occ_coactivation(const occ_layer_desc *desc, const int32_t *topk_idx,
                             int32_t *counts, int32_t accumulate, hipStream_t stream);
 
+/* ---- Backward pass through the BRIMs (bf16 layers without shared experts;
+ * EUNSUP otherwise).  Expert Coupling in MoE Pretraining, Abstract: every
+ * MoE layer runs its all-to-alls in the forward and the backward pass;
+ * Occult, Figure 4 caption: the moves between ORI, SFD and EPD are guided by
+ * the BRIMs, walked here in the opposite direction.  Call order after a
+ * forward (occ_route_topk with logits, occ_build_brim, occ_dispatch,
+ * occ_expert_ffn, occ_combine): occ_grad_combine, occ_expert_backward,
+ * occ_router_backward, occ_grad_dispatch.  Top-k selection is a constant. */
+
+/* Bytes of the workspace of occ_expert_backward (0 for an invalid or
+ * unsupported descriptor). */
+size_t occ_backward_workspace_bytes(const occ_layer_desc *desc);
+
+/* Gradient of the combine, given dy (bf16 [T][d]):
+ *   d_out_sfd[s] = dy[sfd_token[s]]          (bf16 [S_max][d], rows < S; the
+ *                                             backward send buffer; may be NULL)
+ *   d_out_epd[r] = epd_w[r] * dy[epd_token[r]]   (bf16 [R][d], rounded)
+ *   dw_epd[r]    = sum_c dy[t][c] out_epd[r][c]  (fp32 [R]: gradient of the
+ *                                             routing weight of row r) */
+occ_status occ_grad_combine(const occ_layer_desc *desc, const void *dy, const occ_brim *brim,
+                            const void *out_epd, void *d_out_sfd, void *d_out_epd, float *dw_epd,
+                            hipStream_t stream);
+
+/* Gradient of the SwiGLU experts on the EPD rows of each slot:
+ *   [G | U] = EPD W_gate_up[e]^T recomputed (bf16, in bwd_ws)
+ *   dh      = d_out_epd W_down[e];  dG = dh U silu'(G), dU = dh silu(G)
+ *             (bf16, in bwd_ws)
+ *   d_epd   = [dG | dU] W_gate_up[e]                      (bf16 [R][d])
+ *   dw_gate_up[e] = sum over the slot's rows of [dG | dU]^T EPD
+ *                                                  (fp32 [E][2I][d], written)
+ *   dw_down[e]    = sum over the slot's rows of d_out_epd^T h
+ *                                                  (fp32 [E][d][I], written)
+ * h_ws is the forward's workspace (h of every EPD row); bwd_ws holds
+ * occ_backward_workspace_bytes(desc) bytes. */
+occ_status occ_expert_backward(const occ_layer_desc *desc, const void *epd, const occ_brim *brim,
+                               const int32_t *slot_expert_host, const void *w_gate_up,
+                               const void *w_down, const void *h_ws, size_t h_ws_bytes,
+                               const void *d_out_epd, void *bwd_ws, size_t bwd_ws_bytes,
+                               void *d_epd, float *dw_gate_up, float *dw_down,
+                               hipStream_t stream);
+
+/* Gradient of the routing: for each token, dp of its picks from dw_epd
+ * (through the renormalisation when desc->renorm), then the softmax backward
+ * over all E experts, from the forward's fp32 logits:
+ *   dlogits[t][e] = p[e] (dp[e] - sum_e' p[e'] dp[e'])      (fp32 [T][E])
+ *   dx_router     = dlogits W_r                            (fp32 [T][d])
+ *   dw_router     = dlogits^T x                            (fp32 [E][d]) */
+occ_status occ_router_backward(const occ_layer_desc *desc, const void *x, const float *w_router,
+                               const float *logits, const int32_t *topk_idx,
+                               const float *topk_w, const int32_t *slot_expert_host,
+                               const occ_brim *brim, const float *dw_epd, float *dlogits,
+                               float *dx_router, float *dw_router, hipStream_t stream);
+
+/* Gradient of the dispatch (the combine's walk with unit weights):
+ *   d_sfd[s] = sum over l ascending with r = brim1[l][s] >= 0 of d_epd[r]
+ *              (bf16 [S_max][d], rows < S: the backward return payload)
+ *   dx[t]    = dx_router[t] + sum over devices of d_sfd[brim0[dv][t]]
+ *              (bf16 [T][d]; fp32 accumulation, one rounding; dx_router may
+ *              be NULL) */
+occ_status occ_grad_dispatch(const occ_layer_desc *desc, const void *d_epd, const occ_brim *brim,
+                             const float *dx_router, void *d_sfd, void *dx, hipStream_t stream);
+
 /* Cross-layer co-activation (Expert Coupling in MoE Pretraining, Abstract:
  * the experts a token selects at one layer predict those it selects at the
  * next; ExFlow, Abstract: inter-layer expert affinity):

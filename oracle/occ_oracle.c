@@ -78,6 +78,13 @@ static double round_dt(double v, int dt) {
   return nearbyint(v / q) * q;  /* default rounding mode: nearest, ties to even */
 }
 
+/* out[i] = round_dt(in[i]) for an array (dt = 0 fp32, 1 bf16, 2 none). */
+int orc_round_array(long n, int dt, const double *in, double *out) {
+  if (n < 0) return ORC_EINVAL;
+  for (long i = 0; i < n; ++i) out[i] = dt == 2 ? in[i] : round_dt(in[i], dt);
+  return ORC_OK;
+}
+
 /* ---- O1-O3: routing ------------------------------------------------------
  * [CPL-ABS]: each token is routed to k of the E experts.  Softmax gate over
  * all E experts; selection on the logits (softmax is monotone). */

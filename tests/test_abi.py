@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(occ):
     names = declared_symbols()
-    assert len(names) == 18, names
+    assert len(names) == 23, names
     lib = C.CDLL(occ.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -103,6 +103,34 @@ def test_pruned_brim_arguments_are_checked(occ):
     rc = lib.occ_build_brim_pruned(C.byref(d), FAKE, FAKE, se.ctypes.data, 1, 1, C.byref(brim),
                                    FAKE, need - 1, None)
     assert rc == -3
+
+
+def test_backward_arguments_are_checked(occ):
+    lib = occ.lib()
+    brim = occ.make_brim(brim0=FAKE, brim1=FAKE, sfd_offset=FAKE, slot_offset=FAKE,
+                         sfd_token=FAKE, epd_token=FAKE, epd_sfd=FAKE, epd_w=FAKE, S=FAKE)
+    se = np.arange(8, dtype=np.int32)
+    d = _desc(occ)
+    assert occ.occ_backward_workspace_bytes(d) == 2 * 64 * 2 * 2 * 128 * 2
+    f32 = _desc(occ, dtype="f32")
+    assert occ.occ_backward_workspace_bytes(f32) == 0
+    assert lib.occ_grad_combine(C.byref(f32), FAKE, C.byref(brim), FAKE, None, FAKE, FAKE,
+                                None) == -2
+    sh = _desc(occ, n_shared=1, I_shared=64)
+    assert lib.occ_grad_dispatch(C.byref(sh), FAKE, C.byref(brim), None, FAKE, FAKE, None) == -2
+    assert lib.occ_grad_combine(C.byref(d), None, C.byref(brim), FAKE, None, FAKE, FAKE,
+                                None) == -1
+    ws = occ.occ_backward_workspace_bytes(d)
+    hb = occ.occ_ffn_workspace_bytes(d)
+    rc = lib.occ_expert_backward(C.byref(d), FAKE, C.byref(brim), se.ctypes.data, FAKE, FAKE,
+                                 FAKE, hb, FAKE, FAKE, ws - 1, FAKE, FAKE, FAKE, None)
+    assert rc == -3
+    rc = lib.occ_expert_backward(C.byref(d), FAKE, C.byref(brim), se.ctypes.data, FAKE, FAKE,
+                                 FAKE, hb, FAKE, FAKE, ws, FAKE, None, FAKE, None)
+    assert rc == -1
+    rc = lib.occ_router_backward(C.byref(d), FAKE, FAKE, None, FAKE, FAKE, se.ctypes.data,
+                                 C.byref(brim), FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == -1
 
 
 def test_affinity_arguments_are_checked(occ):

@@ -1,0 +1,171 @@
+"""GPU parity of the backward pass through the BRIMs against the backward
+oracle (oracle/backward.py).  Small bf16 layers are compared in full (every
+EPD row, every expert's weight gradient, the router gradients); the
+OLMoE-shaped layer on sampled tokens (their EPD rows) and two slots' weight
+gradients.  Each stage is checked on the inputs the GPU stored for it (its
+routing weights, its out_EPD for dw, its dw for the router, its d_epd for
+the dispatch gradient): those inputs match the oracle's own only to the
+forward's bf16 tolerance, and a stage's own arithmetic is held to a tighter
+bound.  The expert backward itself (recomputed G and U, dG, dU, d_epd and
+the weight gradients) is compared with the oracle's chain end to end."""
+import numpy as np
+import pytest
+
+import workloads as W
+from tests.gpu_common import oracle_logits_parallel, say
+from tests.tolerance import assert_close
+from tests.tolerance import rel_err
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "bf16_ragged": W.LayerConfig("bf16_ragged", T=300, d=128, E=16, I=128, k=4, D=4,
+                                 dtype="bf16", clusters=4),
+    "bf16_renorm": W.LayerConfig("bf16_renorm", T=200, d=128, E=8, I=64, k=2, D=2,
+                                 dtype="bf16", renorm=1),
+    "bf16_e128_pairs": W.LayerConfig("bf16_e128_pairs", T=513, d=64, E=128, I=64, k=6, D=16,
+                                     dtype="bf16", clusters=8),
+    "bf16_one_expert_per_device": W.LayerConfig("bf16_one_expert_per_device", T=150, d=128,
+                                                E=8, I=64, k=2, D=8, dtype="bf16"),
+}
+
+
+def _run_gpu(cfg, inp, dy_bits):
+    import torch
+    from expert_top_router_amd.layer import MoELayer, to_device, upload_inputs
+    lay = MoELayer(cfg, upload_inputs(inp), inp.slot_expert, with_logits=True)
+    lay.prepare_backward()
+    say(f"  gpu forward+backward {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} D={cfg.D}")
+    lay.forward()
+    lay.backward(to_device(dy_bits))
+    torch.cuda.synchronize()
+    R, I = cfg.R, cfg.I
+    ws = lay.bwd_ws.view(torch.int16)
+    half = lay.bwd_bytes // 4  # int16 elements per half of the workspace
+    names = ["topk_idx", "topk_w", "logits", "brim0", "brim1", "slot_offset", "epd_token",
+             "epd_sfd", "epd_w", "S", "d_out_epd", "dw_epd", "d_epd", "dw_gate_up", "dw_down",
+             "dlogits", "dx_router", "dw_router", "d_sfd", "d_out_sfd", "dx", "out_epd"]
+    g = {n: lay.host(n) for n in names}
+    gu = ws[:R * 2 * I].cpu().numpy().view(np.uint16).reshape(R, 2 * I)
+    dgu = ws[half:half + R * 2 * I].cpu().numpy().view(np.uint16).reshape(R, 2 * I)
+    g["gu"], g["dgu"] = gu, dgu
+    del lay
+    torch.cuda.empty_cache()
+    return g
+
+
+def _bf(a):
+    return W.to_f32(a, "bf16").astype(np.float64)
+
+
+def _row_of(b, idx, slot_expert, cfg):
+    """EPD row of (token t, pick j), through BRIM_0 and BRIM_1."""
+    L = cfg.E // cfg.D
+    slot_of = np.empty(cfg.E, np.int64)
+    slot_of[np.asarray(slot_expert)] = np.arange(cfg.E)
+
+    def row_of(t, j):
+        gs = slot_of[idx[t, j]]
+        return int(b["brim1"][gs % L, b["brim0"][gs // L, t]])
+    return row_of
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layer_backward_parity(orc, name):
+    import oracle.backward as ob
+    cfg = SMALL[name]
+    say(f"case backward {name}")
+    inp = W.make_layer(cfg, seed=9)
+    dy = W.from_f64(np.random.default_rng(9).standard_normal((cfg.T, cfg.d)), "bf16")
+    g = _run_gpu(cfg, inp, dy)
+    lg = oracle_logits_parallel(orc, inp.x, inp.w_router, "bf16")
+    assert np.array_equal(g["logits"].view(np.uint32), lg.view(np.uint32))
+    idx = g["topk_idx"]
+    b = orc.brim(idx, g["topk_w"], inp.slot_expert, cfg.E, cfg.D)
+    assert np.array_equal(g["epd_token"], b["epd_token"])
+    o = ob.full(_bf(inp.x), _bf(inp.w_router), _bf(inp.w_gate_up), _bf(inp.w_down), lg, idx,
+                g["topk_w"], cfg.renorm, b, inp.slot_expert, _bf(dy), cfg.D, "bf16")
+    I = cfg.I
+    S = b["S"]
+    g_out_epd = g["out_epd"]
+    # the send buffer is a bit copy of dy
+    assert np.array_equal(g["d_out_sfd"][:S], dy[b["sfd_token"][:S]]), "d_out_sfd"
+    assert_close(_bf(g["d_out_epd"]), o["d_out_epd"], "bf16", "d_out_epd")
+    # dw = <dy, out_EPD> on the GPU's stored out_EPD
+    t_of = b["epd_token"]
+    dw_ref = np.sum(_bf(dy)[t_of] * _bf(g_out_epd), axis=1)
+    assert rel_err(g["dw_epd"], dw_ref) <= 1e-4, "dw_epd"
+    assert_close(g["dw_epd"], o["dw"], "bf16", "dw_epd (oracle chain)")
+    assert_close(_bf(g["gu"][:, :I]), o["G"], "bf16", "G (recomputed)")
+    assert_close(_bf(g["gu"][:, I:]), o["U"], "bf16", "U (recomputed)")
+    assert_close(_bf(g["dgu"][:, :I]), o["dG"], "bf16", "dG")
+    assert_close(_bf(g["dgu"][:, I:]), o["dU"], "bf16", "dU")
+    assert_close(_bf(g["d_epd"]), o["d_epd"], "bf16", "d_epd")
+    assert_close(g["dw_gate_up"], o["dW_gate_up"], "bf16", "dW_gate_up")
+    assert_close(g["dw_down"], o["dW_down"], "bf16", "dW_down")
+    # router gradient on the GPU's dw
+    row_of = _row_of(b, idx, inp.slot_expert, cfg)
+    dl = ob.router_grads(lg, idx, g["topk_w"], cfg.renorm,
+                         lambda t, j: float(g["dw_epd"][row_of(t, j)]), np.arange(cfg.T))
+    assert rel_err(g["dlogits"], dl) <= 1e-4, "dlogits"
+    assert rel_err(g["dx_router"], dl @ _bf(inp.w_router)) <= 1e-4, "dx_router"
+    assert rel_err(g["dw_router"], dl.T @ _bf(inp.x)) <= 1e-4, "dw_router"
+    assert_close(g["dlogits"], o["dlogits"], "bf16", "dlogits (oracle chain)")
+    # dispatch gradient on the GPU's d_epd and dx_router
+    dx, dsfd = ob.grad_dispatch(b, lambda r: _bf(g["d_epd"][r]), np.arange(cfg.T), cfg.T, cfg.D,
+                                cfg.E // cfg.D, cfg.d, "bf16", g["dx_router"])
+    srows = np.array(sorted(dsfd), dtype=np.int64)
+    assert_close(_bf(g["d_sfd"][srows]), np.stack([dsfd[s] for s in srows]), "bf16", "d_sfd")
+    assert_close(_bf(g["dx"]), dx, "bf16", "dx")
+    assert_close(_bf(g["dx"]), o["dx"], "bf16", "dx (oracle chain)")
+
+
+def test_full_size_backward_parity(orc):
+    """OLMoE-shaped layer: sampled tokens' EPD rows, their dx, and the weight
+    gradients of two slots (the least and the most loaded)."""
+    import oracle.backward as ob
+    cfg = W.CONFIGS["olmoe_bf16"]
+    say("case backward full olmoe_bf16: generating inputs")
+    inp = W.make_layer(cfg, seed=0)
+    dy = W.from_f64(np.random.default_rng(10).standard_normal((cfg.T, cfg.d)), "bf16")
+    g = _run_gpu(cfg, inp, dy)
+    idx = g["topk_idx"]
+    b = orc.brim(idx, g["topk_w"], inp.slot_expert, cfg.E, cfg.D)
+    assert np.array_equal(g["epd_token"], b["epd_token"])
+    X, WR, WGU, WD, DY = (_bf(a) for a in (inp.x, inp.w_router, inp.w_gate_up, inp.w_down, dy))
+    rng = np.random.default_rng(11)
+    tok = np.sort(rng.choice(cfg.T, size=24, replace=False))
+    L = cfg.E // cfg.D
+    rows = []
+    for t in tok:
+        for dv in range(cfg.D):
+            s = b["brim0"][dv, t]
+            if s >= 0:
+                rows += [r for r in b["brim1"][:, s] if r >= 0]
+    rows = np.array(sorted(rows), dtype=np.int64)
+    say(f"  oracle on {tok.size} tokens, {rows.size} EPD rows")
+    o = ob.expert_rows(X, WGU, WD, b, inp.slot_expert, DY, rows, "bf16")
+    I = cfg.I
+    assert_close(_bf(g["d_out_epd"][rows]), o["d_out_epd"], "bf16", "d_out_epd")
+    dw_ref = np.sum(DY[b["epd_token"][rows]] * _bf(g["out_epd"][rows]), axis=1)
+    assert rel_err(g["dw_epd"][rows], dw_ref) <= 1e-4, "dw_epd"
+    assert_close(_bf(g["dgu"][rows, :I]), o["dG"], "bf16", "dG")
+    assert_close(_bf(g["dgu"][rows, I:]), o["dU"], "bf16", "dU")
+    assert_close(_bf(g["d_epd"][rows]), o["d_epd"], "bf16", "d_epd")
+    row_of = _row_of(b, idx, inp.slot_expert, cfg)
+    lg = g["logits"]
+    dl = ob.router_grads(lg, idx, g["topk_w"], cfg.renorm,
+                         lambda t, j: float(g["dw_epd"][row_of(t, j)]), tok)
+    assert rel_err(g["dlogits"][tok], dl) <= 1e-4, "dlogits"
+    dxr = dl @ WR
+    assert rel_err(g["dx_router"][tok], dxr) <= 1e-4, "dx_router"
+    dx, _ = ob.grad_dispatch(b, lambda r: _bf(g["d_epd"][r]), tok, cfg.T, cfg.D, L, cfg.d, "bf16",
+                             g["dx_router"][tok])
+    assert_close(_bf(g["dx"][tok]), dx, "bf16", "dx")
+    cnt = np.diff(b["slot_offset"])
+    for gs in (int(np.argmin(np.where(cnt > 0, cnt, cnt.max() + 1))), int(np.argmax(cnt))):
+        say(f"  weight gradients of slot {gs} ({cnt[gs]} rows)")
+        dWgu, dWd = ob.slot_weight_grads(X, WGU, WD, b, inp.slot_expert, DY, gs, "bf16")
+        e = inp.slot_expert[gs]
+        assert_close(g["dw_gate_up"][e], dWgu, "bf16", f"dW_gate_up[{e}]")
+        assert_close(g["dw_down"][e], dWd, "bf16", f"dW_down[{e}]")

@@ -1,0 +1,118 @@
+"""Pins of the backward oracle (oracle/backward.py) on the CPU.
+
+The gradients through the BRIMs (fp64, no rounding) are checked against
+central finite differences of the standard layer written plainly (no SFD,
+no EPD, selections held fixed), and that plain forward against the C
+oracle's forward.  A structural pin: with renormalised weights, a dy that
+gives every expert output the same value has zero routing gradient.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from tests.tolerance import rel_err
+
+
+def _ob():
+    import oracle.backward as ob
+    return ob
+
+
+def _layer(seed=0, renorm=0, T=24, d=16, E=8, I=12, k=3, D=2):
+    cfg = W.LayerConfig("bwd_tiny", T=T, d=d, E=E, I=I, k=k, D=D, dtype="f32", renorm=renorm,
+                        clusters=3)
+    return cfg, W.make_layer(cfg, seed=seed)
+
+
+def fwd64(x, wr, wgu, wdn, idx, renorm):
+    """The standard MoE layer in fp64 with the selections idx held fixed:
+    y[t] = sum_j w_j FFN_{idx[t][j]}(x_t), w = softmax over all experts."""
+    lg = x @ wr.T
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    T, k = idx.shape
+    I = wgu.shape[1] // 2
+    y = np.zeros_like(x)
+    for t in range(T):
+        wsel = p[t, idx[t]]
+        if renorm:
+            wsel = wsel / wsel.sum()
+        for j in range(k):
+            e = idx[t, j]
+            a = wgu[e, :I] @ x[t]
+            u = wgu[e, I:] @ x[t]
+            h = a / (1.0 + np.exp(-a)) * u
+            y[t] += wsel[j] * (wdn[e] @ h)
+    return y
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_gradients_match_finite_differences(orc, renorm):
+    ob = _ob()
+    cfg, inp = _layer(renorm=renorm)
+    x, wr, wgu, wdn = (np.asarray(a, np.float64) for a in (inp.x, inp.w_router, inp.w_gate_up,
+                                                           inp.w_down))
+    lg, idx, w = orc.route(inp.x, inp.w_router, cfg.k, renorm, "f32")
+    b = orc.brim(idx, w, inp.slot_expert, cfg.E, cfg.D)
+    # the plain fp64 forward agrees with the C oracle's layer (fp32 storage)
+    y_c = orc.layer(inp)["y"]
+    y64 = fwd64(x, wr, wgu, wdn, idx, renorm)
+    assert rel_err(y_c, y64) <= 1e-5
+    rng = np.random.default_rng(3)
+    dy = rng.standard_normal(y64.shape)
+    g = ob.full(x, wr, wgu, wdn, lg, idx, w, renorm, b, inp.slot_expert, dy, cfg.D, "f64")
+
+    def loss(x_, wr_, wgu_, wdn_):
+        return float(np.sum(dy * fwd64(x_, wr_, wgu_, wdn_, idx, renorm)))
+
+    eps = 1e-6
+    for name, arr, grad in [("x", x, g["dx"]), ("w_router", wr, g["dW_router"]),
+                            ("w_gate_up", wgu, g["dW_gate_up"]), ("w_down", wdn, g["dW_down"])]:
+        for _ in range(6):
+            pos = tuple(rng.integers(0, s) for s in arr.shape)
+            if name == "w_gate_up" or name == "w_down":
+                pos = (int(idx[rng.integers(0, cfg.T), 0]),) + pos[1:]  # a used expert
+            args = {"x": x, "w_router": wr, "w_gate_up": wgu, "w_down": wdn}
+            plus = {k_: v.copy() for k_, v in args.items()}
+            minus = {k_: v.copy() for k_, v in args.items()}
+            plus[name][pos] += eps
+            minus[name][pos] -= eps
+            fd = (loss(plus["x"], plus["w_router"], plus["w_gate_up"], plus["w_down"]) -
+                  loss(minus["x"], minus["w_router"], minus["w_gate_up"], minus["w_down"])) / (2 * eps)
+            assert abs(fd - grad[pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+
+
+def test_renormalised_routing_gradient_cancels(orc):
+    """With renormalised weights and identical expert outputs along dy, the
+    weights' gradients are equal within a token, so dp and dlogits vanish."""
+    ob = _ob()
+    cfg, inp = _layer(renorm=1, seed=2)
+    lg, idx, w = orc.route(inp.x, inp.w_router, cfg.k, 1, "f32")
+    dw_equal = lambda t, j: 0.37 * (t + 1)  # same for every pick of a token
+    dl = ob.router_grads(lg, idx, w, 1, dw_equal, np.arange(cfg.T))
+    assert np.abs(dl).max() <= 1e-12
+    # without renormalisation the same dw moves the logits
+    dl0 = ob.router_grads(lg, idx, w, 0, dw_equal, np.arange(cfg.T))
+    assert np.abs(dl0).max() > 1e-3
+
+
+def test_rounded_backward_stays_close_to_exact(orc):
+    """bf16 rounding at the storage points changes the gradients by about
+    the bf16 precision (median), and by a few per cent where a sum cancels
+    (dh = d_out W_down of rounded inputs feeds dG, dU and the weight
+    gradients)."""
+    ob = _ob()
+    cfg = W.LayerConfig("bwd_b", T=40, d=64, E=8, I=64, k=2, D=2, dtype="bf16", clusters=3)
+    inp = W.make_layer(cfg, seed=1)
+    lg, idx, w = orc.route(inp.x, inp.w_router, cfg.k, 0, "bf16")
+    b = orc.brim(idx, w, inp.slot_expert, cfg.E, cfg.D)
+    dy = W.to_f32(W.from_f64(np.random.default_rng(4).standard_normal((cfg.T, cfg.d)), "bf16"),
+                  "bf16")
+    args = (W.to_f32(inp.x, "bf16"), W.to_f32(inp.w_router, "bf16"),
+            W.to_f32(inp.w_gate_up, "bf16"), W.to_f32(inp.w_down, "bf16"))
+    g16 = ob.full(*args, lg, idx, w, 0, b, inp.slot_expert, dy, cfg.D, "bf16")
+    g64 = ob.full(*args, lg, idx, w, 0, b, inp.slot_expert, dy, cfg.D, "f64")
+    for name in ("dx", "dW_gate_up", "dW_down", "dW_router"):
+        o = g64[name]
+        rel = np.abs(g16[name] - o) / np.maximum(np.abs(o), np.sqrt(np.mean(o * o)))
+        assert np.median(rel) <= 2e-3 and rel.max() <= 6e-2, (name, np.median(rel), rel.max())
