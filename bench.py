@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=192)
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many forward steps (for rocprofv3), print nothing else")
+    p.add_argument("--profile-backward", action="store_true",
+                   help="with --profile-steps: run the backward after every forward step")
     p.add_argument("--copy-calibration", action="store_true",
                    help="with --profile-steps: first copy 256 MiB twice (counter scale factors)")
     return p.parse_args()
@@ -217,6 +219,64 @@ def affinity(cfg, lay, torch):
             **us}
 
 
+BACKWARD_STAGES = ("grad_combine", "expert_backward", "router_backward", "grad_dispatch")
+
+
+def backward(lay, cfg, steps, torch):
+    """Forward + backward step (bf16 layers without shared experts): the
+    backward walks the BRIMs in reverse (grad-combine, expert backward GEMMs,
+    router gradient, grad-dispatch) for a seeded upstream gradient.  Times K
+    whole steps, then each backward stage with events between stages."""
+    lay.prepare_backward()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    lay.dy.copy_(torch.randn(lay.dy.shape, generator=g, device="cuda").to(lay.dy.dtype))
+
+    def fwd_bwd(marks=None):
+        step(lay)
+        for j, name in enumerate(BACKWARD_STAGES):
+            if marks is not None:
+                marks[j].record()
+            getattr(lay, name)()
+        if marks is not None:
+            marks[-1].record()
+
+    for _ in range(3):
+        fwd_bwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd_bwd()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    n = max(10, min(steps, 50))
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(BACKWARD_STAGES) + 1)]
+             for _ in range(n)]
+    for i in range(n):
+        fwd_bwd(marks[i])
+    torch.cuda.synchronize()
+    t = {name: float(np.mean([m[j].elapsed_time(m[j + 1]) for m in marks])) / 1e3
+         for j, name in enumerate(BACKWARD_STAGES)}
+    S = int(lay.host("S")[0])
+    T, d, E, I, R, b = cfg.T, cfg.d, cfg.E, cfg.I, cfg.R, elem_bytes(cfg)
+    # expert backward: G/U recompute (2I), dh (I), d_epd (2I), dW_down (I), dW_gate_up (2I)
+    ebw_flop = 2.0 * R * d * 8 * I
+    gc_bytes = (T + S + 2 * R) * d * b + 4.0 * R + 4.0 * cfg.D * T + 4.0 * (E // cfg.D) * S
+    gd_bytes = (R + S + T) * d * b + 4.0 * T * d + 4.0 * cfg.D * T + 4.0 * (E // cfg.D) * S
+    rb_flop = 4.0 * T * E * d
+    return {"ms_per_step": elapsed / steps * 1e3, "tokens_per_s": T * steps / elapsed,
+            "grad_combine_us": t["grad_combine"] * 1e6,
+            "grad_combine_hbm_frac": gc_bytes / t["grad_combine"] / 1e9 / PEAK_HBM_GBS,
+            "expert_backward_us": t["expert_backward"] * 1e6,
+            "expert_backward_flop": ebw_flop,
+            "expert_backward_mfma_frac": ebw_flop / t["expert_backward"] / 1e12
+                                         / PEAK_BF16_TFLOPS,
+            "router_backward_us": t["router_backward"] * 1e6,
+            "router_backward_valu_frac": rb_flop / t["router_backward"] / 1e12 / 78.6,
+            "grad_dispatch_us": t["grad_dispatch"] * 1e6,
+            "grad_dispatch_hbm_frac": gd_bytes / t["grad_dispatch"] / 1e9 / PEAK_HBM_GBS}
+
+
 def cpu_baseline(inp, n_tok):
     """The oracle as it stands, one thread: routing and BRIMs on the full
     batch, expert FFN and combine on a seeded sample of tokens; tokens/s
@@ -304,9 +364,14 @@ def main():
                 dst.copy_(src)
             torch.cuda.synchronize()
             del src, dst
+        if args.profile_backward:
+            lay.prepare_backward()
+            lay.dy.normal_()
         for _ in range(args.profile_steps):
             step(lay)
             lay.coactivation()
+            if args.profile_backward:
+                lay.backward()
         torch.cuda.synchronize()
         print(f"profiled {args.profile_steps} steps of {cfg.name}", flush=True)
         return
@@ -395,6 +460,8 @@ def main():
     if cfg.D >= 4:
         out["pruned"] = pruned(cfg, lay.w, inp.slot_expert, max(1, cfg.D // 4), args.steps, torch)
     out["affinity"] = affinity(cfg, lay, torch)
+    if cfg.dtype == "bf16" and cfg.n_shared == 0:
+        out["backward"] = backward(lay, cfg, args.steps, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

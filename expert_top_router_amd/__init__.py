@@ -63,7 +63,7 @@ def _load(path: str = LIB_PATH):
         "occ_backward_workspace_bytes": (SZ, [DP]),
         "occ_grad_combine": (I32, [DP, P, BP, P, P, P, P, P]),
         "occ_expert_backward": (I32, [DP, P, BP, P, P, P, P, SZ, P, P, SZ, P, P, P, P]),
-        "occ_router_backward": (I32, [DP, P, P, P, P, P, P, BP, P, P, P, P, P]),
+        "occ_router_backward": (I32, [DP, P, P, P, P, P, P, BP, P, P, P, P, P, SZ, P]),
         "occ_grad_dispatch": (I32, [DP, P, BP, P, P, P, P]),
         "occ_cross_coactivation": (I32, [I32, I32, I32, P, I32, I32, P, P, I32, P]),
         "occ_home_device": (I32, [I32, I32, I32, P, I32, I32, P, P, P, P]),
@@ -252,13 +252,15 @@ def occ_expert_backward(desc, epd, brim: occ_brim, slot_expert_host, w_gate_up, 
 
 
 def occ_router_backward(desc, x, w_router, logits, topk_idx, topk_w, slot_expert_host,
-                        brim: occ_brim, dw_epd, dlogits, dx_router, dw_router, stream=None):
+                        brim: occ_brim, dw_epd, dlogits, dx_router, dw_router, bwd_ws,
+                        bwd_ws_bytes, stream=None):
     import numpy as np
     se = np.ascontiguousarray(slot_expert_host, dtype=np.int32)
     _check(_lib.occ_router_backward(C.byref(desc), _ptr(x), _ptr(w_router), _ptr(logits),
                                     _ptr(topk_idx), _ptr(topk_w), se.ctypes.data, C.byref(brim),
                                     _ptr(dw_epd), _ptr(dlogits), _ptr(dx_router),
-                                    _ptr(dw_router), _stream(stream)), "occ_router_backward")
+                                    _ptr(dw_router), _ptr(bwd_ws), bwd_ws_bytes,
+                                    _stream(stream)), "occ_router_backward")
 
 
 def occ_grad_dispatch(desc, d_epd, brim: occ_brim, dx_router, d_sfd, dx, stream=None):

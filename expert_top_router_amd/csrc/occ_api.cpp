@@ -341,7 +341,7 @@ static size_t gu_bytes(const occ_layer_desc &L) {
 
 size_t occ_backward_workspace_bytes(const occ_layer_desc *desc) {
   if (check_backward(desc) != OCC_OK) return 0;
-  return 2 * gu_bytes(*desc);
+  return std::max(2 * gu_bytes(*desc), occ::router_backward_ws_bytes(*desc));
 }
 
 occ_status occ_grad_combine(const occ_layer_desc *desc, const void *dy, const occ_brim *brim,
@@ -391,7 +391,8 @@ occ_status occ_router_backward(const occ_layer_desc *desc, const void *x, const 
                                const float *logits, const int32_t *topk_idx,
                                const float *topk_w, const int32_t *slot_expert_host,
                                const occ_brim *brim, const float *dw_epd, float *dlogits,
-                               float *dx_router, float *dw_router, hipStream_t stream) {
+                               float *dx_router, float *dw_router, void *bwd_ws,
+                               size_t bwd_ws_bytes, hipStream_t stream) {
   OCC_TRY(check_backward(desc));
   OCC_TRY(check_brim(*desc, brim, false));
   const occ_layer_desc &L = *desc;
@@ -400,10 +401,15 @@ occ_status occ_router_backward(const occ_layer_desc *desc, const void *x, const 
       missing(topk_w, Tk) || missing(dw_epd, Tk) || missing(dlogits, T * L.E) ||
       missing(dx_router, T * L.d) || !dw_router)
     return fail(OCC_EINVAL, "router backward: an operand is NULL");
+  const size_t need = occ::router_backward_ws_bytes(L);
+  if (need > 0 && (bwd_ws == nullptr || bwd_ws_bytes < need))
+    return fail(OCC_ENOSPC, "router backward: workspace of %zu bytes, need %zu", bwd_ws_bytes,
+                need);
   occ::Placement pl;
   OCC_TRY(make_placement(L, slot_expert_host, pl));
   return hip_status(occ::launch_router_backward(L, pl, x, w_router, logits, topk_idx, topk_w, *brim,
-                                                dw_epd, dlogits, dx_router, dw_router, stream),
+                                                dw_epd, dlogits, dx_router, dw_router, bwd_ws,
+                                                stream),
                     "occ_router_backward");
 }
 

@@ -173,40 +173,128 @@ __global__ __launch_bounds__(kThreads) void router_grad_kernel(
   if (lane + kWave < E) dl[lane + kWave] = p1 * (dp1 - sdp);
 }
 
-// dx_router[t][c] = sum_e dlogit[t][e] W_r[e][c]  (one thread per output)
-__global__ __launch_bounds__(kThreads) void router_dx_kernel(int T, int d, int E,
-                                                             const float *__restrict__ dlogit,
-                                                             const float *__restrict__ wr,
-                                                             float *__restrict__ dx) {
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (gid >= (int64_t)T * d) return;
-  const int t = (int)(gid / d), c = (int)(gid % d);
-  const float *dl = dlogit + (size_t)t * E;
-  float s = 0.0f;
-  for (int e = 0; e < E; ++e) s = __builtin_fmaf(dl[e], wr[(size_t)e * d + c], s);
-  dx[gid] = s;
+// The router's two products, dx_router = dlogit W_r and dW_r = dlogit^T x,
+// as one fp32 VALU tile kernel (contractions over E and over T in fp32;
+// neither is large enough to pay for a split into bf16 MFMA operands).
+//   C[z][m][n] = sum over k in chunk z of A(m, k) B(k, n)
+//   A(m, k) = a[k * lda + m] when A_KM (m contiguous), a[m * lda + k] otherwise
+//   B(k, n) = b[k * ldb + n] (fp32 or bf16, n contiguous, ldb % 8 == 0)
+// A block owns a 64 x 128 tile of C and one chunk of K (kchunk % 32 == 0);
+// each thread keeps 8 x 4 outputs in registers, both operands pass through
+// LDS 32 k at a time with the next k-slab's loads in flight.
+constexpr int kRBM = 64, kRBN = 128, kRBK = 32;
+
+template <bool A_KM, int DT>
+__global__ __launch_bounds__(kThreads) void router_gemm_kernel(
+    int M, int N, int K, int kchunk, const float *__restrict__ a, int lda,
+    const typename Elem<DT>::T *__restrict__ b, int ldb, float *__restrict__ c) {
+  __shared__ float As[kRBK][kRBM + 4];
+  __shared__ float Bs[kRBK][kRBN];
+  constexpr int BW = DT == OCC_BF16 ? 8 : 4;  // B elements per 16-byte load
+  constexpr int BLOADS = kRBK * kRBN / BW / kThreads;
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.y * kRBM, n0 = blockIdx.x * kRBN;
+  const int k_lo = blockIdx.z * kchunk;
+  const int k_hi = min(K, k_lo + kchunk);
+  const int tx = tid % 32, ty = tid / 32;  // outputs: cols n0+4tx.., rows m0+8ty..
+  float acc[8][4] = {};
+  float ar[8];
+  u32x4 br[BLOADS];
+
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = tid + kThreads * j;
+      const int kk = A_KM ? q / kRBM : q % kRBK, mm = A_KM ? q % kRBM : q / kRBK;
+      const int k = k0 + kk, m = m0 + mm;
+      ar[j] = (k < k_hi && m < M) ? (A_KM ? a[(size_t)k * lda + m] : a[(size_t)m * lda + k])
+                                  : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < BLOADS; ++j) {
+      const int q = tid + kThreads * j;
+      const int kk = q / (kRBN / BW), n = n0 + (q % (kRBN / BW)) * BW;
+      const int k = k0 + kk;
+      br[j] = (k < k_hi && n < N)
+                  ? *reinterpret_cast<const u32x4 *>(b + (size_t)k * ldb + n)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = tid + kThreads * j;
+      As[A_KM ? q / kRBM : q % kRBK][A_KM ? q % kRBM : q / kRBK] = ar[j];
+    }
+#pragma unroll
+    for (int j = 0; j < BLOADS; ++j) {
+      const int q = tid + kThreads * j;
+      float f[BW];
+      widen<DT>(br[j], f);
+      float *dst = &Bs[q / (kRBN / BW)][(q % (kRBN / BW)) * BW];
+#pragma unroll
+      for (int i = 0; i < BW; i += 4)
+        *reinterpret_cast<float4 *>(dst + i) = make_float4(f[i], f[i + 1], f[i + 2], f[i + 3]);
+    }
+  };
+
+  if (k_lo < k_hi) load(k_lo);
+  for (int k0 = k_lo; k0 < k_hi; k0 += kRBK) {
+    __syncthreads();
+    store();
+    __syncthreads();
+    if (k0 + kRBK < k_hi) load(k0 + kRBK);
+#pragma unroll 8
+    for (int kk = 0; kk < kRBK; ++kk) {
+      const float4 a0 = *reinterpret_cast<const float4 *>(&As[kk][ty * 8]);
+      const float4 a1 = *reinterpret_cast<const float4 *>(&As[kk][ty * 8 + 4]);
+      const float4 bv = *reinterpret_cast<const float4 *>(&Bs[kk][tx * 4]);
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bw[j], acc[i][j]);
+    }
+  }
+  const int n = n0 + tx * 4;
+  if (n >= N) return;
+  float *cz = c + (size_t)blockIdx.z * M * N;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + ty * 8 + i;
+    if (m < M)
+      *reinterpret_cast<float4 *>(cz + (size_t)m * N + n) =
+          make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+  }
 }
 
-// dW_r[e][c] = sum_t dlogit[t][e] x[t][c]: a block owns 8 experts and 256
-// columns and walks all tokens (deterministic, no atomics).
-template <int DT>
-__global__ __launch_bounds__(kThreads) void router_dw_kernel(int T, int d, int E,
-                                                             const float *__restrict__ dlogit,
-                                                             const typename Elem<DT>::T *__restrict__ x,
-                                                             float *__restrict__ dwr) {
-  const int c = blockIdx.x * kThreads + threadIdx.x;
-  const int e0 = blockIdx.y * 8;
-  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int t = 0; t < T; ++t) {
-    const float xv = c < d ? Elem<DT>::to_f32(x[(size_t)t * d + c]) : 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (e0 + j < E) s[j] = __builtin_fmaf(dlogit[(size_t)t * E + e0 + j], xv, s[j]);
+// out[i] = sum over z ascending of part[z][i] (n4 float4 groups per part).
+__global__ __launch_bounds__(kThreads) void chunk_sum_kernel(int64_t n4, int chunks,
+                                                             const float4 *__restrict__ part,
+                                                             float4 *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n4) return;
+  float4 s = part[i];
+  for (int z = 1; z < chunks; ++z) {
+    const float4 v = part[z * n4 + i];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
   }
-  if (c < d)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (e0 + j < E) dwr[(size_t)(e0 + j) * d + c] = s[j];
+  out[i] = s;
+}
+
+// Split of dW_r's contraction over T: about two blocks per compute unit,
+// chunks of at least 128 tokens.
+int router_dw_kchunk(const occ_layer_desc &Ld) {
+  const int tiles = ((Ld.E + kRBM - 1) / kRBM) * ((Ld.d + kRBN - 1) / kRBN);
+  const int want = (512 + tiles - 1) / tiles;
+  const int most = (Ld.T + 127) / 128;
+  const int chunks = std::max(1, std::min(want, most));
+  const int per = (Ld.T + chunks - 1) / chunks;
+  return std::max(kRBK, (per + kRBK - 1) / kRBK * kRBK);
 }
 
 int chunks_per_lane(int row16) { return (row16 + kWave - 1) / kWave; }
@@ -235,28 +323,39 @@ hipError_t launch_grad_combine(const occ_layer_desc &Ld, const void *dy, const o
   return hipGetLastError();
 }
 
+size_t router_backward_ws_bytes(const occ_layer_desc &Ld) {
+  const int kc = router_dw_kchunk(Ld);
+  const int chunks = Ld.T > 0 ? (Ld.T + kc - 1) / kc : 1;
+  return chunks > 1 ? (size_t)chunks * Ld.E * Ld.d * sizeof(float) : 0;
+}
+
 hipError_t launch_router_backward(const occ_layer_desc &Ld, const Placement &pl, const void *x,
                                   const float *w_router, const float *logits,
                                   const int32_t *idx, const float *topk_w, const occ_brim &b,
                                   const float *dw, float *dlogit, float *dx_router,
-                                  float *dw_router, hipStream_t st) {
+                                  float *dw_router, void *ws, hipStream_t st) {
   const int T = Ld.T, E = Ld.E, d = Ld.d, L = Ld.E / Ld.D;
   const int ld = Ld.T * (Ld.k < Ld.D ? Ld.k : Ld.D);
+  using BT = Elem<OCC_BF16>::T;
   if (T > 0) {
     router_grad_kernel<<<(T + kTokPerBlock - 1) / kTokPerBlock, kThreads, 0, st>>>(
         T, E, Ld.k, Ld.D, L, ld, Ld.renorm, pl, logits, idx, topk_w, b.brim0, b.brim1, dw,
         dlogit);
-    const int64_t n = (int64_t)T * d;
-    router_dx_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, st>>>(
-        T, d, E, dlogit, w_router, dx_router);
+    const dim3 gx((d + kRBN - 1) / kRBN, (T + kRBM - 1) / kRBM, 1);
+    router_gemm_kernel<false, OCC_F32><<<gx, kThreads, 0, st>>>(
+        T, d, E, (E + kRBK - 1) / kRBK * kRBK, dlogit, E, w_router, d, dx_router);
   }
-  const dim3 grid((d + kThreads - 1) / kThreads, (E + 7) / 8);
-  if (Ld.dtype == OCC_F32)
-    router_dw_kernel<OCC_F32><<<grid, kThreads, 0, st>>>(T, d, E, dlogit,
-                                                          static_cast<const float *>(x), dw_router);
-  else
-    router_dw_kernel<OCC_BF16><<<grid, kThreads, 0, st>>>(
-        T, d, E, dlogit, static_cast<const Elem<OCC_BF16>::T *>(x), dw_router);
+  const int kc = router_dw_kchunk(Ld);
+  const int chunks = T > 0 ? (T + kc - 1) / kc : 1;
+  const dim3 gw((d + kRBN - 1) / kRBN, (E + kRBM - 1) / kRBM, chunks);
+  float *dst = chunks > 1 ? static_cast<float *>(ws) : dw_router;
+  router_gemm_kernel<true, OCC_BF16><<<gw, kThreads, 0, st>>>(
+      E, d, T, kc, dlogit, E, static_cast<const BT *>(x), d, dst);
+  if (chunks > 1) {
+    const int64_t n4 = (int64_t)E * d / 4;
+    chunk_sum_kernel<<<(unsigned)((n4 + kThreads - 1) / kThreads), kThreads, 0, st>>>(
+        n4, chunks, static_cast<const float4 *>(ws), reinterpret_cast<float4 *>(dw_router));
+  }
   return hipGetLastError();
 }
 

@@ -97,7 +97,9 @@ hipError_t launch_router_backward(const occ_layer_desc &L, const Placement &pl, 
                                   const float *w_router, const float *logits,
                                   const int32_t *idx, const float *topk_w, const occ_brim &b,
                                   const float *dw, float *dlogit, float *dx_router,
-                                  float *dw_router, hipStream_t st);
+                                  float *dw_router, void *ws, hipStream_t st);
+// Workspace bytes of launch_router_backward (partial sums of dW_r).
+size_t router_backward_ws_bytes(const occ_layer_desc &L);
 
 hipError_t launch_coactivation(const occ_layer_desc &L, const int32_t *idx, int32_t *counts,
                                int accumulate, hipStream_t st);

@@ -215,7 +215,7 @@ class MoELayer:
     def router_backward(self, stream=None):
         occ_router_backward(self.desc, self.w.x, self.w.w_router, self.logits, self.topk_idx,
                             self.topk_w, self.slot_expert, self.brim, self.dw_epd, self.dlogits,
-                            self.dx_router, self.dw_router, stream)
+                            self.dx_router, self.dw_router, self.bwd_ws, self.bwd_bytes, stream)
 
     def grad_dispatch(self, stream=None):
         occ_grad_dispatch(self.desc, self.d_epd, self.brim, self.dx_router, self.d_sfd, self.dx,

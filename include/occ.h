@@ -229,8 +229,9 @@ occ_status occ_coactivation(const occ_layer_desc *desc, const int32_t *topk_idx,
  * occ_expert_ffn, occ_combine): occ_grad_combine, occ_expert_backward,
  * occ_router_backward, occ_grad_dispatch.  Top-k selection is a constant. */
 
-/* Bytes of the workspace of occ_expert_backward (0 for an invalid or
- * unsupported descriptor). */
+/* Bytes of the workspace of occ_expert_backward and occ_router_backward
+ * (one buffer may serve both calls in turn; 0 for an invalid or unsupported
+ * descriptor). */
 size_t occ_backward_workspace_bytes(const occ_layer_desc *desc);
 
 /* Gradient of the combine, given dy (bf16 [T][d]):
@@ -266,12 +267,17 @@ occ_status occ_expert_backward(const occ_layer_desc *desc, const void *epd, cons
  * over all E experts, from the forward's fp32 logits:
  *   dlogits[t][e] = p[e] (dp[e] - sum_e' p[e'] dp[e'])      (fp32 [T][E])
  *   dx_router     = dlogits W_r                            (fp32 [T][d])
- *   dw_router     = dlogits^T x                            (fp32 [E][d]) */
+ *   dw_router     = dlogits^T x                            (fp32 [E][d])
+ * Both products accumulate in fp32; dw_router sums its token chunks in a
+ * fixed order (deterministic).  bwd_ws: device workspace of at least
+ * occ_backward_workspace_bytes(desc) bytes for the partial sums (ENOSPC when
+ * smaller; its contents are not kept). */
 occ_status occ_router_backward(const occ_layer_desc *desc, const void *x, const float *w_router,
                                const float *logits, const int32_t *topk_idx,
                                const float *topk_w, const int32_t *slot_expert_host,
                                const occ_brim *brim, const float *dw_epd, float *dlogits,
-                               float *dx_router, float *dw_router, hipStream_t stream);
+                               float *dx_router, float *dw_router, void *bwd_ws,
+                               size_t bwd_ws_bytes, hipStream_t stream);
 
 /* Gradient of the dispatch (the combine's walk with unit weights):
  *   d_sfd[s] = sum over l ascending with r = brim1[l][s] >= 0 of d_epd[r]

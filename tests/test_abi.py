@@ -129,8 +129,13 @@ def test_backward_arguments_are_checked(occ):
                                  FAKE, hb, FAKE, FAKE, ws, FAKE, None, FAKE, None)
     assert rc == -1
     rc = lib.occ_router_backward(C.byref(d), FAKE, FAKE, None, FAKE, FAKE, se.ctypes.data,
-                                 C.byref(brim), FAKE, FAKE, FAKE, FAKE, None)
+                                 C.byref(brim), FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
     assert rc == -1
+    # a long batch splits dW_r over token chunks, whose partial sums need the workspace
+    big = _desc(occ, T=8192)
+    rc = lib.occ_router_backward(C.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, se.ctypes.data,
+                                 C.byref(brim), FAKE, FAKE, FAKE, FAKE, FAKE, 0, None)
+    assert rc == -3
 
 
 def test_affinity_arguments_are_checked(occ):

@@ -37,17 +37,24 @@ def _run_gpu(cfg, inp, dy_bits):
     lay.prepare_backward()
     say(f"  gpu forward+backward {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} D={cfg.D}")
     lay.forward()
-    lay.backward(to_device(dy_bits))
+    lay.dy.copy_(to_device(dy_bits))
+    lay.grad_combine()
+    lay.expert_backward()
     torch.cuda.synchronize()
+    # [G | U] and [dG | dU] sit in the workspace (each part 256-byte aligned)
+    # until the router gradient reuses it for its partial sums
     R, I = cfg.R, cfg.I
     ws = lay.bwd_ws.view(torch.int16)
-    half = lay.bwd_bytes // 4  # int16 elements per half of the workspace
+    half = -(-R * 2 * I * 2 // 256) * 256 // 2  # int16 elements before [dG | dU]
+    gu = ws[:R * 2 * I].cpu().numpy().view(np.uint16).reshape(R, 2 * I)
+    dgu = ws[half:half + R * 2 * I].cpu().numpy().view(np.uint16).reshape(R, 2 * I)
+    lay.router_backward()
+    lay.grad_dispatch()
+    torch.cuda.synchronize()
     names = ["topk_idx", "topk_w", "logits", "brim0", "brim1", "slot_offset", "epd_token",
              "epd_sfd", "epd_w", "S", "d_out_epd", "dw_epd", "d_epd", "dw_gate_up", "dw_down",
              "dlogits", "dx_router", "dw_router", "d_sfd", "d_out_sfd", "dx", "out_epd"]
     g = {n: lay.host(n) for n in names}
-    gu = ws[:R * 2 * I].cpu().numpy().view(np.uint16).reshape(R, 2 * I)
-    dgu = ws[half:half + R * 2 * I].cpu().numpy().view(np.uint16).reshape(R, 2 * I)
     g["gu"], g["dgu"] = gu, dgu
     del lay
     torch.cuda.empty_cache()
