@@ -75,11 +75,20 @@ def algorithmic(cfg, S):
     }
 
 
+def gemm_source_sha256():
+    """Hash of the forward GEMM's sources (kernel file and shared header)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "expert_top_router_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ("occ_gemm.hip", "occ_gemm_common.h"):
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(cfg):
     """HBM bytes per launch of the gate/up GEMM from the committed counter
     summary (two rocprofv3 --pmc passes, scaled by a plain copy), or None when
     the workload differs or the GEMM source changed since they were taken."""
-    import hashlib
     import re
     path = os.path.join(ROOT, "profiles", f"pmc_traffic_{cfg.name}.md")
     if not os.path.exists(path):
@@ -87,8 +96,7 @@ def measured_traffic(cfg):
     text = open(path).read()
     m = re.search(r"traffic_bytes_per_launch: (\d+)", text)
     h = re.search(r"gemm_source_sha256: ([0-9a-f]+)", text)
-    src = os.path.join(ROOT, "expert_top_router_amd", "csrc", "occ_gemm.hip")
-    if not m or not h or hashlib.sha256(open(src, "rb").read()).hexdigest() != h.group(1):
+    if not m or not h or gemm_source_sha256() != h.group(1):
         return None
     return int(m.group(1))
 

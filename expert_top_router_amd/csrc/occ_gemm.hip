@@ -18,128 +18,10 @@
 // rows read by one MFMA operand load fall in distinct banks); one barrier per
 // k-tile.  The epilogue applies SwiGLU, rounds to bf16 in hardware, stages
 // the tile in LDS and writes it with 16-byte row stores.
-#include "occ_internal.h"
+#include "occ_gemm_common.h"
 
 namespace occ {
 namespace {
-
-struct GemmArgs {
-  const int32_t *row_offset;  // [G+1] on the device (slots); nullptr: one dense group
-  int G;
-  int dense_rows;
-  const void *A;
-  int64_t lda;
-  const void *B;
-  int64_t ldb;
-  int64_t b_group_stride;  // elements between the weights of consecutive experts
-  int64_t a_bytes;         // bytes of the whole A operand (< 4 GiB: buffer loads)
-  int64_t b_bytes;         // bytes of the whole weight operand (< 4 GiB)
-  int64_t up_offset;       // SwiGLU: elements from a gate row to its up row
-  int nseg;                // output columns per weight segment
-  int64_t nseg_stride;     // elements between weight segments along the output
-  int kseg;                // K per weight segment
-  int64_t kseg_stride;     // elements between weight segments along K
-  int K;
-  int N;                   // output columns
-  void *C;
-  int64_t ldc;
-  // backward GEMMs only
-  int M;                   // output rows when K is grouped (fixed)
-  int64_t c_group_stride;  // elements between the outputs of consecutive experts
-  const void *aux;         // SwiGLU backward: the recomputed [G | U] rows
-  int64_t ldaux;
-  int32_t expert_of_group[OCC_MAX_E];
-};
-
-constexpr int kThreads = 256;  // fp32 kernel
-constexpr int kBK = 64;
-constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
-constexpr int kLdsK = kBK + 8;
-
-// Raw buffer resource over a whole operand.  Built from kernel arguments
-// only, so it is wave-uniform and lives in SGPRs; tile and lane positions go
-// into the 32-bit per-lane offset, the k position into the scalar offset.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const void *base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)(uint32_t)bytes,
-                                           kBufferFlags);
-}
-
-__device__ __forceinline__ float silu(float g) {
-  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-}
-
-// Wave 0 writes cumulative m-tile counts of the groups into ts[0..G].
-__device__ __forceinline__ void group_tile_scan(const int32_t *row_offset, int G, int BM,
-                                                int32_t *ts) {
-  const int lane = threadIdx.x;
-  int carry = 0;
-  if (lane == 0) ts[0] = 0;
-  for (int g0 = 0; g0 < G; g0 += kWave) {
-    const int g = g0 + lane;
-    int v = 0;
-    if (g < G) v = (row_offset[g + 1] - row_offset[g] + BM - 1) / BM;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int u = __shfl_up(v, off);
-      if (lane >= off) v += u;
-    }
-    if (g < G) ts[g + 1] = carry + v;
-    carry += __shfl(v, kWave - 1);
-  }
-}
-
-struct TileCoord {
-  int group, row_begin, rows, n0;
-};
-
-// The tile table of a launch: cumulative m-tiles per group (ts[0..G]) and the
-// group row offsets (ro[0..G]) in LDS; returns the number of tiles.
-template <int BM, int BNO>
-__device__ __forceinline__ int tile_table(const GemmArgs &a, int32_t *ts, int32_t *ro) {
-  const int ntn = (a.N + BNO - 1) / BNO;
-  if (a.row_offset == nullptr) return ((a.dense_rows + BM - 1) / BM) * ntn;
-  if (threadIdx.x < kWave) group_tile_scan(a.row_offset, a.G, BM, ts);
-  for (int g = threadIdx.x; g <= a.G; g += blockDim.x) ro[g] = a.row_offset[g];
-  __syncthreads();
-  return ts[a.G] * ntn;
-}
-
-// Tile number `logical` (slot-major, then n-tile, m-tile fastest).
-template <int BM, int BNO>
-__device__ __forceinline__ TileCoord tile_coord(const GemmArgs &a, const int32_t *ts,
-                                                const int32_t *ro, int logical) {
-  const int ntn = (a.N + BNO - 1) / BNO;
-  TileCoord tc;
-  if (a.row_offset != nullptr) {
-    int lo = 0, hi = a.G - 1;  // last group whose first tile is <= logical
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (ts[mid] * ntn <= logical) lo = mid;
-      else hi = mid - 1;
-    }
-    const int mtg = ts[lo + 1] - ts[lo];
-    const int local = logical - ts[lo] * ntn;
-    const int nt = local / mtg, mt = local - nt * mtg;
-    tc.group = lo;
-    tc.row_begin = ro[lo] + mt * BM;
-    tc.rows = min(BM, ro[lo + 1] - tc.row_begin);
-    tc.n0 = nt * BNO;
-  } else {
-    const int total_mt = (a.dense_rows + BM - 1) / BM;
-    const int nt = logical / total_mt, mt = logical - nt * total_mt;
-    tc.group = 0;
-    tc.row_begin = mt * BM;
-    tc.rows = min(BM, a.dense_rows - tc.row_begin);
-    tc.n0 = nt * BNO;
-  }
-  return tc;
-}
-
-typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // bf16 grouped GEMM.  4 waves in 2 x 2, wave tile (BM/2) x (BN/2) made of
 // 32x32 output blocks of v_mfma_f32_32x32x16_bf16.  Operand layout of that
@@ -373,303 +255,6 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
   }
 }
 
-// ---- backward GEMMs -----------------------------------------------------
-// Expert Coupling in MoE Pretraining, Abstract: every MoE layer runs its
-// all-to-alls in the forward and the backward pass.  The expert backward
-// needs products whose operands are not K-contiguous: the data gradients
-// multiply by W_down and W_gate_up as stored ([K][N]), the weight gradients
-// contract over the rows of a slot (dW[e] = sum over the slot's rows of
-// dout^T x), with K grouped by slot and both operands [K][M] / [K][N].
-// gemm_bwd_kernel covers them with the forward's tile shape (256 x 256 x 64,
-// 2 x 2 waves, v_mfma_f32_32x32x16_bf16) and a plain two-stage LDS pipeline:
-//   ALAY / BLAY 0: element (row, k) at row * ld + k (K-contiguous rows)
-//   ALAY / BLAY 1: element (row, k) at k * ld + row; a thread loads an 8 x 8
-//                  block (8 k rows of 8 contiguous elements) and transposes it
-//                  in registers (v_perm_b32) into the LDS layout of layout 0
-//   GK: groups over K (rows [row_offset[g], row_offset[g+1]) of both
-//       operands, the tail of the last k-tile zeroed); else groups over M as
-//       in the forward
-//   EPI_BF16: rounded bf16 rows (staged in LDS, 16-byte stores)
-//   EPI_SWIGLU_BWD: the product is dh; with G and U read from aux,
-//       dG = dh U silu'(G), dU = dh silu(G) are rounded to bf16 and written
-//       to columns [0, N) and [N, 2N) of C (two staged passes)
-//   EPI_F32: fp32 outputs (weight gradients), one output block per expert
-enum { EPI_BF16 = 0, EPI_SWIGLU_BWD = 1, EPI_F32 = 2 };
-
-// 8 x 8 bf16 transpose: in[i] holds 8 consecutive rows at k = i; out[j]
-// holds the 8 k values of row j (pairs packed low/high as in memory).
-__device__ __forceinline__ void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) out[j][q] = __builtin_amdgcn_perm(in[2 * q + 1][j >> 1],
-                                                                  in[2 * q][j >> 1], sel);
-  }
-}
-
-__device__ __forceinline__ float silu_grad(float g, float sg) {  // d silu / dg, sg = sigmoid(g)
-  return sg * (1.0f + g * (1.0f - sg));
-}
-
-template <int ALAY, int BLAY, bool GK, int EPI>
-__global__ __launch_bounds__(256) void gemm_bwd_kernel(GemmArgs a) {
-  constexpr int BM = 256, BN = 256, NT = 256, WM = 128, WN = 128, MI = 4, NI = 4;
-  constexpr int CH = 8;  // 16-byte loads per thread and operand per k-tile
-  constexpr int STAGE = (BM + BN) * kLdsK;
-  constexpr int CLD = BN + 8;
-  constexpr int KSTEPS = kBK / 16;
-  static_assert(BM * CLD <= 2 * STAGE, "output staging must fit in the tile buffers");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
-  __shared__ int32_t ts[OCC_MAX_E + 1];
-  __shared__ int32_t ro[OCC_MAX_E + 1];
-
-  const int ntn = (a.N + BN - 1) / BN;
-  const int ntm = GK ? (a.M + BM - 1) / BM : 0;
-  int ntiles;
-  if (GK) {
-    for (int g = threadIdx.x; g <= a.G; g += blockDim.x) ro[g] = a.row_offset[g];
-    __syncthreads();
-    ntiles = a.G * ntm * ntn;
-  } else {
-    ntiles = tile_table<BM, BN>(a, ts, ro);
-  }
-  const int xcd = blockIdx.x % kXcds;
-  const int nbx = gridDim.x / kXcds + (xcd < (int)(gridDim.x % kXcds) ? 1 : 0);
-  const int x0 = xcd * (ntiles / kXcds) + min(xcd, ntiles % kXcds);
-  const int x1 = x0 + ntiles / kXcds + (xcd < ntiles % kXcds ? 1 : 0);
-  const __amdgpu_buffer_rsrc_t a_rsrc = operand_rsrc(a.A, a.a_bytes);
-  const __amdgpu_buffer_rsrc_t b_rsrc = operand_rsrc(a.B, a.b_bytes);
-  for (int logical = x0 + (int)(blockIdx.x / kXcds); logical < x1; logical += nbx) {
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
-  const int wm = wave >> 1, wn = wave & 1;
-  // tile: output rows [m0, m0 + mrows), columns [n0, ...), K rows [k_lo, k_hi)
-  int group, m0, mrows, n0, k_lo, k_hi;
-  if (GK) {
-    group = logical / (ntm * ntn);
-    const int rem = logical - group * ntm * ntn;
-    const int nt = rem / ntm, mt = rem - nt * ntm;
-    m0 = mt * BM;
-    mrows = min(BM, a.M - m0);
-    n0 = nt * BN;
-    k_lo = ro[group];
-    k_hi = ro[group + 1];
-  } else {
-    const TileCoord tc = tile_coord<BM, BN>(a, ts, ro, logical);
-    group = tc.group;
-    m0 = tc.row_begin;
-    mrows = tc.rows;
-    n0 = tc.n0;
-    k_lo = 0;
-    k_hi = a.K;
-  }
-  const int expert = a.expert_of_group[group];
-  const int64_t b_base = GK ? 0 : (int64_t)expert * a.b_group_stride;
-  // per-thread load coordinates (k rows relative to the k-tile)
-  int a_row[CH], b_row[CH];  // layout 0: tile row per load; layout 1: k row per load
-  const int blk = tid >> 3, kb = tid & 7;
-  const int a_mb = min(m0 + blk * 8, (GK ? a.M : m0 + mrows) - 8);  // layout 1 only
-  const int b_nb = min(n0 + blk * 8, a.N - 8);
-  int a_dst[CH], b_dst[CH];
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    if (ALAY == 0) {
-      const int c = tid + NT * i;
-      a_row[i] = c >> 3;
-      a_dst[i] = (c >> 3) * kLdsK + (c & 7) * 8;
-    } else {
-      a_row[i] = kb * 8 + i;
-      a_dst[i] = (blk * 8 + i) * kLdsK + kb * 8;
-    }
-    if (BLAY == 0) {
-      const int c = tid + NT * i;
-      b_row[i] = c >> 3;
-      b_dst[i] = BM * kLdsK + (c >> 3) * kLdsK + (c & 7) * 8;
-    } else {
-      b_row[i] = kb * 8 + i;
-      b_dst[i] = BM * kLdsK + (blk * 8 + i) * kLdsK + kb * 8;
-    }
-  }
-  u32x4 ra[CH], rb[CH];
-  // Loads of the k-tile starting at K row kk (kk is wave-uniform).  Layout 1
-  // rows at or past k_hi are read at k_hi - 1 (in bounds) and zeroed.
-  auto load_tile = [&](int kk) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      if (ALAY == 0) {
-        const int r = min(a_row[i], mrows - 1);
-        const uint32_t off = (uint32_t)(((int64_t)(m0 + r) * a.lda + (tid & 7) * 8 + kk) * 2);
-        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
-      } else {
-        const int kr = kk + a_row[i];
-        const uint32_t off = (uint32_t)(((int64_t)min(kr, k_hi - 1) * a.lda + a_mb) * 2);
-        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
-        if (kr >= k_hi) ra[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-      if (BLAY == 0) {
-        const int n = n0 + min(b_row[i], a.N - 1 - n0);
-        const uint32_t off = (uint32_t)((b_base + (int64_t)n * a.ldb + (tid & 7) * 8 + kk) * 2);
-        rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, off, 0, 0));
-      } else {
-        const int kr = kk + b_row[i];
-        const uint32_t off =
-            (uint32_t)((b_base + (int64_t)min(kr, k_hi - 1) * a.ldb + b_nb) * 2);
-        rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, off, 0, 0));
-        if (kr >= k_hi) rb[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t *s_ = smem + buf * STAGE;
-    if (ALAY == 1) {
-      u32x4 t[CH];
-      transpose8(ra, t);
-#pragma unroll
-      for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4 *>(s_ + a_dst[i]) = t[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4 *>(s_ + a_dst[i]) = ra[i];
-    }
-    if (BLAY == 1) {
-      u32x4 t[CH];
-      transpose8(rb, t);
-#pragma unroll
-      for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4 *>(s_ + b_dst[i]) = t[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4 *>(s_ + b_dst[i]) = rb[i];
-    }
-  };
-
-  f32x16 acc[MI][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
-  const int frag_r = lane & 31, frag_k = (lane >> 5) * 8;
-  int a_frag[MI], b_frag[NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) a_frag[mi] = (wm * WM + mi * 32 + frag_r) * kLdsK + frag_k;
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) b_frag[ni] = BM * kLdsK + (wn * WN + ni * 32 + frag_r) * kLdsK + frag_k;
-
-  const int nk = k_hi > k_lo ? (k_hi - k_lo + kBK - 1) / kBK : 0;
-  if (nk > 0) {
-    load_tile(k_lo);
-    store_tile(0);
-    __syncthreads();
-    if (nk > 1) load_tile(k_lo + kBK);
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint16_t *S = smem + (kt & 1) * STAGE;
-      bf16x8v af[2][MI], bfr[2][NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) af[0][mi] = *reinterpret_cast<const bf16x8v *>(S + a_frag[mi]);
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) bfr[0][ni] = *reinterpret_cast<const bf16x8v *>(S + b_frag[ni]);
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int q = ks & 1;
-        if (ks + 1 < KSTEPS) {
-#pragma unroll
-          for (int mi = 0; mi < MI; ++mi)
-            af[q ^ 1][mi] = *reinterpret_cast<const bf16x8v *>(S + a_frag[mi] + (ks + 1) * 16);
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            bfr[q ^ 1][ni] = *reinterpret_cast<const bf16x8v *>(S + b_frag[ni] + (ks + 1) * 16);
-        }
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[q][ni], af[q][mi],
-                                                                 acc[mi][ni], 0, 0, 0);
-      }
-      if (kt + 1 < nk) store_tile((kt + 1) & 1);
-      if (kt + 2 < nk) load_tile(k_lo + (kt + 2) * kBK);
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue (lane l: token row l % 32, columns 8q + 4(l/32) + j) -------
-  const int crow = lane & 31, ccol = (lane >> 5) * 4;
-  if (EPI == EPI_F32) {
-    float *Cg = static_cast<float *>(a.C) + (int64_t)expert * a.c_group_stride;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int row = wm * WM + mi * 32 + crow;
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = wn * WN + ni * 32 + ccol + 8 * q;
-          if (row < mrows && n0 + col < a.N)
-            *reinterpret_cast<float4 *>(Cg + (int64_t)(m0 + row) * a.ldc + n0 + col) =
-                make_float4(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
-                            acc[mi][ni][4 * q + 3]);
-        }
-    }
-  } else {
-    constexpr int PASSES = EPI == EPI_SWIGLU_BWD ? 2 : 1;
-    constexpr int RCH = BN / 8;
-    const uint16_t *G = static_cast<const uint16_t *>(a.aux);
-#pragma unroll
-    for (int pass = 0; pass < PASSES; ++pass) {
-      uint16_t *Cs = smem;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = wm * WM + mi * 32 + crow;
-        const int grow = m0 + min(row, mrows - 1);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int col = wn * WN + ni * 32 + ccol;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float v[4];
-            if (EPI == EPI_SWIGLU_BWD) {
-              const int gc = min(n0 + col + 8 * q, a.N - 4);
-              const u32x2 gp = *reinterpret_cast<const u32x2 *>(G + (int64_t)grow * a.ldaux + gc);
-              const u32x2 up = *reinterpret_cast<const u32x2 *>(G + (int64_t)grow * a.ldaux + a.N + gc);
-              const float gv[4] = {__uint_as_float(gp.x << 16), __uint_as_float(gp.x & 0xffff0000u),
-                                   __uint_as_float(gp.y << 16), __uint_as_float(gp.y & 0xffff0000u)};
-              const float uv[4] = {__uint_as_float(up.x << 16), __uint_as_float(up.x & 0xffff0000u),
-                                   __uint_as_float(up.y << 16), __uint_as_float(up.y & 0xffff0000u)};
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float dh = acc[mi][ni][4 * q + j];
-                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[j]));
-                v[j] = pass == 0 ? dh * uv[j] * silu_grad(gv[j], sg) : dh * gv[j] * sg;
-              }
-            } else {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) v[j] = acc[mi][ni][4 * q + j];
-            }
-            const f32x2v lo = {v[0], v[1]}, hi = {v[2], v[3]};
-            const u32x2 packed = {
-                __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2v)),
-                __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2v))};
-            *reinterpret_cast<u32x2 *>(Cs + row * CLD + col + 8 * q) = packed;
-          }
-        }
-      }
-      __syncthreads();
-      uint16_t *Cg = static_cast<uint16_t *>(a.C) + (int64_t)m0 * a.ldc + n0 + pass * a.N;
-      for (int c = tid; c < BM * RCH; c += NT) {
-        const int r = c / RCH, cc = c - r * RCH;
-        if (r < mrows && n0 + cc * 8 < a.N)
-          *reinterpret_cast<u32x4 *>(Cg + (int64_t)r * a.ldc + cc * 8) =
-              *reinterpret_cast<const u32x4 *>(Cs + r * CLD + cc * 8);
-      }
-      __syncthreads();
-    }
-  }
-  __syncthreads();
-  }
-}
-
 // fp32 layers: one thread per output element, fp32 FMAs in K order.
 template <bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a, int max_rows) {
@@ -733,131 +318,7 @@ hipError_t run_gemm(const GemmArgs &a, int dtype, int max_rows, hipStream_t st) 
   return hipGetLastError();
 }
 
-GemmArgs base_args(const Placement &pl) {
-  GemmArgs a{};
-  for (int g = 0; g < OCC_MAX_E; ++g) a.expert_of_group[g] = pl.expert_at[g];
-  return a;
-}
-
 }  // namespace
-
-namespace {
-
-template <int ALAY, int BLAY, bool GK, int EPI>
-hipError_t launch_bwd(const GemmArgs &a, int64_t tiles, hipStream_t st) {
-  if (tiles <= 0) return hipSuccess;
-  int dev = 0, n_cu = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return hipGetLastError();
-  const int64_t grid = tiles < n_cu ? tiles : n_cu;
-  gemm_bwd_kernel<ALAY, BLAY, GK, EPI><<<(unsigned)grid, 256, 0, st>>>(a);
-  return hipGetLastError();
-}
-
-// upper bound of the tiles of a slot-grouped product with max_rows rows
-int64_t grouped_tiles(int max_rows, int G, int N) {
-  return ((int64_t)max_rows + (int64_t)G * 255) / 256 * ((N + 255) / 256);
-}
-
-}  // namespace
-
-hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_offset,
-                                  const Placement &pl, const void *epd, const void *w_gate_up,
-                                  const void *w_down, const void *h, const void *d_out_epd,
-                                  void *gu, void *dgu, void *d_epd, float *dw_gate_up,
-                                  float *dw_down, hipStream_t st) {
-  const int64_t d = L.d, I = L.I, R = (int64_t)L.T * L.k, E = L.E;
-  hipError_t err;
-  // 1. [G | U] = EPD W_gate_up^T, recomputed and stored in bf16
-  GemmArgs a = base_args(pl);
-  a.row_offset = slot_offset;
-  a.G = L.E;
-  a.A = epd;
-  a.lda = d;
-  a.a_bytes = R * d * 2;
-  a.B = w_gate_up;
-  a.ldb = d;
-  a.b_group_stride = 2 * I * d;
-  a.b_bytes = E * 2 * I * d * 2;
-  a.K = (int)d;
-  a.N = (int)(2 * I);
-  a.C = gu;
-  a.ldc = 2 * I;
-  if ((err = launch_bwd<0, 0, false, EPI_BF16>(a, grouped_tiles((int)R, L.E, a.N), st)) != hipSuccess)
-    return err;
-  // 2. dh = d_out_EPD W_down (W_down[e] is [d][I]); SwiGLU backward -> [dG | dU]
-  a = base_args(pl);
-  a.row_offset = slot_offset;
-  a.G = L.E;
-  a.A = d_out_epd;
-  a.lda = d;
-  a.a_bytes = R * d * 2;
-  a.B = w_down;
-  a.ldb = I;
-  a.b_group_stride = d * I;
-  a.b_bytes = E * d * I * 2;
-  a.K = (int)d;
-  a.N = (int)I;
-  a.aux = gu;
-  a.ldaux = 2 * I;
-  a.C = dgu;
-  a.ldc = 2 * I;
-  if ((err = launch_bwd<0, 1, false, EPI_SWIGLU_BWD>(a, grouped_tiles((int)R, L.E, a.N), st)) !=
-      hipSuccess)
-    return err;
-  // 3. dEPD = [dG | dU] W_gate_up (W_gate_up[e] is [2I][d])
-  a = base_args(pl);
-  a.row_offset = slot_offset;
-  a.G = L.E;
-  a.A = dgu;
-  a.lda = 2 * I;
-  a.a_bytes = R * 2 * I * 2;
-  a.B = w_gate_up;
-  a.ldb = d;
-  a.b_group_stride = 2 * I * d;
-  a.b_bytes = E * 2 * I * d * 2;
-  a.K = (int)(2 * I);
-  a.N = (int)d;
-  a.C = d_epd;
-  a.ldc = d;
-  if ((err = launch_bwd<0, 1, false, EPI_BF16>(a, grouped_tiles((int)R, L.E, a.N), st)) != hipSuccess)
-    return err;
-  // 4. dW_down[e] = sum over the slot's rows of d_out_EPD^T h   ([d][I], fp32)
-  a = base_args(pl);
-  a.row_offset = slot_offset;
-  a.G = L.E;
-  a.A = d_out_epd;
-  a.lda = d;
-  a.a_bytes = R * d * 2;
-  a.M = (int)d;
-  a.B = h;
-  a.ldb = I;
-  a.b_bytes = R * I * 2;
-  a.N = (int)I;
-  a.C = dw_down;
-  a.ldc = I;
-  a.c_group_stride = d * I;
-  if ((err = launch_bwd<1, 1, true, EPI_F32>(a, E * ((d + 255) / 256) * ((I + 255) / 256), st)) !=
-      hipSuccess)
-    return err;
-  // 5. dW_gate_up[e] = sum over the slot's rows of [dG | dU]^T EPD   ([2I][d], fp32)
-  a = base_args(pl);
-  a.row_offset = slot_offset;
-  a.G = L.E;
-  a.A = dgu;
-  a.lda = 2 * I;
-  a.a_bytes = R * 2 * I * 2;
-  a.M = (int)(2 * I);
-  a.B = epd;
-  a.ldb = d;
-  a.b_bytes = R * d * 2;
-  a.N = (int)d;
-  a.C = dw_gate_up;
-  a.ldc = d;
-  a.c_group_stride = 2 * I * d;
-  return launch_bwd<1, 1, true, EPI_F32>(a, E * ((2 * I + 255) / 256) * ((d + 255) / 256), st);
-}
 
 hipError_t launch_expert_up(const occ_layer_desc &L, const void *epd, const int32_t *slot_offset,
                             const Placement &pl, const void *w_gate_up, void *h, const void *x,

@@ -1,0 +1,473 @@
+// Grouped GEMMs of the expert backward (bf16).
+//
+// Expert Coupling in MoE Pretraining, Abstract: every MoE layer runs its
+// all-to-alls in the forward and the backward pass; Occult, Figure 4 caption:
+// expert computing runs on the EPD state.  For the SwiGLU experts
+// (h = silu(G) U, out = h W_down^T) the backward of one slot needs
+//   [G | U] = EPD W_gate_up^T                    (recomputed, as in the forward)
+//   dh      = d_out W_down                       (W_down[e] stored [d][I])
+//   dG = dh U silu'(G),  dU = dh silu(G)          (fused into dh's epilogue)
+//   d_EPD   = [dG | dU] W_gate_up                 (W_gate_up[e] stored [2I][d])
+//   dW_down[e]    = sum over the slot's rows of d_out^T h
+//   dW_gate_up[e] = sum over the slot's rows of [dG | dU]^T EPD
+// Three of them read an operand whose contiguous dimension is not K: the
+// weights as stored, and both operands of the weight gradients, where K runs
+// over the rows of a slot.
+//
+// gemm_bwd_kernel keeps the forward kernel's structure: persistent blocks
+// dealt to the XCDs in contiguous tile ranges, 2 x 2 waves on a 256 x 256 x 64
+// tile of v_mfma_f32_32x32x16_bf16, global tiles through registers (one k-tile
+// ahead) into double-buffered LDS, one barrier per k-tile, the stores of the
+// next tile and the loads of the one after interleaved with the MFMA k steps.
+// Per operand, the layout in memory decides the layout in LDS:
+//   layout 0 (K-contiguous rows): LDS [row][K], row stride 72 elements; an
+//     MFMA operand (8 consecutive k of one row) is one 16-byte LDS read.
+//   layout 1 (rows of K, M or N contiguous): LDS [k][row], copied as stored,
+//     row stride 288 elements (576 bytes: the four k rows that one 16-lane
+//     group reads start 64 bytes apart modulo 256, so a half wave touches
+//     every bank once); an MFMA operand is two ds_read_b64_tr_b16, the CDNA4
+//     LDS transpose read (within 16 lanes, lane i receives element i % 4 of
+//     the 8 bytes read by lane 4j + i / 4, j = 0..3).
+// GK: K is grouped (rows [row_offset[g], row_offset[g+1]) of slot g); rows at
+// or past the end are read at the last row (in bounds) and zeroed in A.
+#include "occ_gemm_common.h"
+
+namespace occ {
+namespace {
+
+enum { EPI_BF16 = 0, EPI_SWIGLU_BWD = 1, EPI_F32 = 2 };
+
+constexpr int kLdsMN = 256 + 32;  // layout-1 LDS row stride (elements)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// MFMA operand (8 consecutive k of one row) from a layout-1 LDS tile: p is the
+// lane's address for k rows 0..3 of the 8, computed by mn_frag_base.
+__device__ __forceinline__ bf16x8v lds_tr8(const uint16_t *p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 4 * kLdsMN));
+  return __builtin_bit_cast(bf16x8v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Lane offset (elements) of a layout-1 operand read for the 32 rows starting
+// at row 0 of the tile: lane l needs row l % 32 and k 8(l/32) .. +7; in its
+// group of 16 lanes, the lane with index r reads k row r / 4 (+4 for the
+// second read) at rows 16 ((l / 16) % 2) + 4 (r % 4) .. +3.
+__device__ __forceinline__ int mn_frag_base(int lane) {
+  const int r = lane & 15;
+  return (8 * (lane >> 5) + (r >> 2)) * kLdsMN + 16 * ((lane >> 4) & 1) + 4 * (r & 3);
+}
+
+__device__ __forceinline__ float silu_grad(float g, float sg) {  // d silu / dg, sg = sigmoid(g)
+  return sg * (1.0f + g * (1.0f - sg));
+}
+
+template <int ALAY, int BLAY, bool GK, int EPI>
+__global__ __launch_bounds__(256) void gemm_bwd_kernel(GemmArgs a) {
+  constexpr int BM = 256, BN = 256, NT = 256, WM = 128, WN = 128, MI = 4, NI = 4;
+  constexpr int CH = 8;  // 16-byte chunks per thread and operand per k-tile
+  constexpr int PER = CH / (kBK / 16);  // chunks stored per k step
+  constexpr int A_SZ = ALAY == 0 ? BM * kLdsK : kBK * kLdsMN;
+  constexpr int B_SZ = BLAY == 0 ? BN * kLdsK : kBK * kLdsMN;
+  constexpr int STAGE = A_SZ + B_SZ;
+  constexpr int CLD = BN + 8;
+  constexpr int KSTEPS = kBK / 16;
+  static_assert(BM * CLD <= 2 * STAGE, "output staging must fit in the tile buffers");
+  static_assert(!GK || (ALAY == 1 && BLAY == 1), "grouped K reads rows of K");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ int32_t ts[OCC_MAX_E + 1];
+  __shared__ int32_t ro[OCC_MAX_E + 1];
+
+  const int ntn = (a.N + BN - 1) / BN;
+  const int ntm = GK ? (a.M + BM - 1) / BM : 0;
+  int ntiles;
+  if (GK) {
+    for (int g = threadIdx.x; g <= a.G; g += blockDim.x) ro[g] = a.row_offset[g];
+    __syncthreads();
+    ntiles = a.G * ntm * ntn;
+  } else {
+    ntiles = tile_table<BM, BN>(a, ts, ro);
+  }
+  const int xcd = blockIdx.x % kXcds;
+  const int nbx = gridDim.x / kXcds + (xcd < (int)(gridDim.x % kXcds) ? 1 : 0);
+  const int x0 = xcd * (ntiles / kXcds) + min(xcd, ntiles % kXcds);
+  const int x1 = x0 + ntiles / kXcds + (xcd < ntiles % kXcds ? 1 : 0);
+  const __amdgpu_buffer_rsrc_t a_rsrc = operand_rsrc(a.A, a.a_bytes);
+  const __amdgpu_buffer_rsrc_t b_rsrc = operand_rsrc(a.B, a.b_bytes);
+  for (int logical = x0 + (int)(blockIdx.x / kXcds); logical < x1; logical += nbx) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int wm = wave >> 1, wn = wave & 1;
+  // tile: output rows [m0, m0 + mrows), columns [n0, ...), K rows [k_lo, k_hi)
+  int group, m0, mrows, n0, k_lo, k_hi;
+  if (GK) {
+    group = logical / (ntm * ntn);
+    const int rem = logical - group * ntm * ntn;
+    const int nt = rem / ntm, mt = rem - nt * ntm;
+    m0 = mt * BM;
+    mrows = min(BM, a.M - m0);
+    n0 = nt * BN;
+    k_lo = ro[group];
+    k_hi = ro[group + 1];
+  } else {
+    const TileCoord tc = tile_coord<BM, BN>(a, ts, ro, logical);
+    group = tc.group;
+    m0 = tc.row_begin;
+    mrows = tc.rows;
+    n0 = tc.n0;
+    k_lo = 0;
+    k_hi = a.K;
+  }
+  const int expert = a.expert_of_group[group];
+  const int64_t b_base = GK ? 0 : (int64_t)expert * a.b_group_stride;
+
+  // Per-thread chunk c = tid + NT * i.  Layout 0: tile row c / 8, k chunk c % 8
+  // (voffset fixed per tile, k in the scalar offset).  Layout 1: k row
+  // c / 32 = tid / 32 + 8 i, column chunk tid % 32 (the same for every i).
+  uint32_t a_off[CH], b_off[CH];
+  int a_dst[CH], b_dst[CH];
+  const int mn_kr = tid >> 5, mn_col = (tid & 31) * 8;
+  const int a_col = min(m0 + mn_col, (GK ? a.M : m0 + mrows) - 8);  // layout 1
+  const int b_col = min(n0 + mn_col, a.N - 8);                       // layout 1
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + NT * i;
+    if (ALAY == 0) {
+      a_off[i] = (uint32_t)(((int64_t)(m0 + min(c >> 3, mrows - 1)) * a.lda + (c & 7) * 8) * 2);
+      a_dst[i] = (c >> 3) * kLdsK + (c & 7) * 8;
+    } else {
+      a_off[i] = (uint32_t)(((int64_t)(mn_kr + 8 * i) * a.lda + a_col) * 2);
+      a_dst[i] = (mn_kr + 8 * i) * kLdsMN + mn_col;
+    }
+    if (BLAY == 0) {
+      const int n = n0 + min(c >> 3, a.N - 1 - n0);
+      b_off[i] = (uint32_t)((b_base + (int64_t)n * a.ldb + (c & 7) * 8) * 2);
+      b_dst[i] = A_SZ + (c >> 3) * kLdsK + (c & 7) * 8;
+    } else {
+      b_off[i] = (uint32_t)((b_base + (int64_t)(mn_kr + 8 * i) * a.ldb + b_col) * 2);
+      b_dst[i] = A_SZ + (mn_kr + 8 * i) * kLdsMN + mn_col;
+    }
+  }
+
+  // Loads of chunk i of the k-tile starting at K row k0 (relative to k_lo).
+  auto load_a = [&](int i, int k0) -> u32x4 {
+    if (ALAY == 0)
+      return __builtin_bit_cast(u32x4,
+                                __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[i], k0 * 2, 0));
+    if (!GK)
+      return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           a_rsrc, a_off[i], (int)((int64_t)k0 * a.lda * 2), 0));
+    const int kr = k_lo + k0 + mn_kr + 8 * i;
+    const uint32_t off = (uint32_t)(((int64_t)min(kr, k_hi - 1) * a.lda + a_col) * 2);
+    u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
+    if (kr >= k_hi) v = u32x4{0u, 0u, 0u, 0u};
+    return v;
+  };
+  auto load_b = [&](int i, int k0) -> u32x4 {
+    if (BLAY == 0)
+      return __builtin_bit_cast(u32x4,
+                                __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[i], k0 * 2, 0));
+    if (!GK)
+      return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           b_rsrc, b_off[i], (int)((int64_t)k0 * a.ldb * 2), 0));
+    const int kr = k_lo + k0 + mn_kr + 8 * i;
+    const uint32_t off = (uint32_t)(((int64_t)min(kr, k_hi - 1) * a.ldb + b_col) * 2);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, off, 0, 0));
+  };
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+
+  // fragment addresses (k step 0) of the wave's 32-row blocks
+  const int frag_r = lane & 31, frag_k = (lane >> 5) * 8;
+  const int mnb = mn_frag_base(lane);
+  int a_frag[MI], b_frag[NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+    a_frag[mi] = ALAY == 0 ? (wm * WM + mi * 32 + frag_r) * kLdsK + frag_k
+                           : mnb + wm * WM + mi * 32;
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+    b_frag[ni] = A_SZ + (BLAY == 0 ? (wn * WN + ni * 32 + frag_r) * kLdsK + frag_k
+                                   : mnb + wn * WN + ni * 32);
+  auto frag_a = [&](const uint16_t *S, int mi, int ks) -> bf16x8v {
+    if (ALAY == 0) return *reinterpret_cast<const bf16x8v *>(S + a_frag[mi] + ks * 16);
+    return lds_tr8(S + a_frag[mi] + ks * 16 * kLdsMN);
+  };
+  auto frag_b = [&](const uint16_t *S, int ni, int ks) -> bf16x8v {
+    if (BLAY == 0) return *reinterpret_cast<const bf16x8v *>(S + b_frag[ni] + ks * 16);
+    return lds_tr8(S + b_frag[ni] + ks * 16 * kLdsMN);
+  };
+
+  const int nk = k_hi > k_lo ? (k_hi - k_lo + kBK - 1) / kBK : 0;
+  if (nk > 0) {
+    u32x4 ra[CH], rb[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      ra[i] = load_a(i, 0);
+      rb[i] = load_b(i, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      *reinterpret_cast<u32x4 *>(smem + a_dst[i]) = ra[i];
+      *reinterpret_cast<u32x4 *>(smem + b_dst[i]) = rb[i];
+    }
+    __syncthreads();
+    {
+      const int k1 = min(1, nk - 1) * kBK;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        ra[i] = load_a(i, k1);
+        rb[i] = load_b(i, k1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Step kt multiplies tile kt while it stores tile kt + 1 (in registers)
+    // into the other buffer and refills the registers with tile kt + 2
+    // (clamped to the last tile: re-reads stay in bounds and are unused).
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint16_t *S = smem + (kt & 1) * STAGE;
+      uint16_t *Wn = smem + ((kt + 1) & 1) * STAGE;
+      const int kn = min(kt + 2, nk - 1) * kBK;
+      bf16x8v af[2][MI], bfr[2][NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) af[0][mi] = frag_a(S, mi, 0);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) bfr[0][ni] = frag_b(S, ni, 0);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int q = ks & 1;
+        if (ks + 1 < KSTEPS) {
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) af[q ^ 1][mi] = frag_a(S, mi, ks + 1);
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) bfr[q ^ 1][ni] = frag_b(S, ni, ks + 1);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[q][ni], af[q][mi],
+                                                                 acc[mi][ni], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int i = ks * PER + j;
+          *reinterpret_cast<u32x4 *>(Wn + a_dst[i]) = ra[i];
+          *reinterpret_cast<u32x4 *>(Wn + b_dst[i]) = rb[i];
+          ra[i] = load_a(i, kn);
+          rb[i] = load_b(i, kn);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue (lane l: output row l % 32, columns 8q + 4(l/32) + j) -------
+  const int crow = lane & 31, ccol = (lane >> 5) * 4;
+  if (EPI == EPI_F32) {
+    float *Cg = static_cast<float *>(a.C) + (int64_t)expert * a.c_group_stride;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = wm * WM + mi * 32 + crow;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = wn * WN + ni * 32 + ccol + 8 * q;
+          if (row < mrows && n0 + col < a.N)
+            *reinterpret_cast<float4 *>(Cg + (int64_t)(m0 + row) * a.ldc + n0 + col) =
+                make_float4(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                            acc[mi][ni][4 * q + 3]);
+        }
+    }
+  } else {
+    // bf16 rows staged in LDS and written with 16-byte stores; the SwiGLU
+    // backward writes dG (pass 0, columns [0, N)) and dU (pass 1, [N, 2N)).
+    constexpr int PASSES = EPI == EPI_SWIGLU_BWD ? 2 : 1;
+    constexpr int RCH = BN / 8;
+    const uint16_t *GU = static_cast<const uint16_t *>(a.aux);
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      uint16_t *Cs = smem;
+      // opaque per pass: G and U are re-read in pass 1 rather than kept live
+      int prow = crow;
+      asm volatile("" : "+v"(prow));
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = wm * WM + mi * 32 + prow;
+        const int grow = m0 + min(row, mrows - 1);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = wn * WN + ni * 32 + ccol;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float v[4];
+            if (EPI == EPI_SWIGLU_BWD) {
+              const int gc = min(n0 + col + 8 * q, a.N - 4);
+              const u32x2 gp = *reinterpret_cast<const u32x2 *>(GU + (int64_t)grow * a.ldaux + gc);
+              const u32x2 up =
+                  *reinterpret_cast<const u32x2 *>(GU + (int64_t)grow * a.ldaux + a.N + gc);
+              const float gv[4] = {__uint_as_float(gp.x << 16), __uint_as_float(gp.x & 0xffff0000u),
+                                   __uint_as_float(gp.y << 16), __uint_as_float(gp.y & 0xffff0000u)};
+              const float uv[4] = {__uint_as_float(up.x << 16), __uint_as_float(up.x & 0xffff0000u),
+                                   __uint_as_float(up.y << 16), __uint_as_float(up.y & 0xffff0000u)};
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float dh = acc[mi][ni][4 * q + j];
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[j]));
+                v[j] = pass == 0 ? dh * uv[j] * silu_grad(gv[j], sg) : dh * gv[j] * sg;
+              }
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) v[j] = acc[mi][ni][4 * q + j];
+            }
+            const f32x2v lo = {v[0], v[1]}, hi = {v[2], v[3]};
+            const u32x2 packed = {
+                __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2v)),
+                __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2v))};
+            *reinterpret_cast<u32x2 *>(Cs + row * CLD + col + 8 * q) = packed;
+          }
+        }
+        // one 32-row block at a time: keeps the G / U loads from being
+        // hoisted all together (register pressure)
+        if (EPI == EPI_SWIGLU_BWD) __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+      uint16_t *Cg = static_cast<uint16_t *>(a.C) + (int64_t)m0 * a.ldc + n0 + pass * a.N;
+      for (int c = tid; c < BM * RCH; c += NT) {
+        const int r = c / RCH, cc = c - r * RCH;
+        if (r < mrows && n0 + cc * 8 < a.N)
+          *reinterpret_cast<u32x4 *>(Cg + (int64_t)r * a.ldc + cc * 8) =
+              *reinterpret_cast<const u32x4 *>(Cs + r * CLD + cc * 8);
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();  // the staging area is the next tile's first LDS stage
+  }
+}
+
+template <int ALAY, int BLAY, bool GK, int EPI>
+hipError_t launch_bwd(const GemmArgs &a, int64_t tiles, hipStream_t st) {
+  if (tiles <= 0) return hipSuccess;
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipGetLastError();
+  const int64_t grid = tiles < n_cu ? tiles : n_cu;
+  gemm_bwd_kernel<ALAY, BLAY, GK, EPI><<<(unsigned)grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// upper bound of the tiles of a slot-grouped product with max_rows rows
+int64_t grouped_tiles(int max_rows, int G, int N) {
+  return ((int64_t)max_rows + (int64_t)G * 255) / 256 * ((N + 255) / 256);
+}
+
+}  // namespace
+
+hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_offset,
+                                  const Placement &pl, const void *epd, const void *w_gate_up,
+                                  const void *w_down, const void *h, const void *d_out_epd,
+                                  void *gu, void *dgu, void *d_epd, float *dw_gate_up,
+                                  float *dw_down, hipStream_t st) {
+  const int64_t d = L.d, I = L.I, R = (int64_t)L.T * L.k, E = L.E;
+  hipError_t err;
+  // 1. [G | U] = EPD W_gate_up^T, recomputed and stored in bf16
+  GemmArgs a = base_args(pl);
+  a.row_offset = slot_offset;
+  a.G = L.E;
+  a.A = epd;
+  a.lda = d;
+  a.a_bytes = R * d * 2;
+  a.B = w_gate_up;
+  a.ldb = d;
+  a.b_group_stride = 2 * I * d;
+  a.b_bytes = E * 2 * I * d * 2;
+  a.K = (int)d;
+  a.N = (int)(2 * I);
+  a.C = gu;
+  a.ldc = 2 * I;
+  if ((err = launch_bwd<0, 0, false, EPI_BF16>(a, grouped_tiles((int)R, L.E, a.N), st)) != hipSuccess)
+    return err;
+  // 2. dh = d_out_EPD W_down (W_down[e] is [d][I]); SwiGLU backward -> [dG | dU]
+  a = base_args(pl);
+  a.row_offset = slot_offset;
+  a.G = L.E;
+  a.A = d_out_epd;
+  a.lda = d;
+  a.a_bytes = R * d * 2;
+  a.B = w_down;
+  a.ldb = I;
+  a.b_group_stride = d * I;
+  a.b_bytes = E * d * I * 2;
+  a.K = (int)d;
+  a.N = (int)I;
+  a.aux = gu;
+  a.ldaux = 2 * I;
+  a.C = dgu;
+  a.ldc = 2 * I;
+  if ((err = launch_bwd<0, 1, false, EPI_SWIGLU_BWD>(a, grouped_tiles((int)R, L.E, a.N), st)) !=
+      hipSuccess)
+    return err;
+  // 3. dEPD = [dG | dU] W_gate_up (W_gate_up[e] is [2I][d])
+  a = base_args(pl);
+  a.row_offset = slot_offset;
+  a.G = L.E;
+  a.A = dgu;
+  a.lda = 2 * I;
+  a.a_bytes = R * 2 * I * 2;
+  a.B = w_gate_up;
+  a.ldb = d;
+  a.b_group_stride = 2 * I * d;
+  a.b_bytes = E * 2 * I * d * 2;
+  a.K = (int)(2 * I);
+  a.N = (int)d;
+  a.C = d_epd;
+  a.ldc = d;
+  if ((err = launch_bwd<0, 1, false, EPI_BF16>(a, grouped_tiles((int)R, L.E, a.N), st)) != hipSuccess)
+    return err;
+  // 4. dW_down[e] = sum over the slot's rows of d_out_EPD^T h   ([d][I], fp32)
+  a = base_args(pl);
+  a.row_offset = slot_offset;
+  a.G = L.E;
+  a.A = d_out_epd;
+  a.lda = d;
+  a.a_bytes = R * d * 2;
+  a.M = (int)d;
+  a.B = h;
+  a.ldb = I;
+  a.b_bytes = R * I * 2;
+  a.N = (int)I;
+  a.C = dw_down;
+  a.ldc = I;
+  a.c_group_stride = d * I;
+  if ((err = launch_bwd<1, 1, true, EPI_F32>(a, E * ((d + 255) / 256) * ((I + 255) / 256), st)) !=
+      hipSuccess)
+    return err;
+  // 5. dW_gate_up[e] = sum over the slot's rows of [dG | dU]^T EPD   ([2I][d], fp32)
+  a = base_args(pl);
+  a.row_offset = slot_offset;
+  a.G = L.E;
+  a.A = dgu;
+  a.lda = 2 * I;
+  a.a_bytes = R * 2 * I * 2;
+  a.M = (int)(2 * I);
+  a.B = epd;
+  a.ldb = d;
+  a.b_bytes = R * d * 2;
+  a.N = (int)d;
+  a.C = dw_gate_up;
+  a.ldc = d;
+  a.c_group_stride = 2 * I * d;
+  return launch_bwd<1, 1, true, EPI_F32>(a, E * ((2 * I + 255) / 256) * ((d + 255) / 256), st);
+}
+}  // namespace occ
