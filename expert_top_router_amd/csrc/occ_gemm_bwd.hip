@@ -28,8 +28,9 @@
 //     every bank once); an MFMA operand is two ds_read_b64_tr_b16, the CDNA4
 //     LDS transpose read (within 16 lanes, lane i receives element i % 4 of
 //     the 8 bytes read by lane 4j + i / 4, j = 0..3).
-// GK: K is grouped (rows [row_offset[g], row_offset[g+1]) of slot g); rows at
-// or past the end are read at the last row (in bounds) and zeroed in A.
+// GK: K is grouped (rows [row_offset[g], row_offset[g+1]) of slot g); the
+// operands' buffer resources end at the slot's last row, so rows past it in
+// the last k-tile load as zero (the buffer unit's range check).
 #include "occ_gemm_common.h"
 
 namespace occ {
@@ -78,24 +79,46 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
   __shared__ int32_t ts[OCC_MAX_E + 1];
   __shared__ int32_t ro[OCC_MAX_E + 1];
+  __shared__ int32_t byrank[OCC_MAX_E];
 
   const int ntn = (a.N + BN - 1) / BN;
   const int ntm = GK ? (a.M + BM - 1) / BM : 0;
-  int ntiles;
+  // Blocks are dealt round-robin to the XCDs (nx groups when the grid is
+  // smaller); the blocks of group x walk its tiles with stride nbx.
+  const int nx = min((int)gridDim.x, kXcds);
+  const int xcd = blockIdx.x % nx;
+  const int nbx = gridDim.x / nx + (xcd < (int)(gridDim.x % nx) ? 1 : 0);
+  int x0, x1;
   if (GK) {
+    // A slot's tiles all contract over its rows, so a tile costs about its
+    // slot's row count.  Slots are ranked by rows (descending, lower slot on
+    // ties) and dealt to the groups in snake order (0..nx-1, nx-1..0, ...):
+    // the j-th slot of group x has rank nx j + (j even ? x : nx - 1 - x).
     for (int g = threadIdx.x; g <= a.G; g += blockDim.x) ro[g] = a.row_offset[g];
     __syncthreads();
-    ntiles = a.G * ntm * ntn;
+    for (int g = threadIdx.x; g < a.G; g += blockDim.x) {
+      const int rg = ro[g + 1] - ro[g];
+      int r = 0;
+      for (int h = 0; h < a.G; ++h) {
+        const int rh = ro[h + 1] - ro[h];
+        r += (rh > rg || (rh == rg && h < g)) ? 1 : 0;
+      }
+      byrank[r] = g;
+    }
+    __syncthreads();
+    int nslot = 0;
+    for (int j = 0; nx * j + ((j & 1) ? nx - 1 - xcd : xcd) < a.G; ++j) ++nslot;
+    x0 = 0;
+    x1 = nslot * ntm * ntn;
   } else {
-    ntiles = tile_table<BM, BN>(a, ts, ro);
+    // tiles in slot order, contiguous ranges per group
+    const int ntiles = tile_table<BM, BN>(a, ts, ro);
+    x0 = xcd * (ntiles / nx) + min(xcd, ntiles % nx);
+    x1 = x0 + ntiles / nx + (xcd < ntiles % nx ? 1 : 0);
   }
-  const int xcd = blockIdx.x % kXcds;
-  const int nbx = gridDim.x / kXcds + (xcd < (int)(gridDim.x % kXcds) ? 1 : 0);
-  const int x0 = xcd * (ntiles / kXcds) + min(xcd, ntiles % kXcds);
-  const int x1 = x0 + ntiles / kXcds + (xcd < ntiles % kXcds ? 1 : 0);
   const __amdgpu_buffer_rsrc_t a_rsrc = operand_rsrc(a.A, a.a_bytes);
   const __amdgpu_buffer_rsrc_t b_rsrc = operand_rsrc(a.B, a.b_bytes);
-  for (int logical = x0 + (int)(blockIdx.x / kXcds); logical < x1; logical += nbx) {
+  for (int logical = x0 + (int)(blockIdx.x / nx); logical < x1; logical += nbx) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -103,8 +126,9 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(GemmArgs a) {
   // tile: output rows [m0, m0 + mrows), columns [n0, ...), K rows [k_lo, k_hi)
   int group, m0, mrows, n0, k_lo, k_hi;
   if (GK) {
-    group = logical / (ntm * ntn);
-    const int rem = logical - group * ntm * ntn;
+    const int j = logical / (ntm * ntn);
+    group = byrank[nx * j + ((j & 1) ? nx - 1 - xcd : xcd)];
+    const int rem = logical - j * ntm * ntn;
     const int nt = rem / ntm, mt = rem - nt * ntm;
     m0 = mt * BM;
     mrows = min(BM, a.M - m0);
@@ -120,6 +144,13 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(GemmArgs a) {
     k_lo = 0;
     k_hi = a.K;
   }
+  // tile coordinates are uniform over the block: keep them in scalar registers
+  group = __builtin_amdgcn_readfirstlane(group);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  mrows = __builtin_amdgcn_readfirstlane(mrows);
+  n0 = __builtin_amdgcn_readfirstlane(n0);
+  k_lo = __builtin_amdgcn_readfirstlane(k_lo);
+  k_hi = __builtin_amdgcn_readfirstlane(k_hi);
   const int expert = a.expert_of_group[group];
   const int64_t b_base = GK ? 0 : (int64_t)expert * a.b_group_stride;
 
@@ -138,7 +169,7 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(GemmArgs a) {
       a_off[i] = (uint32_t)(((int64_t)(m0 + min(c >> 3, mrows - 1)) * a.lda + (c & 7) * 8) * 2);
       a_dst[i] = (c >> 3) * kLdsK + (c & 7) * 8;
     } else {
-      a_off[i] = (uint32_t)(((int64_t)(mn_kr + 8 * i) * a.lda + a_col) * 2);
+      a_off[i] = (uint32_t)(((int64_t)(k_lo + mn_kr + 8 * i) * a.lda + a_col) * 2);
       a_dst[i] = (mn_kr + 8 * i) * kLdsMN + mn_col;
     }
     if (BLAY == 0) {
@@ -146,12 +177,22 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(GemmArgs a) {
       b_off[i] = (uint32_t)((b_base + (int64_t)n * a.ldb + (c & 7) * 8) * 2);
       b_dst[i] = A_SZ + (c >> 3) * kLdsK + (c & 7) * 8;
     } else {
-      b_off[i] = (uint32_t)((b_base + (int64_t)(mn_kr + 8 * i) * a.ldb + b_col) * 2);
+      b_off[i] = (uint32_t)((b_base + (int64_t)(k_lo + mn_kr + 8 * i) * a.ldb + b_col) * 2);
       b_dst[i] = A_SZ + (mn_kr + 8 * i) * kLdsMN + mn_col;
     }
   }
 
   // Loads of chunk i of the k-tile starting at K row k0 (relative to k_lo).
+  // Layout 0: fixed per-lane offset, k in the scalar offset.  Layout 1 with a
+  // fixed K: fixed per-lane offset, k row in the scalar offset.  Grouped K:
+  // the operand's buffer resource ends at the slot's last row (k_hi), and the
+  // whole offset goes into the per-lane offset, which the buffer unit checks
+  // against that size: rows at or past k_hi in the last k-tile read as zero
+  // and touch no memory.
+  const __amdgpu_buffer_rsrc_t ga_rsrc =
+      GK ? operand_rsrc(a.A, (int64_t)k_hi * a.lda * 2) : a_rsrc;
+  const __amdgpu_buffer_rsrc_t gb_rsrc =
+      GK ? operand_rsrc(a.B, (int64_t)k_hi * a.ldb * 2) : b_rsrc;
   auto load_a = [&](int i, int k0) -> u32x4 {
     if (ALAY == 0)
       return __builtin_bit_cast(u32x4,
@@ -159,11 +200,8 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(GemmArgs a) {
     if (!GK)
       return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                            a_rsrc, a_off[i], (int)((int64_t)k0 * a.lda * 2), 0));
-    const int kr = k_lo + k0 + mn_kr + 8 * i;
-    const uint32_t off = (uint32_t)(((int64_t)min(kr, k_hi - 1) * a.lda + a_col) * 2);
-    u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0));
-    if (kr >= k_hi) v = u32x4{0u, 0u, 0u, 0u};
-    return v;
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         ga_rsrc, a_off[i] + (uint32_t)(k0 * a.lda * 2), 0, 0));
   };
   auto load_b = [&](int i, int k0) -> u32x4 {
     if (BLAY == 0)
@@ -172,9 +210,8 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(GemmArgs a) {
     if (!GK)
       return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                            b_rsrc, b_off[i], (int)((int64_t)k0 * a.ldb * 2), 0));
-    const int kr = k_lo + k0 + mn_kr + 8 * i;
-    const uint32_t off = (uint32_t)(((int64_t)min(kr, k_hi - 1) * a.ldb + b_col) * 2);
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, off, 0, 0));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         gb_rsrc, b_off[i] + (uint32_t)(k0 * a.ldb * 2), 0, 0));
   };
 
   f32x16 acc[MI][NI];
