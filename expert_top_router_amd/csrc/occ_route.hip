@@ -27,6 +27,16 @@ namespace occ {
 namespace {
 
 
+// acc = fma(x of lane J of this lane's 16-lane row, w, acc): the FMA takes
+// its first operand through DPP row_newbcast (CDNA3/4), which hands every
+// lane of a row the value held by lane J of that row.  One v_fmac_f32_dpp,
+// rounding once like fmaf.
+template <int J> __device__ __forceinline__ void fmac_row_bcast(float &acc, float x, float w) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc)
+      : "v"(x), "v"(w), "i"(J));
+}
+
 struct Best {
   float key;
   int e;
@@ -118,6 +128,42 @@ __global__ __launch_bounds__(THR) void route_topk_kernel(
     }                                                                                 \
   } while (0)
 
+  // Whole-wave segments (ESEG == 64, one token per segment) with few tokens
+  // per lane: per 16 columns a lane reads its router values (4 x 16 bytes per
+  // expert) and, per token, only the one X value of its position in its
+  // 16-lane row; the FMAs take X through DPP row broadcasts.  X reads from LDS
+  // drop 16-fold against the broadcast 16-byte reads of the general loop,
+  // which matters when 1-2 tokens per lane leave the router reads little
+  // reuse (OLMoE-shaped layer: 57 -> 48 us); with 8 tokens per lane the
+  // general loop measured slightly faster.  jn is a multiple of 8.
+  constexpr bool BC = ESEG == kWave && TPL <= 2;
+  auto chunk_bcast = [&](const float *wsc, const float *xsc, int jn) {
+    const int xl = lane & 15;
+    for (int g = 0; g < jn; g += 16) {
+      float4 wv[EP][4];
+#pragma unroll
+      for (int i = 0; i < EP; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          wv[i][v] = *reinterpret_cast<const float4 *>(&wsc[(el + ESEG * i) * kLds + g + 4 * v]);
+      float xv[TPL];
+#pragma unroll
+      for (int m = 0; m < TPL; ++m) xv[m] = xsc[(wave * TW + q + Q * m) * kLds + g + xl];
+      // j ascending inside every chain; the TPL * EP chains interleave
+#define OCC_ROUTE_BC(J, C)                                                            \
+  _Pragma("unroll") for (int m = 0; m < TPL; ++m)                                     \
+  _Pragma("unroll") for (int i = 0; i < EP; ++i)                                      \
+      fmac_row_bcast<J>(acc[m][i], xv[m], wv[i][(J) / 4].C);
+      OCC_ROUTE_BC(0, x) OCC_ROUTE_BC(1, y) OCC_ROUTE_BC(2, z) OCC_ROUTE_BC(3, w)
+      OCC_ROUTE_BC(4, x) OCC_ROUTE_BC(5, y) OCC_ROUTE_BC(6, z) OCC_ROUTE_BC(7, w)
+      if (g + 8 < jn) {
+        OCC_ROUTE_BC(8, x) OCC_ROUTE_BC(9, y) OCC_ROUTE_BC(10, z) OCC_ROUTE_BC(11, w)
+        OCC_ROUTE_BC(12, x) OCC_ROUTE_BC(13, y) OCC_ROUTE_BC(14, z) OCC_ROUTE_BC(15, w)
+      }
+#undef OCC_ROUTE_BC
+    }
+  };
+
   const int nch = (d + kJC - 1) / kJC;
   // chunk ch is multiplied from LDS buffer ch % 2, chunk ch + 1 waits in
   // register set (ch + 1) % 2, and chunk ch + 2 is loading into set ch % 2
@@ -132,6 +178,9 @@ __global__ __launch_bounds__(THR) void route_topk_kernel(
     const int jn = min(kJC, d - j0); /* multiple of 8 (d % 8 == 0) */                 \
     const float *xsc = xs[cur_];                                                      \
     const float *wsc = ws[cur_];                                                      \
+    if (BC) {                                                                         \
+      chunk_bcast(wsc, xsc, jn);                                                      \
+    } else {                                                                          \
     _Pragma("unroll 8") for (int jj = 0; jj < kJC; jj += 4) {                         \
       if (jj < jn) {                                                                  \
         float4 wv[EP], xv[TPL];                                                       \
@@ -153,6 +202,7 @@ __global__ __launch_bounds__(THR) void route_topk_kernel(
         _Pragma("unroll") for (int i = 0; i < EP; ++i)                                \
             acc[m][i] = __builtin_fmaf(xv[m].w, wv[i].w, acc[m][i]);                  \
       }                                                                               \
+    }                                                                                 \
     }                                                                                 \
     if ((ch_) + 1 < nch) OCC_ROUTE_STORE(xn, wn, (cur_) ^ 1);                         \
     if ((ch_) + 3 < nch) OCC_ROUTE_LOAD(xn, wn, ((ch_) + 3) * kJC);                   \
@@ -256,7 +306,9 @@ hipError_t launch_tpl(const occ_layer_desc &L, const void *x, const float *wr, i
   // About two waves per SIMD (2048) before lengthening the per-lane token
   // list.  Routers of 33..64 experts use 8-wave blocks: every block re-reads
   // the whole router, so more tokens per block means less router traffic
-  // (wider routers already carry 8 tokens per lane).
+  // (wider routers already carry 8 tokens per lane).  (One 4-wave block per
+  // CU with four tokens per lane measured slower: one wave per SIMD leaves
+  // the LDS and FMA latencies exposed.)
   constexpr int THR = ESEG == 64 && EP == 1 ? 512 : 256;
   const long per = (long)L.T / ((long)Q * 2048);
   if (per >= 8) launch_jc<DT, ESEG, EP, 8, THR>(L, x, wr, idx, w, logits, st);
