@@ -176,3 +176,23 @@ def test_full_size_backward_parity(orc):
         e = inp.slot_expert[gs]
         assert_close(g["dw_gate_up"][e], dWgu, "bf16", f"dW_gate_up[{e}]")
         assert_close(g["dw_down"][e], dWd, "bf16", f"dW_down[{e}]")
+
+
+def test_empty_batch_backward():
+    """T = 0: every call is a no-op on the rows, and the weight gradients
+    (sums over no rows) are written as zeros over poisoned buffers."""
+    import torch
+    from expert_top_router_amd.layer import MoELayer, upload_inputs
+    cfg = W.LayerConfig("bf16_empty", T=0, d=64, E=8, I=64, k=2, D=2, dtype="bf16")
+    inp = W.make_layer(cfg, seed=3)
+    lay = MoELayer(cfg, upload_inputs(inp), inp.slot_expert, with_logits=True)
+    lay.prepare_backward()
+    say("  gpu forward+backward bf16_empty T=0")
+    for name in ("dw_gate_up", "dw_down", "dw_router"):
+        getattr(lay, name).fill_(float("nan"))
+    lay.forward()
+    lay.backward()
+    torch.cuda.synchronize()
+    for name in ("dw_gate_up", "dw_down", "dw_router"):
+        g = lay.host(name)
+        assert g.size > 0 and np.all(g == 0.0), name
