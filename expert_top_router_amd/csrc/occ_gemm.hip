@@ -16,8 +16,9 @@
 // tiles go through registers (raw buffer loads, one k-tile ahead) into
 // double-buffered, padded LDS (row stride 72 elements = 144 bytes, so the 16
 // rows read by one MFMA operand load fall in distinct banks); one barrier per
-// k-tile.  The epilogue applies SwiGLU, rounds to bf16 in hardware, stages
-// the tile in LDS and writes it with 16-byte row stores.
+// k-tile.  The epilogue applies SwiGLU, rounds to bf16 in hardware and
+// stores the rows (straight from registers for SwiGLU tiles, through an LDS
+// staging area for full-width tiles).
 #include "occ_gemm_common.h"
 
 namespace occ {
@@ -38,9 +39,9 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
   constexpr int B_CH = BN * (kBK / 8) / NT;
   static_assert(A_CH * NT == BM * (kBK / 8) && B_CH * NT == BN * (kBK / 8), "whole chunks");
   constexpr int STAGE = (BM + BN) * kLdsK;          // elements per LDS stage
-  constexpr int CLD = BNO + 8;                      // staged output row stride
   constexpr int KSTEPS = kBK / 16;
-  static_assert(BM * CLD <= 2 * STAGE, "output staging must fit in the tile buffers");
+  constexpr int CLD = BNO + 8;  // staged output row stride (full-width tiles)
+  static_assert(SWIGLU || BM * CLD <= 2 * STAGE, "output staging must fit in the tile buffers");
   static_assert(!SWIGLU || NI % 2 == 0, "gate and up halves");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
   __shared__ int32_t ts[OCC_MAX_E + 1];
@@ -213,12 +214,19 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
 #undef OCC_LOAD_REGS
 #undef OCC_STORE_LDS
 
-  // ---- epilogue: (SwiGLU), round to bf16, stage, coalesced row stores -----
+  // ---- epilogue: (SwiGLU), round to bf16, store ---------------------------
   // The weight fragment is the MFMA's first operand, so a 32 x 32 accumulator
   // block holds (output column, token) pairs: lane l has token row l % 32 and
   // the output columns 8q + 4(l / 32) + j (j < 4) in registers 4q + j, i.e.
   // four runs of 4 adjacent columns.  Each run is rounded to bf16 in hardware
-  // (round to nearest even) and staged with one 8-byte LDS store.
+  // (round to nearest even).  SwiGLU tiles (128 output columns) store each
+  // run with one 8-byte store: lanes l and l + 32 write adjacent runs and the
+  // four q of a block complete 64 bytes of a row, which the write-back L2
+  // merges into whole lines; staging these tiles in LDS measured slower (two
+  // more barriers and an LDS round trip).  Full-width tiles (256 columns) are
+  // staged in LDS with 8-byte stores and written as 16-byte row segments,
+  // which measured faster for them.
+  uint16_t *Cg = static_cast<uint16_t *>(a.C) + (int64_t)tc.row_begin * a.ldc + tc.n0;
   uint16_t *Cs = smem;
   const int crow = lane & 31, ccol = (lane >> 5) * 4;
 #pragma unroll
@@ -238,20 +246,28 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
         const f32x2v lo = {v[0], v[1]}, hi = {v[2], v[3]};
         const u32x2 packed = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2v)),
                               __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2v))};
-        *reinterpret_cast<u32x2 *>(Cs + row * CLD + col + 8 * q) = packed;
+        if (SWIGLU) {
+          if (row < tc.rows && tc.n0 + col + 8 * q < a.N)
+            *reinterpret_cast<u32x2 *>(Cg + (int64_t)row * a.ldc + col + 8 * q) = packed;
+        } else {
+          *reinterpret_cast<u32x2 *>(Cs + row * CLD + col + 8 * q) = packed;
+        }
       }
     }
   }
-  __syncthreads();
-  constexpr int RCH = BNO / 8;  // 16-byte chunks per output row
-  uint16_t *Cg = static_cast<uint16_t *>(a.C) + (int64_t)tc.row_begin * a.ldc + tc.n0;
-  for (int c = tid; c < BM * RCH; c += NT) {
-    const int r = c / RCH, cc = c - r * RCH;
-    if (r < tc.rows && tc.n0 + cc * 8 < a.N)
-      *reinterpret_cast<u32x4 *>(Cg + (int64_t)r * a.ldc + cc * 8) =
-          *reinterpret_cast<const u32x4 *>(Cs + r * CLD + cc * 8);
+  if (!SWIGLU) {
+    __syncthreads();
+    constexpr int RCH = BNO / 8;  // 16-byte chunks per output row
+    for (int c = tid; c < BM * RCH; c += NT) {
+      const int r = c / RCH, cc = c - r * RCH;
+      if (r < tc.rows && tc.n0 + cc * 8 < a.N)
+        *reinterpret_cast<u32x4 *>(Cg + (int64_t)r * a.ldc + cc * 8) =
+            *reinterpret_cast<const u32x4 *>(Cs + r * CLD + cc * 8);
+    }
+    __syncthreads();  // the staging area is the next tile's first LDS stage
   }
-  __syncthreads();  // the staging area is the next tile's first LDS stage
+  // (SwiGLU tiles: the k loop ended with a barrier, so the next tile's first
+  // LDS stores cannot overwrite a stage another wave still reads)
   }
 }
 
