@@ -29,7 +29,11 @@
 namespace occ {
 namespace {
 
-constexpr int kTB = 64;  // tokens per block = one wave (many blocks, no intra-block prefix)
+constexpr int kTB = 64;  // tokens per block = one wave's lanes (no intra-block prefix)
+// Waves per count / fill block: all of them hold the block's 64 tokens and
+// split the keys (devices, slots) among themselves, so a wave's serial loop
+// over keys is kWB times shorter.
+constexpr int kWB = 4;
 
 // Per-lane view of one token: device bitmask and slot bitmask (E <= 128).
 template <int KMAX> struct TokenKeys {
@@ -129,20 +133,20 @@ __device__ __forceinline__ TokenKeys<KMAX> load_keys(int t, int T, int k, int L,
 
 // count: the wave's number of tokens per device and per slot -> cnt[key][blk]
 template <int KMAX>
-__global__ __launch_bounds__(kTB) void brim_count_kernel(int T, int k, int D, int E, int L,
-                                                         int nblk, const int32_t *idx,
-                                                         const float *w, Placement pl, Prune pr,
-                                                         int32_t *cnt) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(kTB * kWB) void brim_count_kernel(int T, int k, int D, int E, int L,
+                                                               int nblk, const int32_t *idx,
+                                                               const float *w, Placement pl,
+                                                               Prune pr, int32_t *cnt) {
+  const int lane = threadIdx.x % kTB, wv = threadIdx.x / kTB;
   const int t = blockIdx.x * kTB + lane;
   // the weights matter for counting only when pruning decides by them
   const TokenKeys<KMAX> tk =
       load_keys<KMAX>(t, T, k, L, idx, pr.budget < OCC_MAX_D ? w : nullptr, pl, pr);
-  for (int dv = 0; dv < D; ++dv) {
+  for (int dv = wv; dv < D; dv += kWB) {
     const uint64_t b = __ballot((tk.dmask >> dv) & 1u);
     if (lane == 0) cnt[(size_t)dv * nblk + blockIdx.x] = __popcll(b);
   }
-  for (int g = 0; g < E; ++g) {
+  for (int g = wv; g < E; g += kWB) {
     const uint64_t b = __ballot(slot_bit(tk, g));
     if (lane == 0) cnt[(size_t)(D + g) * nblk + blockIdx.x] = __popcll(b);
   }
@@ -196,31 +200,35 @@ __device__ __forceinline__ int32_t wave_exclusive(const int32_t *tot, int n, int
 // fill: rank of each token among the wave's earlier lanes with the same key,
 // plus the key's prefix and the block's prefix inside the key
 template <int KMAX>
-__global__ __launch_bounds__(kTB) void brim_fill_kernel(
+__global__ __launch_bounds__(kTB * kWB) void brim_fill_kernel(
     int T, int k, int D, int E, int L, int nblk, int ld, const int32_t *idx, const float *w,
     Placement pl, Prune pr, const int32_t *within, const int32_t *tot, int32_t *brim0,
     int32_t *brim1,
     int32_t *sfd_token, int32_t *epd_token, int32_t *epd_sfd, float *epd_w, int32_t *sfd_offset,
     int32_t *slot_offset, int32_t *S_out) {
   __shared__ int32_t base[OCC_MAX_D + OCC_MAX_E];
-  const int lane = threadIdx.x;
-  // key prefixes: devices and slots are two separate exclusive scans
-  const int32_t S = wave_exclusive(tot, D, base);
-  const int32_t R = wave_exclusive(tot + D, E, base + D);
+  const int lane = threadIdx.x % kTB, wv = threadIdx.x / kTB;
+  // key prefixes (wave 0): devices and slots are two separate exclusive scans
+  int32_t S = 0, R = 0;
+  if (wv == 0) {
+    S = wave_exclusive(tot, D, base);
+    R = wave_exclusive(tot + D, E, base + D);
+  }
   __syncthreads();
-  if (blockIdx.x == 0) {
+  if (wv == 0 && blockIdx.x == 0) {
     for (int c = lane; c <= D; c += kTB) sfd_offset[c] = c == D ? S : base[c];
     for (int c = lane; c <= E; c += kTB) slot_offset[c] = c == E ? R : base[D + c];
     if (lane == 0) S_out[0] = S;
   }
-  if (nblk == 0) return;  // no tokens: only the offsets above
-  for (int c = lane; c < D + E; c += kTB) base[c] += within[(size_t)c * nblk + blockIdx.x];
+  if (nblk == 0) return;  // no tokens: only the offsets above (uniform over the block)
+  if (wv == 0)
+    for (int c = lane; c < D + E; c += kTB) base[c] += within[(size_t)c * nblk + blockIdx.x];
   __syncthreads();
   const int t = blockIdx.x * kTB + lane;
   const bool live = t < T;
   const TokenKeys<KMAX> tk = load_keys<KMAX>(t, T, k, L, idx, w, pl, pr);
   const uint64_t lt = lanemask_lt();
-  for (int dv = 0; dv < D; ++dv) {
+  for (int dv = wv; dv < D; dv += kWB) {
     const bool hasd = live && ((tk.dmask >> dv) & 1u);
     const uint64_t bd = __ballot(hasd);
     const int32_t s = hasd ? base[dv] + __popcll(bd & lt) : -1;
@@ -260,13 +268,13 @@ void launch_kmax(int T, int k, int D, int E, int L, int nblk, int ld, const int3
                  const float *w, const Placement &pl, const Prune &pr, const occ_brim &b,
                  int32_t *cnt, int32_t *tot, hipStream_t st) {
   if (nblk > 0) {
-    brim_count_kernel<KMAX><<<nblk, kTB, 0, st>>>(T, k, D, E, L, nblk, idx, w, pl, pr, cnt);
+    brim_count_kernel<KMAX><<<nblk, kTB * kWB, 0, st>>>(T, k, D, E, L, nblk, idx, w, pl, pr, cnt);
     brim_keyscan_kernel<<<D + E, kTB, 0, st>>>(nblk, cnt, tot);
   } else {
     // no tokens: every key total is zero
     brim_zero_kernel<<<1, kTB, 0, st>>>(tot, D + E);
   }
-  brim_fill_kernel<KMAX><<<nblk > 0 ? nblk : 1, kTB, 0, st>>>(
+  brim_fill_kernel<KMAX><<<nblk > 0 ? nblk : 1, kTB * kWB, 0, st>>>(
       T, k, D, E, L, nblk, ld, idx, w, pl, pr, cnt, tot, b.brim0, b.brim1, b.sfd_token, b.epd_token,
       b.epd_sfd, b.epd_w, b.sfd_offset, b.slot_offset, b.S);
 }
