@@ -17,7 +17,9 @@
 // waves share one staged d-chunk of X (as fp32) and of the router (fp32, each
 // row read by one lane as 16-byte vectors; the row stride of JC + 4 floats
 // puts the 16 rows of a quarter-wave in distinct banks); X values are
-// segment-wide LDS broadcasts.  Chunks of JC = 32..128 columns go through a
+// segment-wide LDS broadcasts, or, when a whole wave serves one token with
+// one or two tokens per lane, one LDS value per lane handed to the FMAs by
+// DPP row broadcasts (chunk_bcast).  Chunks of JC = 32..128 columns go through a
 // two-deep register pipeline (chunk c + 2 loads while chunk c is multiplied
 // from LDS and chunk c + 1 waits in registers), one barrier per chunk.
 // Softmax and top-k then run inside each segment with xor shuffles.
@@ -25,7 +27,6 @@
 
 namespace occ {
 namespace {
-
 
 // acc = fma(x of lane J of this lane's 16-lane row, w, acc): the FMA takes
 // its first operand through DPP row_newbcast (CDNA3/4), which hands every
