@@ -14,7 +14,11 @@ SwiGLU epilogue): achieved = algorithmic flops per launch / its mean launch
 time, from HIP events recorded around it in every timed step on the stream
 it runs on.  The per-stage times come from a second pass of the same steps
 with an event between every two stages.  cpu_baseline times the CPU
-oracle (single thread) on a bounded sample of the same workload.
+oracle (single thread) on a bounded sample of the same workload.  After the
+headline steps the line also carries the widened rows (conventional, pruned,
+affinity, backward) and a calibration: the vendor library's dense bf16
+matmul with the gate/up GEMM's flop on the same box (context for the
+roofline fraction; not part of any measured step).
 """
 from __future__ import annotations
 
@@ -285,6 +289,29 @@ def backward(lay, cfg, steps, torch):
             "grad_dispatch_hbm_frac": gd_bytes / t["grad_dispatch"] / 1e9 / PEAK_HBM_GBS}
 
 
+def dense_library_rate(cfg, torch):
+    """Context for the grouped GEMM's fraction: torch's bf16 matmul (the vendor
+    library) on one dense GEMM with the gate/up GEMM's flop (T*k x d @ d x 2I),
+    timed on the same box, outside the measured steps."""
+    M, K, N = cfg.R, cfg.d, 2 * cfg.I
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(K, N, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(10):
+        c = a @ b
+    ev[1].record()
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) / 10 * 1e-3
+    del a, b, c
+    tf = 2.0 * M * K * N / t / 1e12
+    return {"dense_matmul": f"{M}x{K}x{N} bf16, torch.matmul", "us": t * 1e6, "tflops": tf,
+            "frac": tf / PEAK_BF16_TFLOPS}
+
+
 def cpu_baseline(inp, n_tok):
     """The oracle as it stands, one thread: routing and BRIMs on the full
     batch, expert FFN and combine on a seeded sample of tokens; tokens/s
@@ -470,6 +497,8 @@ def main():
     out["affinity"] = affinity(cfg, lay, torch)
     if cfg.dtype == "bf16" and cfg.n_shared == 0:
         out["backward"] = backward(lay, cfg, args.steps, torch)
+    if cfg.dtype == "bf16":
+        out["calibration"] = dense_library_rate(cfg, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)
