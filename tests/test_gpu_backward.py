@@ -27,6 +27,9 @@ SMALL = {
                                      dtype="bf16", clusters=8),
     "bf16_one_expert_per_device": W.LayerConfig("bf16_one_expert_per_device", T=150, d=128,
                                                 E=8, I=64, k=2, D=8, dtype="bf16"),
+    # the largest device count and picks per token the library takes
+    "bf16_max_devices_and_k": W.LayerConfig("bf16_max_devices_and_k", T=200, d=64, E=64, I=64,
+                                            k=16, D=32, dtype="bf16", clusters=4),
 }
 
 
