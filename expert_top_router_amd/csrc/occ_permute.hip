@@ -138,6 +138,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 #pragma unroll
       for (int u = 0; u < VE; ++u) yacc[c][u] = 0.0f;
     }
+    // an fp32 term (the backward's dx_router), first in the sum; loaded here
+    // so that its latency overlaps the EPD row loads
+    if (add32 != nullptr && i < row16) {
+      const float *ap = add32 + ((size_t)t * row16 + i) * VE;
+#pragma unroll
+      for (int u = 0; u < VE; ++u) yacc[c][u] += ap[u];
+    }
 #pragma unroll
     for (int u = 0; u < VE; ++u) acc[c][u] = 0.0f;
   }
@@ -206,11 +213,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int i = lane + kWave * c;
-    if (add32 != nullptr && i < row16) {  // an fp32 term added before the final rounding
-      const float *ap = add32 + ((size_t)t * row16 + i) * VE;
-#pragma unroll
-      for (int u = 0; u < VE; ++u) yacc[c][u] += ap[u];
-    }
     if (i < row16) y[(size_t)t * row16 + i] = CK::pack(yacc[c]);
   }
 }
@@ -294,7 +296,7 @@ hipError_t launch_combine(const occ_layer_desc &Ld, const void *out_epd, const o
 }
 
 // Gradient of the dispatch (the same walk, unit weights): d_sfd[s] = sum over
-// l of d_epd[r], dx[t] = sum over devices of d_sfd[s] + add32[t] (fp32).
+// l of d_epd[r], dx[t] = add32[t] (fp32) + sum over devices of d_sfd[s].
 hipError_t launch_grad_dispatch(const occ_layer_desc &Ld, const void *d_epd, const occ_brim &b,
                                 const float *add32, void *d_sfd, void *dx, hipStream_t st) {
   if (Ld.T == 0) return hipSuccess;
