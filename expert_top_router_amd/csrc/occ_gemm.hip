@@ -11,8 +11,9 @@
 // no host synchronisation is needed.
 //
 // bf16: persistent blocks, one per CU, each walking a contiguous range of
-// tiles of its XCD.  A block is 2 x 2 waves with a 256 x 256 x 64 tile, wave
-// tile 128 x 128 of v_mfma_f32_32x32x16_bf16, fp32 accumulators.  Global
+// tiles of its XCD.  A block works on a 256 x 256 x 64 tile with 2 x 2 waves
+// (wave tile 128 x 128, SwiGLU GEMM) or 2 x 4 waves (128 x 64, two waves per
+// SIMD, down GEMM) of v_mfma_f32_32x32x16_bf16, fp32 accumulators.  Global
 // tiles go through registers (raw buffer loads, one k-tile ahead) into
 // double-buffered, padded LDS (row stride 72 elements = 144 bytes, so the 16
 // rows read by one MFMA operand load fall in distinct banks); one barrier per
@@ -362,7 +363,11 @@ hipError_t run_gemm(const GemmArgs &a, int dtype, int max_rows, hipStream_t st) 
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipGetLastError();
-  launch_bf16<256, 256, 1, SWIGLU, 2>(a, max_rows, n_cu, st);
+  // Full-width tiles (down) run 8 waves (2 x 4, two per SIMD, 128 x 64 wave
+  // tiles); SwiGLU tiles run 4 (2 x 2, 128 x 128 wave tiles): each measured
+  // faster for its GEMM on the OLMoE-shaped layer.
+  if (SWIGLU) launch_bf16<256, 256, 1, true, 2>(a, max_rows, n_cu, st);
+  else launch_bf16<256, 256, 1, false, 4>(a, max_rows, n_cu, st);
   return hipGetLastError();
 }
 
