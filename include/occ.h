@@ -269,9 +269,11 @@ occ_status occ_expert_backward(const occ_layer_desc *desc, const void *epd, cons
  *   dx_router     = dlogits W_r                            (fp32 [T][d])
  *   dw_router     = dlogits^T x                            (fp32 [E][d])
  * Both products accumulate in fp32; dw_router sums its token chunks in a
- * fixed order (deterministic).  With a BRIM from occ_build_brim_pruned,
- * dw_epd is the gradient of the stored (rescaled) weights, dropped picks get
- * no gradient and the rescaling factor is held constant.  bwd_ws: device workspace of at least
+ * fixed order (deterministic).  The gradient is exact for a BRIM from
+ * occ_build_brim.  With one from occ_build_brim_pruned it takes dw_epd (the
+ * gradient of each stored, possibly rescaled, weight) as the gradient of
+ * that pick's routing weight and gives dropped picks none: an approximation
+ * that ignores the pruning and the rescaling factor.  bwd_ws: device workspace of at least
  * occ_backward_workspace_bytes(desc) bytes for the partial sums (ENOSPC when
  * smaller; its contents are not kept). */
 occ_status occ_router_backward(const occ_layer_desc *desc, const void *x, const float *w_router,
