@@ -191,15 +191,23 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
         cur_dev = dv;
         cur_s = __builtin_amdgcn_readlane(s, b);
       }
+      // the row's loads go out before the weight is read from its lane, so
+      // they do not wait for the weight's load (one dependent latency fewer)
       const int32_t row = __builtin_amdgcn_readlane(r, b);
-      const float wb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(wr), b));
       const u32x4 *srcp = out_epd + (size_t)row * row16;
+      u32x4 v[NCH];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int i = lane + kWave * c;
+        if (i < row16) v[c] = srcp[i];
+      }
+      const float wb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(wr), b));
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int i = lane + kWave * c;
         if (i < row16) {
           float f[VE];
-          CK::unpack(srcp[i], f);
+          CK::unpack(v[c], f);
 #pragma unroll
           for (int u = 0; u < VE; ++u) {
             if (PRE) acc[c][u] = __builtin_fmaf(wb, f[u], acc[c][u]);
