@@ -86,7 +86,15 @@ __global__ __launch_bounds__(kThreads) void grad_combine_kernel(
     while (mr) {
       const int b = __ffsll((long long)mr) - 1;
       mr &= mr - 1;
+      // the row's loads go out before the weight is read from its lane, so
+      // they do not wait for the weight's load
       const int32_t row = __builtin_amdgcn_readlane(r, b);
+      u32x4 ov[NCH];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int i = lane + kWave * c;
+        if (i < row16) ov[c] = out_epd[(size_t)row * row16 + i];
+      }
       const float wb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(wr), b));
       float dot = 0.0f;
 #pragma unroll
@@ -94,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void grad_combine_kernel(
         const int i = lane + kWave * c;
         if (i < row16) {
           float o[8], d[8];
-          unpack_bf16(out_epd[(size_t)row * row16 + i], o);
+          unpack_bf16(ov[c], o);
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             dot = __builtin_fmaf(g[c][u], o[u], dot);
