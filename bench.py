@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
+PEAK_F32_VALU_TFLOPS = 78.6  # fp32 FMA without packed math (256 CU x 64 lanes x 2 x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE-layer tokens/sec (route+dispatch+FFN+combine); % HBM and % MFMA peak"
 DEFAULT_WORKLOAD = "olmoe_bf16"
@@ -284,7 +285,7 @@ def backward(lay, cfg, steps, torch):
             "expert_backward_mfma_frac": ebw_flop / t["expert_backward"] / 1e12
                                          / PEAK_BF16_TFLOPS,
             "router_backward_us": t["router_backward"] * 1e6,
-            "router_backward_valu_frac": rb_flop / t["router_backward"] / 1e12 / 78.6,
+            "router_backward_valu_frac": rb_flop / t["router_backward"] / 1e12 / PEAK_F32_VALU_TFLOPS,
             "grad_dispatch_us": t["grad_dispatch"] * 1e6,
             "grad_dispatch_hbm_frac": gd_bytes / t["grad_dispatch"] / 1e9 / PEAK_HBM_GBS}
 
@@ -455,7 +456,7 @@ def main():
     up_tf = alg["up_flop"] / up_s / 1e12
     stages = {
         "route_us": t["route"] * 1e6,
-        "route_valu_frac": alg["route_flop"] / t["route"] / 1e12 / 78.6,
+        "route_valu_frac": alg["route_flop"] / t["route"] / 1e12 / PEAK_F32_VALU_TFLOPS,
         "build_brim_us": t["build_brim"] * 1e6,
         "dispatch_us": t["dispatch"] * 1e6,
         "dispatch_hbm_frac": alg["dispatch_bytes"] / t["dispatch"] / 1e9 / PEAK_HBM_GBS,
