@@ -285,7 +285,8 @@ def backward(lay, cfg, steps, torch):
             "expert_backward_mfma_frac": ebw_flop / t["expert_backward"] / 1e12
                                          / PEAK_BF16_TFLOPS,
             "router_backward_us": t["router_backward"] * 1e6,
-            "router_backward_valu_frac": rb_flop / t["router_backward"] / 1e12 / PEAK_F32_VALU_TFLOPS,
+            "router_backward_valu_frac": rb_flop / t["router_backward"] / 1e12
+                                         / PEAK_F32_VALU_TFLOPS,
             "grad_dispatch_us": t["grad_dispatch"] * 1e6,
             "grad_dispatch_hbm_frac": gd_bytes / t["grad_dispatch"] / 1e9 / PEAK_HBM_GBS}
 

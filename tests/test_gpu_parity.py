@@ -4,8 +4,9 @@ Small layers are compared element by element at every stage (routing, BRIMs,
 dispatch, expert outputs, pre-reduction, combine, co-activation); they span
 several GEMM tiles with ragged tails, both dtypes, shared experts, more than
 64 (device, expert) pairs, non-power-of-two expert counts, D = 1, L = 1, the
-largest device count and picks per token (D = 32, k = 16) and an empty batch.  The five full-size layers are compared on the full batch for
-all integer work and on sampled tokens for the expert arithmetic.
+largest device count and picks per token (D = 32, k = 16) and an empty batch.
+The five full-size layers are compared on the full batch for all integer work
+and on sampled tokens for the expert arithmetic.
 """
 import numpy as np
 import pytest
