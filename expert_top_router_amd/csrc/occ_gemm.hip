@@ -11,13 +11,15 @@
 // no host synchronisation is needed.
 //
 // bf16: persistent blocks, one per CU, each walking a contiguous range of
-// tiles of its XCD.  A block works on a 256 x 256 x 64 tile with 2 x 2 waves
-// (wave tile 128 x 128, SwiGLU GEMM) or 2 x 4 waves (128 x 64, two waves per
-// SIMD, down GEMM) of v_mfma_f32_32x32x16_bf16, fp32 accumulators.  Global
-// tiles go through registers (raw buffer loads, one k-tile ahead) into
-// double-buffered, padded LDS (row stride 72 elements = 144 bytes, so the 16
-// rows read by one MFMA operand load fall in distinct banks); one barrier per
-// k-tile.  The epilogue applies SwiGLU, rounds to bf16 in hardware and
+// tiles of its XCD.  A block works on a 256 x 256 x 64 tile with 2 x 4 waves
+// (wave tile 128 x 64, two waves per SIMD) of v_mfma_f32_32x32x16_bf16, fp32
+// accumulators.  Global tiles go through registers (raw buffer loads, one
+// k-tile ahead) into double-buffered, padded LDS (row stride 72 elements =
+// 144 bytes, so the 16 rows read by one MFMA operand load fall in distinct
+// banks); one barrier per k-tile, placed before the last k step so that the
+// next k-tile's first fragments load under that step's MFMAs.  The next
+// tile's first k-tile is loaded during the epilogue.  The epilogue applies
+// SwiGLU, rounds to bf16 in hardware and
 // stores the rows (straight from registers for SwiGLU tiles, through an LDS
 // staging area for full-width tiles).
 #include "occ_gemm_common.h"
@@ -25,7 +27,7 @@
 namespace occ {
 namespace {
 
-// bf16 grouped GEMM.  4 waves in 2 x 2, wave tile (BM/2) x (BN/2) made of
+// bf16 grouped GEMM.  2 x NWN waves, wave tile (BM/2) x (BN/NWN) made of
 // 32x32 output blocks of v_mfma_f32_32x32x16_bf16.  Operand layout of that
 // instruction: lane l supplies row (or column) l % 32 and the eight k values
 // 8*(l/32) .. 8*(l/32)+7 of a 16-deep k step; output element i of lane l is
@@ -102,24 +104,17 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i) rb[set_][i] = __builtin_bit_cast( \
         u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[i], (int)bk_ * 2, 0)); \
   } while (0)
-  // Full-width tiles (down GEMM) load the next tile's first k-tile into
-  // registers right after the k loop, so its latency hides behind the
-  // epilogue, where those registers are free (down GEMM about 3% faster on
-  // the OLMoE-shaped layer).  SwiGLU tiles load it at the top of the tile:
-  // their epilogue needs the registers (the prefetch spilled and was slower).
+  // The next tile's first k-tile is loaded into registers right after the k
+  // loop, so its latency hides behind the epilogue, where those registers
+  // are free.
   int logical = x0 + (int)(blockIdx.x / kXcds);
   TileCoord tc{};
-  if (!SWIGLU && logical < x1) {
+  if (logical < x1) {
     tc = tile_coord<BM, BNO>(a, ts, ro, logical);
     set_offsets(tc);
     OCC_LOAD_REGS(0, 0);
   }
   for (; logical < x1; logical += nbx) {
-  if (SWIGLU) {
-    tc = tile_coord<BM, BNO>(a, ts, ro, logical);
-    set_offsets(tc);
-    OCC_LOAD_REGS(0, 0);
-  }
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -171,15 +166,23 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
 
   // nk % PF == 0 (the launcher picks PF so); loads past the last tile re-read
   // the last tile (in bounds, L2-resident), which keeps the loop branch-free.
-  // Step kt multiplies tile kt from one LDS buffer while, k step by k step,
-  // it stores tile kt+1 (register set (u+1) % PF) into the other buffer and
-  // refills those registers with tile kt+1+PF; one barrier per step.
-  constexpr int A_PER = (A_CH + KSTEPS - 1) / KSTEPS;  // chunks per k step
-  constexpr int B_PER = (B_CH + KSTEPS - 1) / KSTEPS;
+  // Step kt multiplies tile kt from one LDS buffer while, during k steps
+  // 0..KSTEPS-2, it stores tile kt+1 (register set (u+1) % PF) into the other
+  // buffer and refills those registers with tile kt+1+PF (A and B chunks as
+  // one sequence, spread evenly).  The step's one barrier follows those
+  // stores, and the last k step's MFMAs then cover the LDS latency of tile
+  // kt+1's first fragments.
+  constexpr int WSTEPS = KSTEPS - 1;
+  constexpr int C_PER = (A_CH + B_CH + WSTEPS - 1) / WSTEPS;  // chunks per k step
   const int nk = a.K / kBK;
   OCC_STORE_LDS(0, 0);  // k-tile 0
   __syncthreads();
   OCC_LOAD_REGS(min(PF, nk - 1), 0);
+  bf16x8v af[2][MI], bfr[2][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) af[0][mi] = *reinterpret_cast<const bf16x8v *>(smem + a_frag[mi]);
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) bfr[0][ni] = *reinterpret_cast<const bf16x8v *>(smem + b_frag[ni]);
   __builtin_amdgcn_sched_barrier(0);
   for (int kb = 0; kb < nk; kb += PF) {
 #pragma unroll
@@ -191,55 +194,47 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
       const int k0n = kn * kBK;
       const int ksn = k0n / a.kseg;
       const int64_t bkn = (int64_t)ksn * a.kseg_stride + (k0n - ksn * a.kseg);
-      bf16x8v af[2][MI], bfr[2][NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        af[0][mi] = *reinterpret_cast<const bf16x8v *>(S + a_frag[mi]);
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        bfr[0][ni] = *reinterpret_cast<const bf16x8v *>(S + b_frag[ni]);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int q = ks & 1;
-        if (ks + 1 < KSTEPS) {  // fragments of the next k step while these multiply
+        // fragments of the next k step (of the next tile in the last step:
+        // after the barrier, from the other buffer) while these multiply
+        const uint16_t *Fs = ks + 1 < KSTEPS ? S + (ks + 1) * 16 : Wn;
 #pragma unroll
-          for (int mi = 0; mi < MI; ++mi)
-            af[q ^ 1][mi] = *reinterpret_cast<const bf16x8v *>(S + a_frag[mi] + (ks + 1) * 16);
+        for (int mi = 0; mi < MI; ++mi)
+          af[q ^ 1][mi] = *reinterpret_cast<const bf16x8v *>(Fs + a_frag[mi]);
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            bfr[q ^ 1][ni] = *reinterpret_cast<const bf16x8v *>(S + b_frag[ni] + (ks + 1) * 16);
-        }
+        for (int ni = 0; ni < NI; ++ni)
+          bfr[q ^ 1][ni] = *reinterpret_cast<const bf16x8v *>(Fs + b_frag[ni]);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[q][ni], af[q][mi],
                                                                  acc[mi][ni], 0, 0, 0);
+        if (ks < WSTEPS) {
 #pragma unroll
-        for (int j = 0; j < A_PER; ++j) {
-          const int i = ks * A_PER + j;
-          if (i < A_CH) {
-            *reinterpret_cast<u32x4 *>(Wn + a_dst[i]) = ra[(u + 1) % PF][i];
-            ra[(u + 1) % PF][i] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[i], k0n * 2, 0));
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < B_PER; ++j) {
-          const int i = ks * B_PER + j;
-          if (i < B_CH) {
-            *reinterpret_cast<u32x4 *>(Wn + b_dst[i]) = rb[(u + 1) % PF][i];
-            rb[(u + 1) % PF][i] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[i], (int)bkn * 2, 0));
+          for (int j = 0; j < C_PER; ++j) {
+            const int c = ks * C_PER + j;
+            if (c < A_CH) {
+              *reinterpret_cast<u32x4 *>(Wn + a_dst[c]) = ra[(u + 1) % PF][c];
+              ra[(u + 1) % PF][c] = __builtin_bit_cast(
+                  u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[c], k0n * 2, 0));
+            } else if (c < A_CH + B_CH) {
+              const int i = c - A_CH;
+              *reinterpret_cast<u32x4 *>(Wn + b_dst[i]) = rb[(u + 1) % PF][i];
+              rb[(u + 1) % PF][i] = __builtin_bit_cast(
+                  u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[i], (int)bkn * 2, 0));
+            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (ks == WSTEPS - 1) __syncthreads();
       }
-      __syncthreads();
     }
   }
   const TileCoord cur = tc;
-  if (!SWIGLU && logical + nbx < x1) {  // the next tile's first k-tile, during this epilogue
+  if (logical + nbx < x1) {  // the next tile's first k-tile, during this epilogue
     tc = tile_coord<BM, BNO>(a, ts, ro, logical + nbx);
     set_offsets(tc);
     OCC_LOAD_REGS(0, 0);
@@ -297,8 +292,9 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
     }
     __syncthreads();  // the staging area is the next tile's first LDS stage
   }
-  // (SwiGLU tiles: the k loop ended with a barrier, so the next tile's first
-  // LDS stores cannot overwrite a stage another wave still reads)
+  // (SwiGLU tiles: every read of real data in the last k-tile came before
+  // its barrier, and the last k step's reads of the other buffer are dead,
+  // so the next tile's first LDS stores overwrite nothing still needed)
   }
 #undef OCC_LOAD_REGS
 #undef OCC_STORE_LDS
@@ -363,10 +359,12 @@ hipError_t run_gemm(const GemmArgs &a, int dtype, int max_rows, hipStream_t st) 
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipGetLastError();
-  // Full-width tiles (down) run 8 waves (2 x 4, two per SIMD, 128 x 64 wave
-  // tiles); SwiGLU tiles run 4 (2 x 2, 128 x 128 wave tiles): each measured
-  // faster for its GEMM on the OLMoE-shaped layer.
-  if (SWIGLU) launch_bf16<256, 256, 1, true, 2>(a, max_rows, n_cu, st);
+  // 8 waves (2 x 4, two per SIMD, 128 x 64 wave tiles): against 4 waves of
+  // 128 x 128 the LDS serves about 1.7 times the fragment bandwidth, which
+  // bounds the k loop (same-process A/B on the OLMoE-shaped layer: gate/up
+  // 325 -> 297 us with the barrier before the last k step; 4 waves with the
+  // barrier at the end of the k-tile measured faster than 8).
+  if (SWIGLU) launch_bf16<256, 256, 1, true, 4>(a, max_rows, n_cu, st);
   else launch_bf16<256, 256, 1, false, 4>(a, max_rows, n_cu, st);
   return hipGetLastError();
 }
