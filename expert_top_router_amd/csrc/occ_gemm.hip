@@ -19,9 +19,8 @@
 // banks); one barrier per k-tile, placed before the last k step so that the
 // next k-tile's first fragments load under that step's MFMAs.  The next
 // tile's first k-tile is loaded during the epilogue.  The epilogue applies
-// SwiGLU, rounds to bf16 in hardware and
-// stores the rows (straight from registers for SwiGLU tiles, through an LDS
-// staging area for full-width tiles).
+// SwiGLU, rounds to bf16 in hardware and stages the tile in LDS, which is
+// written out as 16-byte row segments.
 #include "occ_gemm_common.h"
 
 namespace occ {
@@ -43,8 +42,8 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
   static_assert(A_CH * NT == BM * (kBK / 8) && B_CH * NT == BN * (kBK / 8), "whole chunks");
   constexpr int STAGE = (BM + BN) * kLdsK;          // elements per LDS stage
   constexpr int KSTEPS = kBK / 16;
-  constexpr int CLD = BNO + 8;  // staged output row stride (full-width tiles)
-  static_assert(SWIGLU || BM * CLD <= 2 * STAGE, "output staging must fit in the tile buffers");
+  constexpr int CLD = BNO + 8;  // staged output row stride
+  static_assert(BM * CLD <= 2 * STAGE, "output staging must fit in the tile buffers");
   static_assert(!SWIGLU || NI % 2 == 0, "gate and up halves");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
   __shared__ int32_t ts[OCC_MAX_E + 1];
@@ -245,13 +244,9 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
   // block holds (output column, token) pairs: lane l has token row l % 32 and
   // the output columns 8q + 4(l / 32) + j (j < 4) in registers 4q + j, i.e.
   // four runs of 4 adjacent columns.  Each run is rounded to bf16 in hardware
-  // (round to nearest even).  SwiGLU tiles (128 output columns) store each
-  // run with one 8-byte store: lanes l and l + 32 write adjacent runs and the
-  // four q of a block complete 64 bytes of a row, which the write-back L2
-  // merges into whole lines; staging these tiles in LDS measured slower (two
-  // more barriers and an LDS round trip).  Full-width tiles (256 columns) are
-  // staged in LDS with 8-byte stores and written as 16-byte row segments,
-  // which measured faster for them.
+  // (round to nearest even), staged in LDS with one 8-byte store and the tile
+  // is written as 16-byte row segments (8-byte stores straight from registers
+  // measured 2% slower for SwiGLU tiles and 16% slower for full-width ones).
   uint16_t *Cg = static_cast<uint16_t *>(a.C) + (int64_t)cur.row_begin * a.ldc + cur.n0;
   uint16_t *Cs = smem;
   const int crow = lane & 31, ccol = (lane >> 5) * 4;
@@ -272,29 +267,22 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
         const f32x2v lo = {v[0], v[1]}, hi = {v[2], v[3]};
         const u32x2 packed = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2v)),
                               __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2v))};
-        if (SWIGLU) {
-          if (row < cur.rows && cur.n0 + col + 8 * q < a.N)
-            *reinterpret_cast<u32x2 *>(Cg + (int64_t)row * a.ldc + col + 8 * q) = packed;
-        } else {
-          *reinterpret_cast<u32x2 *>(Cs + row * CLD + col + 8 * q) = packed;
-        }
+        *reinterpret_cast<u32x2 *>(Cs + row * CLD + col + 8 * q) = packed;
       }
     }
   }
-  if (!SWIGLU) {
-    __syncthreads();
-    constexpr int RCH = BNO / 8;  // 16-byte chunks per output row
-    for (int c = tid; c < BM * RCH; c += NT) {
-      const int r = c / RCH, cc = c - r * RCH;
-      if (r < cur.rows && cur.n0 + cc * 8 < a.N)
-        *reinterpret_cast<u32x4 *>(Cg + (int64_t)r * a.ldc + cc * 8) =
-            *reinterpret_cast<const u32x4 *>(Cs + r * CLD + cc * 8);
-    }
-    __syncthreads();  // the staging area is the next tile's first LDS stage
+  // (every read of real data in the last k-tile came before its barrier, and
+  // the last k step's reads of the other buffer are dead, so the staging
+  // stores overwrite nothing still needed)
+  __syncthreads();
+  constexpr int RCH = BNO / 8;  // 16-byte chunks per output row
+  for (int c = tid; c < BM * RCH; c += NT) {
+    const int r = c / RCH, cc = c - r * RCH;
+    if (r < cur.rows && cur.n0 + cc * 8 < a.N)
+      *reinterpret_cast<u32x4 *>(Cg + (int64_t)r * a.ldc + cc * 8) =
+          *reinterpret_cast<const u32x4 *>(Cs + r * CLD + cc * 8);
   }
-  // (SwiGLU tiles: every read of real data in the last k-tile came before
-  // its barrier, and the last k step's reads of the other buffer are dead,
-  // so the next tile's first LDS stores overwrite nothing still needed)
+  __syncthreads();  // the staging area is the next tile's first LDS stage
   }
 #undef OCC_LOAD_REGS
 #undef OCC_STORE_LDS
