@@ -19,7 +19,8 @@
 // puts the 16 rows of a quarter-wave in distinct banks); X values are
 // segment-wide LDS broadcasts, or, when a whole wave serves one token with
 // one or two tokens per lane, one LDS value per lane handed to the FMAs by
-// DPP row broadcasts (chunk_bcast).  Chunks of JC = 32..128 columns go through a
+// DPP row broadcasts (chunk_bcast, software-pipelined over 16-column groups).
+// Chunks of JC = 32..128 columns go through a
 // two-deep register pipeline (chunk c + 2 loads while chunk c is multiplied
 // from LDS and chunk c + 1 waits in registers), one barrier per chunk.
 // Softmax and top-k then run inside each segment with xor shuffles.
@@ -136,10 +137,50 @@ __global__ __launch_bounds__(THR) void route_topk_kernel(
   // drop 16-fold against the broadcast 16-byte reads of the general loop,
   // which matters when 1-2 tokens per lane leave the router reads little
   // reuse (OLMoE-shaped layer: 57 -> 48 us); with 8 tokens per lane the
-  // general loop measured slightly faster.  jn is a multiple of 8.
-  constexpr bool BC = ESEG == kWave && TPL <= 2;
+  // general loop measured faster before this loop was software-pipelined.
+  // On whole chunks the reads of the next 16 columns are issued before the
+  // FMAs of these (scheduling barriers keep the compiler from sinking them):
+  // OLMoE-shaped layer 48 -> 43 us; with it, one expert and 8 tokens per lane
+  // (DeepSeek-V2-Lite-shaped layer) also gain (116 -> 111 us), while two
+  // experts per lane (128 experts) stay on the general loop (543 against
+  // 680 us).  jn is a multiple of 8.
+  constexpr bool BC = ESEG == kWave && (TPL <= 2 || EP == 1);
   auto chunk_bcast = [&](const float *wsc, const float *xsc, int jn) {
     const int xl = lane & 15;
+    if (jn == kJC && kJC % 16 == 0) {
+      // whole chunk: the loads of column group g + 16 go out before the FMAs
+      // of group g, so the LDS latency hides behind them (two register sets)
+      float4 wv[2][EP][4];
+      float xv[2][TPL];
+      auto load_group = [&](int g, int set) {
+#pragma unroll
+        for (int i = 0; i < EP; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            wv[set][i][v] =
+                *reinterpret_cast<const float4 *>(&wsc[(el + ESEG * i) * kLds + g + 4 * v]);
+#pragma unroll
+        for (int m = 0; m < TPL; ++m) xv[set][m] = xsc[(wave * TW + q + Q * m) * kLds + g + xl];
+      };
+      load_group(0, 0);
+#pragma unroll
+      for (int g = 0; g < kJC; g += 16) {
+        const int cs = (g / 16) & 1;
+        if (g + 16 < kJC) load_group(g + 16, cs ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+#define OCC_ROUTE_BCP(J, C)                                                           \
+  _Pragma("unroll") for (int m = 0; m < TPL; ++m)                                     \
+  _Pragma("unroll") for (int i = 0; i < EP; ++i)                                      \
+      fmac_row_bcast<J>(acc[m][i], xv[cs][m], wv[cs][i][(J) / 4].C);
+        OCC_ROUTE_BCP(0, x) OCC_ROUTE_BCP(1, y) OCC_ROUTE_BCP(2, z) OCC_ROUTE_BCP(3, w)
+        OCC_ROUTE_BCP(4, x) OCC_ROUTE_BCP(5, y) OCC_ROUTE_BCP(6, z) OCC_ROUTE_BCP(7, w)
+        OCC_ROUTE_BCP(8, x) OCC_ROUTE_BCP(9, y) OCC_ROUTE_BCP(10, z) OCC_ROUTE_BCP(11, w)
+        OCC_ROUTE_BCP(12, x) OCC_ROUTE_BCP(13, y) OCC_ROUTE_BCP(14, z) OCC_ROUTE_BCP(15, w)
+#undef OCC_ROUTE_BCP
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
     for (int g = 0; g < jn; g += 16) {
       float4 wv[EP][4];
 #pragma unroll
