@@ -206,6 +206,64 @@ __global__ __launch_bounds__(THR) void route_topk_kernel(
     }
   };
 
+  // General loop: per 4 columns, one 16-byte router read per expert and one
+  // segment-broadcast 16-byte X read per token.  With few chains per lane
+  // (TPL * EP <= 4) the loop is latency-bound, and on whole chunks the reads
+  // of the next 4 columns go out before the FMAs of these (two register
+  // sets, scheduling barriers keep the order): Mixtral-shaped layer
+  // 73 -> 46 us.  With 16 chains per lane that order measured slower
+  // (544 -> 665 us on the 128-expert layer) and is not used.
+  auto fma4 = [&](const float4 *wv, const float4 *xv) {
+    // j ascending inside every chain; the TPL*EP chains interleave
+#pragma unroll
+    for (int m = 0; m < TPL; ++m)
+#pragma unroll
+      for (int i = 0; i < EP; ++i) acc[m][i] = __builtin_fmaf(xv[m].x, wv[i].x, acc[m][i]);
+#pragma unroll
+    for (int m = 0; m < TPL; ++m)
+#pragma unroll
+      for (int i = 0; i < EP; ++i) acc[m][i] = __builtin_fmaf(xv[m].y, wv[i].y, acc[m][i]);
+#pragma unroll
+    for (int m = 0; m < TPL; ++m)
+#pragma unroll
+      for (int i = 0; i < EP; ++i) acc[m][i] = __builtin_fmaf(xv[m].z, wv[i].z, acc[m][i]);
+#pragma unroll
+    for (int m = 0; m < TPL; ++m)
+#pragma unroll
+      for (int i = 0; i < EP; ++i) acc[m][i] = __builtin_fmaf(xv[m].w, wv[i].w, acc[m][i]);
+  };
+  auto chunk_general = [&](const float *wsc, const float *xsc, int jn) {
+    auto load4 = [&](int jj, float4 *wv, float4 *xv) {
+#pragma unroll
+      for (int i = 0; i < EP; ++i)
+        wv[i] = *reinterpret_cast<const float4 *>(&wsc[(el + ESEG * i) * kLds + jj]);
+#pragma unroll
+      for (int m = 0; m < TPL; ++m)
+        xv[m] = *reinterpret_cast<const float4 *>(&xsc[(wave * TW + q + Q * m) * kLds + jj]);
+    };
+    if (TPL * EP <= 4 && jn == kJC) {
+      float4 wv[2][EP], xv[2][TPL];
+      load4(0, wv[0], xv[0]);
+#pragma unroll
+      for (int jj = 0; jj < kJC; jj += 4) {
+        const int cs = (jj / 4) & 1;
+        if (jj + 4 < kJC) load4(jj + 4, wv[cs ^ 1], xv[cs ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        fma4(wv[cs], xv[cs]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
+#pragma unroll 8
+    for (int jj = 0; jj < kJC; jj += 4) {
+      if (jj < jn) {
+        float4 wv[EP], xv[TPL];
+        load4(jj, wv, xv);
+        fma4(wv, xv);
+      }
+    }
+  };
+
   const int nch = (d + kJC - 1) / kJC;
   // chunk ch is multiplied from LDS buffer ch % 2, chunk ch + 1 waits in
   // register set (ch + 1) % 2, and chunk ch + 2 is loading into set ch % 2
@@ -223,28 +281,7 @@ __global__ __launch_bounds__(THR) void route_topk_kernel(
     if (BC) {                                                                         \
       chunk_bcast(wsc, xsc, jn);                                                      \
     } else {                                                                          \
-    _Pragma("unroll 8") for (int jj = 0; jj < kJC; jj += 4) {                         \
-      if (jj < jn) {                                                                  \
-        float4 wv[EP], xv[TPL];                                                       \
-        _Pragma("unroll") for (int i = 0; i < EP; ++i) wv[i] =                        \
-            *reinterpret_cast<const float4 *>(&wsc[(el + ESEG * i) * kLds + jj]);     \
-        _Pragma("unroll") for (int m = 0; m < TPL; ++m) xv[m] =                       \
-            *reinterpret_cast<const float4 *>(&xsc[(wave * TW + q + Q * m) * kLds + jj]); \
-        /* j ascending inside every chain; the TPL*EP chains interleave */            \
-        _Pragma("unroll") for (int m = 0; m < TPL; ++m)                               \
-        _Pragma("unroll") for (int i = 0; i < EP; ++i)                                \
-            acc[m][i] = __builtin_fmaf(xv[m].x, wv[i].x, acc[m][i]);                  \
-        _Pragma("unroll") for (int m = 0; m < TPL; ++m)                               \
-        _Pragma("unroll") for (int i = 0; i < EP; ++i)                                \
-            acc[m][i] = __builtin_fmaf(xv[m].y, wv[i].y, acc[m][i]);                  \
-        _Pragma("unroll") for (int m = 0; m < TPL; ++m)                               \
-        _Pragma("unroll") for (int i = 0; i < EP; ++i)                                \
-            acc[m][i] = __builtin_fmaf(xv[m].z, wv[i].z, acc[m][i]);                  \
-        _Pragma("unroll") for (int m = 0; m < TPL; ++m)                               \
-        _Pragma("unroll") for (int i = 0; i < EP; ++i)                                \
-            acc[m][i] = __builtin_fmaf(xv[m].w, wv[i].w, acc[m][i]);                  \
-      }                                                                               \
-    }                                                                                 \
+      chunk_general(wsc, xsc, jn);                                                    \
     }                                                                                 \
     if ((ch_) + 1 < nch) OCC_ROUTE_STORE(xn, wn, (cur_) ^ 1);                         \
     if ((ch_) + 3 < nch) OCC_ROUTE_LOAD(xn, wn, ((ch_) + 3) * kJC);                   \
