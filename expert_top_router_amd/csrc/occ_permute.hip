@@ -63,7 +63,9 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int i = lane + kWave * c;
-        if (i < row16) dst[i] = v[c];
+        // the send buffer is not read again by this step: non-temporal
+        // stores keep it out of the caches the expert GEMM reads through
+        if (i < row16) __builtin_nontemporal_store(v[c], dst + i);
       }
     }
     while (mr) {
@@ -160,7 +162,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
         const float v = CK::stored(acc[c][u]);
         acc[c][u] = v;
       }
-      if (i < row16) dst[i] = CK::pack(acc[c]);
+      // the return payload is not read again by this step (non-temporal)
+      if (i < row16) __builtin_nontemporal_store(CK::pack(acc[c]), dst + i);
 #pragma unroll
       for (int u = 0; u < VE; ++u) {
         yacc[c][u] += acc[c][u];
