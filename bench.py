@@ -70,7 +70,7 @@ def algorithmic(cfg, S):
     nsh, Ish = cfg.n_shared, cfg.I_shared
     return {
         "route_flop": 2.0 * T * d * E,
-        "route_bytes": T * d * b + E * d * b + 8.0 * T * k,
+        "route_bytes": T * d * b + E * d * 4.0 + 8.0 * T * k,  # the router is fp32
         "brim_bytes": 8.0 * T * k + 4.0 * D * T + 4.0 * L * S + 4.0 * S + 12.0 * R,
         "dispatch_bytes": (T + S + R) * d * b + 4.0 * D * T + 4.0 * L * S + 4.0 * R,
         "up_flop": 4.0 * R * d * I + 4.0 * T * d * Ish * nsh,
@@ -458,7 +458,9 @@ def main():
     stages = {
         "route_us": t["route"] * 1e6,
         "route_valu_frac": alg["route_flop"] / t["route"] / 1e12 / PEAK_F32_VALU_TFLOPS,
+        "route_hbm_frac": alg["route_bytes"] / t["route"] / 1e9 / PEAK_HBM_GBS,
         "build_brim_us": t["build_brim"] * 1e6,
+        "build_brim_hbm_frac": alg["brim_bytes"] / t["build_brim"] / 1e9 / PEAK_HBM_GBS,
         "dispatch_us": t["dispatch"] * 1e6,
         "dispatch_hbm_frac": alg["dispatch_bytes"] / t["dispatch"] / 1e9 / PEAK_HBM_GBS,
         "expert_up_us": t["expert_up"] * 1e6,
