@@ -49,7 +49,7 @@ def parse():
     p.add_argument("--config", default=DEFAULT_WORKLOAD)
     p.add_argument("--placement", default="contiguous", choices=["contiguous", "greedy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=192)
+    p.add_argument("--cpu-sample-tokens", type=int, default=448)
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many forward steps (for rocprofv3), print nothing else")
     p.add_argument("--profile-backward", action="store_true",
