@@ -20,7 +20,11 @@ the oracle's own rounding) at the points where the layer stores a tensor:
                  dlogit = p (dp - <p, dp>);  dx_router = dlogit W_r,
                  dW_r = dlogit^T X
 Top-k selection is a constant of the backward.  dtype "f64" skips every
-rounding (used by the finite-difference pins).
+rounding (used by the finite-difference pins).  Under collaboration pruning
+the BRIMs hold only the kept picks with their stored (rescaled) weights: the
+expert part is the exact gradient of that layer, and in the routing gradient
+a kept pick carries its stored weight's gradient and a dropped one none
+(the pruning decision and the rescaling factor are held constant).
 """
 from __future__ import annotations
 
@@ -186,12 +190,19 @@ def full(x, wr, wgu, wdn, logits, idx, w, renorm, b, slot_expert, dy, D, dtype):
     slot_of[np.asarray(slot_expert)] = np.arange(E)
 
     def row_of(t, j):
+        # -1 when the pick has no EPD row (dropped by collaboration pruning)
         gsl = slot_of[idx[t, j]]
         s = b["brim0"][gsl // L, t]
-        return b["brim1"][gsl % L, s]
+        return b["brim1"][gsl % L, s] if s >= 0 else -1
+
+    def dw_of(t, j):
+        # a dropped pick's weight gets no gradient; a kept pick's is that of
+        # its stored (possibly rescaled) weight
+        rr = row_of(t, j)
+        return r["dw"][rr] if rr >= 0 else 0.0
 
     tokens = np.arange(T)
-    dl = router_grads(logits, idx, w, renorm, lambda t, j: r["dw"][row_of(t, j)], tokens)
+    dl = router_grads(logits, idx, w, renorm, dw_of, tokens)
     X = _f64(x, dtype)
     dxr = dl @ np.asarray(wr, np.float64)
     dWr = dl.T @ X

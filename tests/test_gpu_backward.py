@@ -199,3 +199,71 @@ def test_empty_batch_backward():
     for name in ("dw_gate_up", "dw_down", "dw_router"):
         g = lay.host(name)
         assert g.size > 0 and np.all(g == 0.0), name
+
+
+@pytest.mark.parametrize("budget,rescale", [(1, 1), (2, 0)])
+def test_pruned_layer_backward_parity(orc, budget, rescale):
+    """The backward under collaboration pruning: the BRIMs hold the kept
+    picks with their stored weights; the expert backward, the dispatch
+    gradient and the routing gradient (no gradient for dropped picks)
+    against the backward oracle on the same BRIMs."""
+    import torch
+    import oracle.backward as ob
+    from expert_top_router_amd.layer import MoELayer, to_device, upload_inputs
+    cfg = SMALL["bf16_ragged"]
+    say(f"case pruned backward budget={budget} rescale={rescale}")
+    inp = W.make_layer(cfg, seed=21)
+    dy = W.from_f64(np.random.default_rng(21).standard_normal((cfg.T, cfg.d)), "bf16")
+    lay = MoELayer(cfg, upload_inputs(inp), inp.slot_expert, with_logits=True, budget=budget,
+                   rescale=rescale)
+    lay.prepare_backward()
+    lay.forward()
+    lay.dy.copy_(to_device(dy))
+    lay.grad_combine()
+    lay.expert_backward()
+    torch.cuda.synchronize()
+    R, I = int(lay.host("slot_offset")[cfg.E]), cfg.I
+    Rmax = cfg.R
+    ws = lay.bwd_ws.view(torch.int16)
+    half = -(-Rmax * 2 * I * 2 // 256) * 256 // 2
+    gu = ws[:Rmax * 2 * I].cpu().numpy().view(np.uint16).reshape(Rmax, 2 * I)[:R]
+    dgu = ws[half:half + Rmax * 2 * I].cpu().numpy().view(np.uint16).reshape(Rmax, 2 * I)[:R]
+    lay.router_backward()
+    lay.grad_dispatch()
+    torch.cuda.synchronize()
+    g = {n: lay.host(n) for n in ("topk_idx", "topk_w", "logits", "epd_token", "dw_epd", "d_epd",
+                                  "dw_gate_up", "dw_down", "dlogits", "dx", "dx_router")}
+    del lay
+    torch.cuda.empty_cache()
+    idx, w = g["topk_idx"], g["topk_w"]
+    ik, wk = orc.prune(idx, w, inp.slot_expert, cfg.E, cfg.D, budget, rescale)
+    assert np.any(ik < 0)
+    b = orc.brim(ik, wk, inp.slot_expert, cfg.E, cfg.D)
+    assert b["R"] == R and np.array_equal(g["epd_token"][:R], b["epd_token"])
+    o = ob.full(_bf(inp.x), _bf(inp.w_router), _bf(inp.w_gate_up), _bf(inp.w_down), g["logits"],
+                idx, w, cfg.renorm, b, inp.slot_expert, _bf(dy), cfg.D, "bf16")
+    assert_close(_bf(gu[:, :I]), o["G"], "bf16", "G (recomputed)")
+    assert_close(_bf(gu[:, I:]), o["U"], "bf16", "U (recomputed)")
+    assert_close(_bf(dgu[:, :I]), o["dG"], "bf16", "dG")
+    assert_close(_bf(dgu[:, I:]), o["dU"], "bf16", "dU")
+    assert_close(_bf(g["d_epd"][:R]), o["d_epd"], "bf16", "d_epd")
+    assert_close(g["dw_gate_up"], o["dW_gate_up"], "bf16", "dW_gate_up")
+    assert_close(g["dw_down"], o["dW_down"], "bf16", "dW_down")
+    assert_close(g["dw_epd"][:R], o["dw"], "bf16", "dw_epd")
+    # routing gradient on the GPU's own dw: dropped picks carry none
+    row_of = _row_of(b, idx, inp.slot_expert, cfg)
+    L = cfg.E // cfg.D
+    slot_of = np.empty(cfg.E, np.int64)
+    slot_of[np.asarray(inp.slot_expert)] = np.arange(cfg.E)
+
+    def dw_of(t, j):
+        gs = slot_of[idx[t, j]]
+        if b["brim0"][gs // L, t] < 0:
+            return 0.0
+        return float(g["dw_epd"][row_of(t, j)])
+    dl = ob.router_grads(g["logits"], idx, w, cfg.renorm, dw_of, np.arange(cfg.T))
+    assert rel_err(g["dlogits"], dl) <= 1e-4, "dlogits"
+    assert rel_err(g["dx_router"], dl @ _bf(inp.w_router)) <= 1e-4, "dx_router"
+    dx, _ = ob.grad_dispatch(b, lambda r: _bf(g["d_epd"][r]), np.arange(cfg.T), cfg.T, cfg.D,
+                             L, cfg.d, "bf16", g["dx_router"])
+    assert_close(_bf(g["dx"]), dx, "bf16", "dx")

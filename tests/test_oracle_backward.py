@@ -116,3 +116,65 @@ def test_rounded_backward_stays_close_to_exact(orc):
         o = g64[name]
         rel = np.abs(g16[name] - o) / np.maximum(np.abs(o), np.sqrt(np.mean(o * o)))
         assert np.median(rel) <= 2e-3 and rel.max() <= 6e-2, (name, np.median(rel), rel.max())
+
+
+def fwd_kept64(x, wgu, wdn, idx, w):
+    """The layer with fixed picks and fixed weights (no router): y[t] = sum
+    over the picks j with idx >= 0 of w[t][j] FFN_{idx[t][j]}(x_t)."""
+    T, k = idx.shape
+    I = wgu.shape[1] // 2
+    y = np.zeros_like(x)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            if e < 0:
+                continue
+            a = wgu[e, :I] @ x[t]
+            u = wgu[e, I:] @ x[t]
+            y[t] += w[t, j] * (wdn[e] @ (a / (1.0 + np.exp(-a)) * u))
+    return y
+
+
+@pytest.mark.parametrize("rescale", [0, 1])
+def test_pruned_expert_gradients_match_finite_differences(orc, rescale):
+    """Collaboration pruning (budget 1 of 2 devices): the BRIMs of the kept
+    picks with their stored weights give the exact weight gradients of the
+    layer those picks and weights define, and dropped picks get no routing
+    weight gradient."""
+    ob = _ob()
+    cfg, inp = _layer(seed=5, k=4, E=8, D=2)
+    x, wr, wgu, wdn = (np.asarray(a, np.float64) for a in (inp.x, inp.w_router, inp.w_gate_up,
+                                                           inp.w_down))
+    lg, idx, w = orc.route(inp.x, inp.w_router, cfg.k, 0, "f32")
+    ik, wk = orc.prune(idx, w, inp.slot_expert, cfg.E, cfg.D, 1, rescale)
+    assert np.any(ik < 0)  # something was dropped
+    b = orc.brim(ik, wk, inp.slot_expert, cfg.E, cfg.D)
+    rng = np.random.default_rng(6)
+    dy = rng.standard_normal(x.shape)
+    g = ob.full(x, wr, wgu, wdn, lg, idx, w, 0, b, inp.slot_expert, dy, cfg.D, "f64")
+    wk64 = wk.astype(np.float64)
+
+    def loss(wgu_, wdn_):
+        return float(np.sum(dy * fwd_kept64(x, wgu_, wdn_, ik, wk64)))
+
+    eps = 1e-6
+    for name, arr, grad in [("w_gate_up", wgu, g["dW_gate_up"]), ("w_down", wdn, g["dW_down"])]:
+        for _ in range(6):
+            t0 = rng.integers(0, cfg.T)
+            j0 = int(np.flatnonzero(ik[t0] >= 0)[0])
+            pos = (int(ik[t0, j0]),) + tuple(rng.integers(0, s) for s in arr.shape[1:])
+            plus, minus = wgu.copy(), wgu.copy()
+            if name == "w_down":
+                plus, minus = wdn.copy(), wdn.copy()
+            plus[pos] += eps
+            minus[pos] -= eps
+            fd = ((loss(plus, wdn) - loss(minus, wdn)) if name == "w_gate_up" else
+                  (loss(wgu, plus) - loss(wgu, minus))) / (2 * eps)
+            assert abs(fd - grad[pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+    # routing: dropped picks carry no weight gradient
+    dw_zero_dropped = lambda t, j: 0.0 if ik[t, j] < 0 else 1.0  # noqa: E731
+    dl = ob.router_grads(lg, idx, w, 0, dw_zero_dropped, np.arange(cfg.T))
+    full_pick = lambda t, j: 1.0  # noqa: E731
+    dl_all = ob.router_grads(lg, idx, w, 0, full_pick, np.arange(cfg.T))
+    dropped_tokens = np.flatnonzero(np.any(ik < 0, axis=1))
+    assert not np.allclose(dl[dropped_tokens], dl_all[dropped_tokens])
