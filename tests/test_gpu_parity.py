@@ -4,7 +4,8 @@ Small layers are compared element by element at every stage (routing, BRIMs,
 dispatch, expert outputs, pre-reduction, combine, co-activation); they span
 several GEMM tiles with ragged tails, both dtypes, shared experts, more than
 64 (device, expert) pairs, non-power-of-two expert counts, D = 1, L = 1, the
-largest device count and picks per token (D = 32, k = 16) and an empty batch.
+largest device count and picks per token (D = 32, k = 16), top-1, top-E and
+an empty batch.
 The five full-size layers are compared on the full batch for all integer work
 and on sampled tokens for the expert arithmetic.
 """
@@ -33,6 +34,13 @@ SMALL = {
     "bf16_wide_rows": W.LayerConfig("bf16_wide_rows", T=130, d=4096, E=4, I=64, k=2, D=2,
                                     dtype="bf16"),
     "f32_empty": W.LayerConfig("f32_empty", T=0, d=64, E=8, I=32, k=2, D=2, dtype="f32"),
+    # one expert per token (each token on one device, S = T)
+    "bf16_top1": W.LayerConfig("bf16_top1", T=257, d=128, E=16, I=64, k=1, D=4, dtype="bf16",
+                               clusters=4),
+    # every token picks every expert (S = T * D, EPD = T * E; renormalised
+    # weights equal the softmax)
+    "bf16_all_experts": W.LayerConfig("bf16_all_experts", T=96, d=64, E=8, I=64, k=8, D=4,
+                                      dtype="bf16", renorm=1),
     # the largest device count and picks per token the library takes
     "bf16_max_devices_and_k": W.LayerConfig("bf16_max_devices_and_k", T=200, d=64, E=64, I=64,
                                             k=16, D=32, dtype="bf16", clusters=4),
