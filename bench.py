@@ -321,6 +321,32 @@ def cpu_baseline(inp, n_tok):
     import oracle
     if not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
         oracle.build()
+    # one thread on one core (the calling thread is pinned to the first core
+    # of its mask for the timing, then released)
+    mask = os.sched_getaffinity(0)
+    core = min(mask)
+    os.sched_setaffinity(0, {core})
+    try:
+        res = _cpu_baseline_timed(inp, n_tok)
+    finally:
+        os.sched_setaffinity(0, mask)
+    res.update({"pinned_core": core, "host_cpus": len(mask), "cpu_model": _cpu_model()})
+    return res
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_baseline_timed(inp, n_tok):
+    import oracle
     cfg = inp.cfg
     T, E, k, D, d = cfg.T, cfg.E, cfg.k, cfg.D, cfg.d
     L = E // D
