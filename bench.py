@@ -277,7 +277,23 @@ def backward(lay, cfg, steps, torch):
     gc_bytes = (T + S + 2 * R) * d * b + 4.0 * R + 4.0 * cfg.D * T + 4.0 * (E // cfg.D) * S
     gd_bytes = (R + S + T) * d * b + 4.0 * T * d + 4.0 * cfg.D * T + 4.0 * (E // cfg.D) * S
     rb_flop = 4.0 * T * E * d
+
+    # the same step with the forward keeping [G | U] for the expert backward
+    def fwd_bwd_kept():
+        lay.forward_keep()
+        lay.backward_kept()
+
+    for _ in range(3):
+        fwd_bwd_kept()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd_bwd_kept()
+    torch.cuda.synchronize()
+    kept = time.perf_counter() - t0
     return {"ms_per_step": elapsed / steps * 1e3, "tokens_per_s": T * steps / elapsed,
+            "kept_gu_ms_per_step": kept / steps * 1e3,
+            "kept_gu_tokens_per_s": T * steps / kept,
             "grad_combine_us": t["grad_combine"] * 1e6,
             "grad_combine_hbm_frac": gc_bytes / t["grad_combine"] / 1e9 / PEAK_HBM_GBS,
             "expert_backward_us": t["expert_backward"] * 1e6,

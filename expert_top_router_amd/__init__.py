@@ -63,6 +63,8 @@ def _load(path: str = LIB_PATH):
         "occ_backward_workspace_bytes": (SZ, [DP]),
         "occ_grad_combine": (I32, [DP, P, BP, P, P, P, P, P]),
         "occ_expert_backward": (I32, [DP, P, BP, P, P, P, P, SZ, P, P, SZ, P, P, P, P]),
+        "occ_expert_ffn_keep": (I32, [DP, P, BP, P, P, P, P, SZ, P, P, P]),
+        "occ_expert_backward_kept": (I32, [DP, P, BP, P, P, P, P, SZ, P, P, P, SZ, P, P, P, P]),
         "occ_router_backward": (I32, [DP, P, P, P, P, P, P, BP, P, P, P, P, P, SZ, P]),
         "occ_grad_dispatch": (I32, [DP, P, BP, P, P, P, P]),
         "occ_cross_coactivation": (I32, [I32, I32, I32, P, I32, I32, P, P, I32, P]),
@@ -86,7 +88,8 @@ EXPORTED = ("occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk", 
             "occ_dispatch", "occ_expert_ffn", "occ_expert_up", "occ_expert_down", "occ_combine",
             "occ_dispatch_direct", "occ_combine_direct", "occ_backward_workspace_bytes",
             "occ_grad_combine", "occ_expert_backward", "occ_router_backward",
-            "occ_grad_dispatch", "occ_coactivation",
+            "occ_grad_dispatch", "occ_expert_ffn_keep", "occ_expert_backward_kept",
+            "occ_coactivation",
             "occ_cross_coactivation", "occ_home_device", "occ_local_hits", "occ_place_greedy",
             "occ_last_error")
 
@@ -251,6 +254,29 @@ def occ_expert_backward(desc, epd, brim: occ_brim, slot_expert_host, w_gate_up, 
            "occ_expert_backward")
 
 
+def occ_expert_ffn_keep(desc, epd, brim: occ_brim, slot_expert_host, w_gate_up, w_down, h_ws,
+                        h_ws_bytes, gu, out_epd, stream=None):
+    import numpy as np
+    se = np.ascontiguousarray(slot_expert_host, dtype=np.int32)
+    _check(_lib.occ_expert_ffn_keep(C.byref(desc), _ptr(epd), C.byref(brim), se.ctypes.data,
+                                    _ptr(w_gate_up), _ptr(w_down), _ptr(h_ws), h_ws_bytes,
+                                    _ptr(gu), _ptr(out_epd), _stream(stream)),
+           "occ_expert_ffn_keep")
+
+
+def occ_expert_backward_kept(desc, epd, brim: occ_brim, slot_expert_host, w_gate_up, w_down,
+                             h_ws, h_ws_bytes, gu, d_out_epd, bwd_ws, bwd_ws_bytes, d_epd,
+                             dw_gate_up, dw_down, stream=None):
+    import numpy as np
+    se = np.ascontiguousarray(slot_expert_host, dtype=np.int32)
+    _check(_lib.occ_expert_backward_kept(C.byref(desc), _ptr(epd), C.byref(brim),
+                                         se.ctypes.data, _ptr(w_gate_up), _ptr(w_down),
+                                         _ptr(h_ws), h_ws_bytes, _ptr(gu), _ptr(d_out_epd),
+                                         _ptr(bwd_ws), bwd_ws_bytes, _ptr(d_epd),
+                                         _ptr(dw_gate_up), _ptr(dw_down), _stream(stream)),
+           "occ_expert_backward_kept")
+
+
 def occ_router_backward(desc, x, w_router, logits, topk_idx, topk_w, slot_expert_host,
                         brim: occ_brim, dw_epd, dlogits, dx_router, dw_router, bwd_ws,
                         bwd_ws_bytes, stream=None):
@@ -305,6 +331,6 @@ __all__ = ["MoELayer", "OccError", "occ_layer_desc", "occ_brim", "make_desc", "d
            "occ_build_brim", "occ_build_brim_pruned", "occ_dispatch", "occ_expert_ffn", "occ_expert_up",
            "occ_expert_down", "occ_combine", "occ_dispatch_direct", "occ_combine_direct",
            "occ_backward_workspace_bytes", "occ_grad_combine", "occ_expert_backward",
-           "occ_router_backward", "occ_grad_dispatch",
-           "occ_coactivation", "occ_cross_coactivation", "occ_home_device", "occ_local_hits",
+           "occ_router_backward", "occ_grad_dispatch", "occ_expert_ffn_keep",
+           "occ_expert_backward_kept", "occ_coactivation", "occ_cross_coactivation", "occ_home_device", "occ_local_hits",
            "occ_place_greedy", "last_error"]

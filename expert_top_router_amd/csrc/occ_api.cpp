@@ -387,6 +387,59 @@ occ_status occ_expert_backward(const occ_layer_desc *desc, const void *epd, cons
                     "occ_expert_backward");
 }
 
+occ_status occ_expert_ffn_keep(const occ_layer_desc *desc, const void *epd, const occ_brim *brim,
+                               const int32_t *slot_expert_host, const void *w_gate_up,
+                               const void *w_down, void *h_ws, size_t h_ws_bytes, void *gu,
+                               void *out_epd, hipStream_t stream) {
+  OCC_TRY(check_backward(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const occ_layer_desc &L = *desc;
+  const int64_t Rd = (int64_t)L.T * L.k * L.d;
+  if (missing(epd, Rd) || !w_gate_up || !w_down || missing(h_ws, (int64_t)h_bytes(L)) ||
+      missing(gu, (int64_t)gu_bytes(L)) || missing(out_epd, Rd))
+    return fail(OCC_EINVAL, "epd, w_gate_up, w_down, h_ws, gu and out_epd must be set");
+  if (h_ws_bytes < h_bytes(L))
+    return fail(OCC_ENOSPC, "h workspace of %zu bytes < %zu required", h_ws_bytes, h_bytes(L));
+  occ::Placement pl;
+  OCC_TRY(make_placement(L, slot_expert_host, pl));
+  char *h = static_cast<char *>(h_ws);
+  hipError_t e = occ::launch_expert_up(L, epd, brim->slot_offset, pl, w_gate_up, h, nullptr,
+                                       nullptr, nullptr, stream, gu);
+  if (e != hipSuccess) return hip_status(e, "occ_expert_ffn_keep (up)");
+  return hip_status(occ::launch_expert_down(L, brim->slot_offset, pl, w_down, h, out_epd,
+                                            nullptr, nullptr, nullptr, stream),
+                    "occ_expert_ffn_keep (down)");
+}
+
+occ_status occ_expert_backward_kept(const occ_layer_desc *desc, const void *epd,
+                                    const occ_brim *brim, const int32_t *slot_expert_host,
+                                    const void *w_gate_up, const void *w_down, const void *h_ws,
+                                    size_t h_ws_bytes, const void *gu, const void *d_out_epd,
+                                    void *bwd_ws, size_t bwd_ws_bytes, void *d_epd,
+                                    float *dw_gate_up, float *dw_down, hipStream_t stream) {
+  OCC_TRY(check_backward(desc));
+  OCC_TRY(check_brim(*desc, brim, false));
+  const occ_layer_desc &L = *desc;
+  const int64_t Rd = (int64_t)L.T * L.k * L.d;
+  if (missing(epd, Rd) || !w_gate_up || !w_down || missing(d_out_epd, Rd) || missing(d_epd, Rd) ||
+      !dw_gate_up || !dw_down || missing(h_ws, (int64_t)h_bytes(L)) ||
+      missing(gu, (int64_t)gu_bytes(L)) || missing(bwd_ws, (int64_t)(2 * gu_bytes(L))))
+    return fail(OCC_EINVAL, "expert backward: an operand is NULL");
+  if (h_ws_bytes < h_bytes(L))
+    return fail(OCC_ENOSPC, "h workspace of %zu bytes < %zu", h_ws_bytes, h_bytes(L));
+  if (bwd_ws_bytes < 2 * gu_bytes(L))
+    return fail(OCC_ENOSPC, "backward workspace of %zu bytes < %zu", bwd_ws_bytes,
+                2 * gu_bytes(L));
+  occ::Placement pl;
+  OCC_TRY(make_placement(L, slot_expert_host, pl));
+  char *ws = static_cast<char *>(bwd_ws);
+  return hip_status(occ::launch_expert_backward(L, brim->slot_offset, pl, epd, w_gate_up, w_down,
+                                                h_ws, d_out_epd, const_cast<void *>(gu),
+                                                ws + gu_bytes(L), d_epd, dw_gate_up, dw_down,
+                                                stream, false),
+                    "occ_expert_backward_kept");
+}
+
 occ_status occ_router_backward(const occ_layer_desc *desc, const void *x, const float *w_router,
                                const float *logits, const int32_t *topk_idx,
                                const float *topk_w, const int32_t *slot_expert_host,

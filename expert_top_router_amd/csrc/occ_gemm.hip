@@ -20,7 +20,9 @@
 // next k-tile's first fragments load under that step's MFMAs.  The next
 // tile's first k-tile is loaded during the epilogue.  The epilogue applies
 // SwiGLU, rounds to bf16 in hardware and stages the tile in LDS, which is
-// written out as 16-byte row segments.
+// written out as 16-byte row segments.  For training steps the SwiGLU GEMM
+// can also keep its pre-activations [G | U] (KEEP), staged and written the
+// same way before h, so the backward need not recompute them.
 #include "occ_gemm_common.h"
 
 namespace occ {
@@ -31,7 +33,7 @@ namespace {
 // instruction: lane l supplies row (or column) l % 32 and the eight k values
 // 8*(l/32) .. 8*(l/32)+7 of a 16-deep k step; output element i of lane l is
 // row 8*(i/4) + 4*(l/32) + i%4, column l % 32.
-template <int BM, int BN, int PF, bool SWIGLU, int NWN>
+template <int BM, int BN, int PF, bool SWIGLU, int NWN, bool KEEP = false>
 __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int NT = 2 * NWN * kWave;               // 2 x NWN waves
   constexpr int WM = BM / 2, WN = BN / NWN;
@@ -44,6 +46,8 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
   constexpr int KSTEPS = kBK / 16;
   constexpr int CLD = BNO + 8;  // staged output row stride
   static_assert(BM * CLD <= 2 * STAGE, "output staging must fit in the tile buffers");
+  constexpr int GLD = BN + 8;  // staged [G | U] row stride (KEEP)
+  static_assert(!KEEP || (SWIGLU && BM * GLD <= 2 * STAGE), "[G | U] staging");
   static_assert(!SWIGLU || NI % 2 == 0, "gate and up halves");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
   __shared__ int32_t ts[OCC_MAX_E + 1];
@@ -250,6 +254,39 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
   uint16_t *Cg = static_cast<uint16_t *>(a.C) + (int64_t)cur.row_begin * a.ldc + cur.n0;
   uint16_t *Cs = smem;
   const int crow = lane & 31, ccol = (lane >> 5) * 4;
+  if (KEEP) {
+    // [G | U] of the tile, rounded to bf16 like h's inputs, staged as 256
+    // columns (gate columns, then up columns) and written to the G and U
+    // halves of the kept rows
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = wm * WM + mi * 32 + crow;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int col = brow[ni] + ccol;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x2v lo = {acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1]};
+          const f32x2v hi = {acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]};
+          const u32x2 packed = {
+              __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2v)),
+              __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2v))};
+          *reinterpret_cast<u32x2 *>(Cs + row * GLD + col + 8 * q) = packed;
+        }
+      }
+    }
+    __syncthreads();
+    uint16_t *Gg = static_cast<uint16_t *>(a.gu) + (int64_t)cur.row_begin * a.ldgu + cur.n0;
+    constexpr int GCH = BN / 8, HALF = GCH / 2;  // 16-byte chunks per staged row
+    for (int c = tid; c < BM * GCH; c += NT) {
+      const int r = c / GCH, cc = c - r * GCH;
+      const int hc = cc < HALF ? cc : cc - HALF;  // chunk inside its half
+      if (r < cur.rows && cur.n0 + hc * 8 < a.N)
+        *reinterpret_cast<u32x4 *>(Gg + (int64_t)r * a.ldgu + (cc < HALF ? 0 : a.N) + hc * 8) =
+            *reinterpret_cast<const u32x4 *>(Cs + r * GLD + cc * 8);
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
     const int row = wm * WM + mi * 32 + crow;
@@ -322,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a, int max_
   static_cast<float *>(a.C)[(int64_t)row * a.ldc + col] = v;
 }
 
-template <int BM, int BN, int PF, bool SWIGLU, int NWN>
+template <int BM, int BN, int PF, bool SWIGLU, int NWN, bool KEEP = false>
 void launch_bf16(const GemmArgs &a, int max_rows, int n_cu, hipStream_t st) {
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
   // worst case over all splits of max_rows rows into the groups
@@ -331,7 +368,7 @@ void launch_bf16(const GemmArgs &a, int max_rows, int n_cu, hipStream_t st) {
   const int64_t tiles = mt * ((a.N + BNO - 1) / BNO);
   // one persistent block per CU (a block fills a CU's LDS)
   const int64_t grid = tiles < n_cu ? tiles : n_cu;
-  gemm_bf16_kernel<BM, BN, PF, SWIGLU, NWN><<<(unsigned)grid, 2 * NWN * kWave, 0, st>>>(a);
+  gemm_bf16_kernel<BM, BN, PF, SWIGLU, NWN, KEEP><<<(unsigned)grid, 2 * NWN * kWave, 0, st>>>(a);
 }
 
 template <bool SWIGLU>
@@ -352,7 +389,8 @@ hipError_t run_gemm(const GemmArgs &a, int dtype, int max_rows, hipStream_t st) 
   // bounds the k loop (same-process A/B on the OLMoE-shaped layer: gate/up
   // 325 -> 297 us with the barrier before the last k step; 4 waves with the
   // barrier at the end of the k-tile measured faster than 8).
-  if (SWIGLU) launch_bf16<256, 256, 1, true, 4>(a, max_rows, n_cu, st);
+  if (SWIGLU && a.gu != nullptr) launch_bf16<256, 256, 1, true, 4, true>(a, max_rows, n_cu, st);
+  else if (SWIGLU) launch_bf16<256, 256, 1, true, 4>(a, max_rows, n_cu, st);
   else launch_bf16<256, 256, 1, false, 4>(a, max_rows, n_cu, st);
   return hipGetLastError();
 }
@@ -361,7 +399,7 @@ hipError_t run_gemm(const GemmArgs &a, int dtype, int max_rows, hipStream_t st) 
 
 hipError_t launch_expert_up(const occ_layer_desc &L, const void *epd, const int32_t *slot_offset,
                             const Placement &pl, const void *w_gate_up, void *h, const void *x,
-                            const void *w_gate_up_sh, void *h_sh, hipStream_t st) {
+                            const void *w_gate_up_sh, void *h_sh, hipStream_t st, void *gu) {
   const int64_t d = L.d, I = L.I;
   GemmArgs a = base_args(pl);
   a.row_offset = slot_offset;
@@ -382,6 +420,8 @@ hipError_t launch_expert_up(const occ_layer_desc &L, const void *epd, const int3
   a.N = (int)I;
   a.C = h;
   a.ldc = I;
+  a.gu = gu;
+  a.ldgu = 2 * I;
   hipError_t err = run_gemm<true>(a, L.dtype, L.T * L.k, st);
   if (err != hipSuccess || L.n_shared == 0) return err;
   const int64_t Is = L.I_shared;

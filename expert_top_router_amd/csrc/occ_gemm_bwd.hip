@@ -431,7 +431,7 @@ hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_o
                                   const Placement &pl, const void *epd, const void *w_gate_up,
                                   const void *w_down, const void *h, const void *d_out_epd,
                                   void *gu, void *dgu, void *d_epd, float *dw_gate_up,
-                                  float *dw_down, hipStream_t st) {
+                                  float *dw_down, hipStream_t st, bool recompute_gu) {
   const int64_t d = L.d, I = L.I, R = (int64_t)L.T * L.k, E = L.E;
   hipError_t err;
   // 1. [G | U] = EPD W_gate_up^T, recomputed and stored in bf16
@@ -449,7 +449,10 @@ hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_o
   a.N = (int)(2 * I);
   a.C = gu;
   a.ldc = 2 * I;
-  if ((err = launch_bwd<0, 0, false, EPI_BF16, 4>(a, grouped_tiles((int)R, L.E, a.N), st)) != hipSuccess)
+  // (skipped when the forward kept them: the same products, same rounding)
+  if (recompute_gu &&
+      (err = launch_bwd<0, 0, false, EPI_BF16, 4>(a, grouped_tiles((int)R, L.E, a.N), st)) !=
+          hipSuccess)
     return err;
   // 2. dh = d_out_EPD W_down (W_down[e] is [d][I]); SwiGLU backward -> [dG | dU]
   a = base_args(pl);

@@ -27,6 +27,10 @@ struct GemmArgs {
   int N;                   // output columns
   void *C;
   int64_t ldc;
+  // SwiGLU forward with the pre-activations kept: [G | U] rows (bf16, row
+  // stride ldgu, G in columns [0, N), U in [N, 2N)), else nullptr
+  void *gu;
+  int64_t ldgu;
   // backward GEMMs only
   int M;                   // output rows when K is grouped (fixed)
   int64_t c_group_stride;  // elements between the outputs of consecutive experts

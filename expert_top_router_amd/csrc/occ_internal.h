@@ -126,11 +126,13 @@ hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_o
                                   const Placement &pl, const void *epd, const void *w_gate_up,
                                   const void *w_down, const void *h, const void *d_out_epd,
                                   void *gu, void *dgu, void *d_epd, float *dw_gate_up,
-                                  float *dw_down, hipStream_t st);
+                                  float *dw_down, hipStream_t st, bool recompute_gu = true);
+// gu: when set (bf16 layers without shared experts), the [G | U] rows are
+// also written (bf16 [R][2I])
 hipError_t launch_expert_up(const occ_layer_desc &L, const void *epd, const int32_t *slot_offset,
                             const Placement &pl, const void *w_gate_up, void *h,
                             const void *x, const void *w_gate_up_sh, void *h_sh,
-                            hipStream_t st);
+                            hipStream_t st, void *gu = nullptr);
 hipError_t launch_expert_down(const occ_layer_desc &L, const int32_t *slot_offset,
                               const Placement &pl, const void *w_down, const void *h,
                               void *out_epd, const void *w_down_sh, const void *h_sh,

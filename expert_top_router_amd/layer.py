@@ -14,6 +14,7 @@ import numpy as np
 
 from . import (desc_of, make_brim, occ_backward_workspace_bytes, occ_build_brim,
                occ_build_brim_pruned, occ_coactivation, occ_combine, occ_expert_backward,
+               occ_expert_backward_kept, occ_expert_ffn_keep,
                occ_grad_combine, occ_grad_dispatch, occ_router_backward,
                occ_combine_direct, occ_dispatch, occ_dispatch_direct, occ_expert_down,
                occ_expert_ffn, occ_expert_up, occ_ffn_workspace_bytes, occ_route_topk,
@@ -202,6 +203,7 @@ class MoELayer:
         self.dw_router = buf((E, d), f32)
         self.d_sfd = buf((S_max, d), el)
         self.dx = buf((T, d), el)
+        self.gu = buf((R, 2 * cfg.I), el)  # kept [G | U] (forward_keep)
 
     def grad_combine(self, stream=None):
         occ_grad_combine(self.desc, self.dy, self.brim, self.out_epd, self.d_out_sfd,
@@ -211,6 +213,37 @@ class MoELayer:
         occ_expert_backward(self.desc, self.epd, self.brim, self.slot_expert, self.w.w_gate_up,
                             self.w.w_down, self.h_ws, self.h_bytes, self.d_out_epd, self.bwd_ws,
                             self.bwd_bytes, self.d_epd, self.dw_gate_up, self.dw_down, stream)
+
+    # ---- training steps that keep [G | U] instead of recomputing it -----------
+    def expert_ffn_keep(self, stream=None):
+        self._grad_buffers()
+        occ_expert_ffn_keep(self.desc, self.epd, self.brim, self.slot_expert, self.w.w_gate_up,
+                            self.w.w_down, self.h_ws, self.h_bytes, self.gu, self.out_epd, stream)
+
+    def expert_backward_kept(self, stream=None):
+        occ_expert_backward_kept(self.desc, self.epd, self.brim, self.slot_expert,
+                                 self.w.w_gate_up, self.w.w_down, self.h_ws, self.h_bytes,
+                                 self.gu, self.d_out_epd, self.bwd_ws, self.bwd_bytes, self.d_epd,
+                                 self.dw_gate_up, self.dw_down, stream)
+
+    def forward_keep(self, stream=None):
+        """forward() with the expert FFN keeping [G | U] for backward_kept()."""
+        self.route(stream)
+        self.build_brim(stream)
+        self.dispatch(stream)
+        self.expert_ffn_keep(stream)
+        self.combine(stream)
+
+    def backward_kept(self, dy=None, stream=None):
+        """backward() after forward_keep(): the expert backward reads the kept
+        [G | U] instead of recomputing it."""
+        self._grad_buffers()
+        if dy is not None:
+            self.dy.copy_(dy)
+        self.grad_combine(stream)
+        self.expert_backward_kept(stream)
+        self.router_backward(stream)
+        self.grad_dispatch(stream)
 
     def router_backward(self, stream=None):
         occ_router_backward(self.desc, self.w.x, self.w.w_router, self.logits, self.topk_idx,

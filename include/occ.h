@@ -262,6 +262,28 @@ occ_status occ_expert_backward(const occ_layer_desc *desc, const void *epd, cons
                                void *d_epd, float *dw_gate_up, float *dw_down,
                                hipStream_t stream);
 
+/* Training (Expert Coupling in MoE Pretraining, Abstract: the layer runs
+ * forward and backward): the pair for steps that keep the experts' pre-activations instead
+ * of recomputing them (bf16 layers without shared experts; EUNSUP otherwise):
+ * occ_expert_ffn_keep is occ_expert_ffn that also writes
+ *   gu[r] = [EPD W_gate^T | EPD W_up^T] of EPD row r   (bf16 [R][2I], rows < R;
+ *           the products rounded once, as h's inputs)
+ * and occ_expert_backward_kept is occ_expert_backward reading [G | U] from gu
+ * (written by occ_expert_ffn_keep for the same layer, weights and BRIM)
+ * instead of recomputing it; bwd_ws as for occ_expert_backward.  The results
+ * equal occ_expert_ffn's and occ_expert_backward's bit for bit; the pair
+ * trades 2 R I bf16 values of device memory for one grouped GEMM. */
+occ_status occ_expert_ffn_keep(const occ_layer_desc *desc, const void *epd, const occ_brim *brim,
+                               const int32_t *slot_expert_host, const void *w_gate_up,
+                               const void *w_down, void *h_ws, size_t h_ws_bytes, void *gu,
+                               void *out_epd, hipStream_t stream);
+occ_status occ_expert_backward_kept(const occ_layer_desc *desc, const void *epd,
+                                    const occ_brim *brim, const int32_t *slot_expert_host,
+                                    const void *w_gate_up, const void *w_down, const void *h_ws,
+                                    size_t h_ws_bytes, const void *gu, const void *d_out_epd,
+                                    void *bwd_ws, size_t bwd_ws_bytes, void *d_epd,
+                                    float *dw_gate_up, float *dw_down, hipStream_t stream);
+
 /* Gradient of the routing: for each token, dp of its picks from dw_epd
  * (through the renormalisation when desc->renorm), then the softmax backward
  * over all E experts, from the forward's fp32 logits:

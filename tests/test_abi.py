@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(occ):
     names = declared_symbols()
-    assert len(names) == 23, names
+    assert len(names) == 25, names
     lib = C.CDLL(occ.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -131,6 +131,22 @@ def test_backward_arguments_are_checked(occ):
     rc = lib.occ_router_backward(C.byref(d), FAKE, FAKE, None, FAKE, FAKE, se.ctypes.data,
                                  C.byref(brim), FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
     assert rc == -1
+    # the pair that keeps [G | U]: bf16 without shared experts, gu required
+    assert lib.occ_expert_ffn_keep(C.byref(f32), FAKE, C.byref(brim), se.ctypes.data, FAKE, FAKE,
+                                   FAKE, hb, FAKE, FAKE, None) == -2
+    assert lib.occ_expert_ffn_keep(C.byref(sh), FAKE, C.byref(brim), se.ctypes.data, FAKE, FAKE,
+                                   FAKE, hb, FAKE, FAKE, None) == -2
+    assert lib.occ_expert_ffn_keep(C.byref(d), FAKE, C.byref(brim), se.ctypes.data, FAKE, FAKE,
+                                   FAKE, hb, None, FAKE, None) == -1
+    assert lib.occ_expert_ffn_keep(C.byref(d), FAKE, C.byref(brim), se.ctypes.data, FAKE, FAKE,
+                                   FAKE, hb - 1, FAKE, FAKE, None) == -3
+    rc = lib.occ_expert_backward_kept(C.byref(d), FAKE, C.byref(brim), se.ctypes.data, FAKE,
+                                      FAKE, FAKE, hb, None, FAKE, FAKE, ws, FAKE, FAKE, FAKE, None)
+    assert rc == -1
+    rc = lib.occ_expert_backward_kept(C.byref(d), FAKE, C.byref(brim), se.ctypes.data, FAKE,
+                                      FAKE, FAKE, hb, FAKE, FAKE, FAKE, ws - 1, FAKE, FAKE, FAKE,
+                                      None)
+    assert rc == -3
     # a long batch splits dW_r over token chunks, whose partial sums need the workspace
     big = _desc(occ, T=8192)
     rc = lib.occ_router_backward(C.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, se.ctypes.data,

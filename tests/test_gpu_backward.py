@@ -267,3 +267,48 @@ def test_pruned_layer_backward_parity(orc, budget, rescale):
     dx, _ = ob.grad_dispatch(b, lambda r: _bf(g["d_epd"][r]), np.arange(cfg.T), cfg.T, cfg.D,
                              L, cfg.d, "bf16", g["dx_router"])
     assert_close(_bf(g["dx"]), dx, "bf16", "dx")
+
+
+@pytest.mark.parametrize("name", ["bf16_ragged", "olmoe_bf16"])
+def test_kept_preactivations_match_recompute(name):
+    """occ_expert_ffn_keep + occ_expert_backward_kept against occ_expert_ffn +
+    occ_expert_backward: the kept [G | U] equals the backward's recomputed
+    one, and every output and gradient is the same, bit for bit."""
+    import torch
+    from expert_top_router_amd.layer import MoELayer, to_device, upload_inputs
+    from tests.test_gpu_parity import SMALL
+
+    cfg = SMALL[name] if name in SMALL else W.CONFIGS[name]
+    say(f"case kept [G | U] {name}")
+    inp = W.make_layer(cfg, seed=23)
+    lay = MoELayer(cfg, upload_inputs(inp), inp.slot_expert, with_logits=True)
+    lay.prepare_backward()
+    dy = W.from_f64(np.random.default_rng(23).standard_normal((cfg.T, cfg.d)), "bf16")
+    lay.dy.copy_(to_device(dy))
+    names = ("out_epd", "y", "d_epd", "dw_gate_up", "dw_down", "dx", "dw_router", "dlogits")
+
+    def bits(t):
+        return t.contiguous().view(torch.uint8).clone()
+
+    lay.forward()
+    lay.grad_combine()
+    lay.expert_backward()
+    torch.cuda.synchronize()
+    R = int(lay.host("slot_offset")[-1])
+    I2 = 2 * cfg.I
+    # the recomputed [G | U] (the router gradient reuses the workspace next)
+    gu_ref = bits(lay.bwd_ws[:R * I2 * 2])
+    lay.router_backward()
+    lay.grad_dispatch()
+    torch.cuda.synchronize()
+    ref = {n: bits(getattr(lay, n)) for n in names}
+    lay.poison()
+    for n in ("d_epd", "dw_gate_up", "dw_down", "dx", "dw_router", "dlogits", "gu", "bwd_ws"):
+        getattr(lay, n).view(torch.uint8).fill_(0xA5)
+    torch.cuda.synchronize()
+    lay.forward_keep()
+    lay.backward_kept()
+    torch.cuda.synchronize()
+    assert torch.equal(bits(lay.gu.view(-1)[:R * I2]), gu_ref), "kept [G | U]"
+    for n in names:
+        assert torch.equal(bits(getattr(lay, n)), ref[n]), n
