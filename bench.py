@@ -6,19 +6,23 @@ A step is one forward pass of the whole layer over one batch: routing and
 top-k, BRIM build, dispatch ORI -> SFD -> EPD, the grouped SwiGLU experts and
 the pre-reduction + combine back to ORI, issued back to back on one stream
 with every input already resident in HBM.  The default workload is the
-OLMoE-shaped layer (T=4096, d=2048, E=64, I=1024, top-8, 8 logical devices,
-clustered tokens).  Prints one JSON line.
+largest single-GPU layer of the suite, the skewed top-6 stress layer
+(T=65536, d=2048, E=128, I=768, 16 logical devices, 64 token clusters, a
+router skewed toward 14 hot expert groups).  Prints one JSON line.
 
 The roofline object describes the dominant kernel (the gate/up GEMM with the
 SwiGLU epilogue): achieved = algorithmic flops per launch / its mean launch
 time, from HIP events recorded around it in every timed step on the stream
 it runs on.  The per-stage times come from a second pass of the same steps
-with an event between every two stages.  cpu_baseline times the CPU
-oracle (single thread) on a bounded sample of the same workload.  After the
-headline steps the line also carries the widened rows (conventional, pruned,
-affinity, backward) and a calibration: the vendor library's dense bf16
-matmul with the gate/up GEMM's flop on the same box (context for the
-roofline fraction; not part of any measured step).
+with an event between every two stages; step_breakdown sets their sum
+against the wall time per step and gives the step replayed from a HIP
+graph.  cpu_baseline times the CPU oracle (single thread) on a bounded
+sample of the same workload.  After the headline steps the line also
+carries the widened rows (conventional, pruned, affinity, backward), a
+calibration (the vendor library's dense bf16 matmul with the gate/up GEMM's
+flop on the same box: context for the roofline fraction, not part of any
+measured step) and, under "workloads", the other bf16 layers (the
+DeepSeek-V2-Lite-shaped one under contiguous and correlated placement).
 """
 from __future__ import annotations
 
@@ -38,7 +42,7 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_F32_VALU_TFLOPS = 78.6  # fp32 FMA without packed math (256 CU x 64 lanes x 2 x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE-layer tokens/sec (route+dispatch+FFN+combine); % HBM and % MFMA peak"
-DEFAULT_WORKLOAD = "olmoe_bf16"
+DEFAULT_WORKLOAD = "stress_bf16"
 
 
 def parse():
@@ -49,7 +53,12 @@ def parse():
     p.add_argument("--config", default=DEFAULT_WORKLOAD)
     p.add_argument("--placement", default="contiguous", choices=["contiguous", "greedy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=448)
+    p.add_argument("--no-others", action="store_true",
+                   help="skip the secondary workloads (the other bf16 layers)")
+    p.add_argument("--cpu-route-tokens", type=int, default=4096,
+                   help="oracle baseline: tokens of the sub-batch routed and re-indexed")
+    p.add_argument("--cpu-sample-tokens", type=int, default=448,
+                   help="oracle baseline: tokens whose expert FFN and combine are timed")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many forward steps (for rocprofv3), print nothing else")
     p.add_argument("--profile-backward", action="store_true",
@@ -330,10 +339,11 @@ def dense_library_rate(cfg, torch):
             "frac": tf / PEAK_BF16_TFLOPS}
 
 
-def cpu_baseline(inp, n_tok):
-    """The oracle as it stands, one thread: routing and BRIMs on the full
-    batch, expert FFN and combine on a seeded sample of tokens; tokens/s
-    extrapolated linearly from the per-token cost of each part."""
+def cpu_baseline(inp, n_route, n_ffn):
+    """The oracle as it stands, one thread, on a bounded sample of the
+    workload: routing, BRIMs and gathers on a sub-batch of the first n_route
+    tokens, expert FFN and combine on n_ffn seeded tokens of that sub-batch;
+    tokens/s extrapolated linearly from the per-token cost of each part."""
     import oracle
     if not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
         oracle.build()
@@ -343,7 +353,7 @@ def cpu_baseline(inp, n_tok):
     core = min(mask)
     os.sched_setaffinity(0, {core})
     try:
-        res = _cpu_baseline_timed(inp, n_tok)
+        res = _cpu_baseline_timed(inp, n_route, n_ffn)
     finally:
         os.sched_setaffinity(0, mask)
     res.update({"pinned_core": core, "host_cpus": len(mask), "cpu_model": _cpu_model()})
@@ -361,20 +371,22 @@ def _cpu_model():
     return "unknown"
 
 
-def _cpu_baseline_timed(inp, n_tok):
+def _cpu_baseline_timed(inp, n_route, n_ffn):
     import oracle
     cfg = inp.cfg
-    T, E, k, D, d = cfg.T, cfg.E, cfg.k, cfg.D, cfg.d
+    E, k, D, d = cfg.E, cfg.k, cfg.D, cfg.d
     L = E // D
+    Tb = min(n_route, cfg.T)
+    x = inp.x[:Tb]
     t0 = time.perf_counter()
-    lg = oracle.logits(inp.x, inp.w_router, cfg.dtype)
+    lg = oracle.logits(x, inp.w_router, cfg.dtype)
     idx, w = oracle.topk(lg, k, cfg.renorm)
     b = oracle.brim(idx, w, inp.slot_expert, E, D)
-    sfd = oracle.gather(inp.x, b["sfd_token"][:b["S"]])
+    sfd = oracle.gather(x, b["sfd_token"][:b["S"]])
     oracle.gather(sfd, b["epd_sfd"])
-    t_full = time.perf_counter() - t0
+    t_batch = time.perf_counter() - t0
     rng = np.random.default_rng(0)
-    tok = np.sort(rng.choice(T, size=min(n_tok, T), replace=False)).astype(np.int32)
+    tok = np.sort(rng.choice(Tb, size=min(n_ffn, Tb), replace=False)).astype(np.int32)
     t1 = time.perf_counter()
     rows = []
     for dv in range(D):
@@ -385,21 +397,159 @@ def _cpu_baseline_timed(inp, n_tok):
             rows.append(r[r >= 0])
     rows = np.sort(np.concatenate(rows)).astype(np.int64)
     ex_of_slot = np.repeat(np.asarray(inp.slot_expert), np.diff(b["slot_offset"]))
-    out = oracle.expert_rows(inp.x, b["epd_token"][rows], ex_of_slot[rows], inp.w_gate_up,
+    out = oracle.expert_rows(x, b["epd_token"][rows], ex_of_slot[rows], inp.w_gate_up,
                              inp.w_down, cfg.dtype)
-    epd_row = np.full(T * k, -1, np.int32)
+    epd_row = np.full(Tb * k, -1, np.int32)
     epd_row[rows] = np.arange(rows.size, dtype=np.int32)
     shared = None
     if cfg.n_shared:
-        shared = oracle.shared_rows(inp.x, tok, inp.w_gate_up_sh, inp.w_down_sh, cfg.dtype)
-    oracle.combine(tok, b, T, D, L, d, cfg.dtype, out, epd_row, shared)
+        shared = oracle.shared_rows(x, tok, inp.w_gate_up_sh, inp.w_down_sh, cfg.dtype)
+    oracle.combine(tok, b, Tb, D, L, d, cfg.dtype, out, epd_row, shared)
     t_sample = time.perf_counter() - t1
-    per_token = t_full / T + t_sample / tok.size
+    per_token = t_batch / Tb + t_sample / tok.size
     return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"routing, BRIMs and gathers on all {T} tokens ({t_full:.2f} s); "
-                       f"expert FFN and combine on {tok.size} seeded tokens with all their "
-                       f"{rows.size} EPD rows ({t_sample:.2f} s); tokens/s = 1 / (full-batch "
-                       f"time / T + sample time / sample tokens), one thread")}
+            "sample": (f"routing, BRIMs and gathers on a sub-batch of the first {Tb} of the "
+                       f"{cfg.T} tokens ({t_batch:.2f} s); expert FFN and combine on {tok.size} "
+                       f"seeded tokens of it with all their {rows.size} EPD rows "
+                       f"({t_sample:.2f} s); tokens/s = 1 / (sub-batch time / {Tb} + sample "
+                       f"time / {tok.size}), one thread")}
+
+
+def stage_times(lay, cfg, n, torch):
+    """Mean time of each stage over n steps (an event between every two
+    stages on the launch stream), with the derived roofline fractions, and
+    the co-activation side output timed alone."""
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+             for _ in range(n)]
+    for i in range(n):
+        step(lay, marks[i])
+    ca = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ca[0].record()
+    for _ in range(n):
+        lay.coactivation()
+    ca[1].record()
+    torch.cuda.synchronize()
+    t = {name: float(np.mean([m[j].elapsed_time(m[j + 1]) for m in marks])) / 1e3
+         for j, name in enumerate(STAGES)}
+    t["coactivation"] = ca[0].elapsed_time(ca[1]) / 1e3 / n
+    S = int(lay.host("S")[0])
+    alg = algorithmic(cfg, S)
+    peak_mfma = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    return {
+        "route_us": t["route"] * 1e6,
+        "route_valu_frac": alg["route_flop"] / t["route"] / 1e12 / PEAK_F32_VALU_TFLOPS,
+        "route_hbm_frac": alg["route_bytes"] / t["route"] / 1e9 / PEAK_HBM_GBS,
+        "build_brim_us": t["build_brim"] * 1e6,
+        "build_brim_hbm_frac": alg["brim_bytes"] / t["build_brim"] / 1e9 / PEAK_HBM_GBS,
+        "dispatch_us": t["dispatch"] * 1e6,
+        "dispatch_hbm_frac": alg["dispatch_bytes"] / t["dispatch"] / 1e9 / PEAK_HBM_GBS,
+        "expert_up_us": t["expert_up"] * 1e6,
+        "expert_up_mfma_frac": alg["up_flop"] / t["expert_up"] / 1e12 / peak_mfma,
+        "expert_down_us": t["expert_down"] * 1e6,
+        "expert_down_mfma_frac": alg["down_flop"] / t["expert_down"] / 1e12 / peak_mfma,
+        "combine_us": t["combine"] * 1e6,
+        "combine_hbm_frac": alg["combine_bytes"] / t["combine"] / 1e9 / PEAK_HBM_GBS,
+        "coactivation_us": t["coactivation"] * 1e6,
+        "sum_us": sum(t[name] for name in STAGES) * 1e6,
+    }
+
+
+def timed_steps(lay, steps, torch):
+    """Seconds for `steps` whole steps back to back (synchronised both sides)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(lay)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def graph_replay(lay, steps, torch):
+    """The same step captured once into a HIP graph (torch's graph API around
+    the same C-ABI calls) and replayed: ms per step without host launch
+    overhead.  The library allocates nothing, so nothing is captured but its
+    kernels."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            step(lay)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(lay)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    del g
+    return el / steps * 1e3
+
+
+def greedy_placement(cfg, torch):
+    """Correlated placement from a calibration batch (token seed 1): its
+    routing and co-activation counts on the GPU, then occ_place_greedy."""
+    import expert_top_router_amd as occ
+    import workloads as W
+    from expert_top_router_amd.layer import MoELayer, upload_inputs
+    cal = W.make_layer(cfg, seed=0, token_seed=1, experts=False)
+    lay = MoELayer(cfg, upload_inputs(cal), cal.slot_expert)
+    lay.route()
+    lay.coactivation()
+    torch.cuda.synchronize()
+    counts = lay.host("counts")
+    del lay
+    return occ.occ_place_greedy(cfg.E, cfg.D, counts), counts
+
+
+def intra_share(counts, slot_expert, D):
+    """Share of co-selection events (pairs i < j of a token's experts) whose
+    two experts sit on one device."""
+    E = counts.shape[0]
+    L = E // D
+    dev = np.empty(E, np.int64)
+    dev[np.asarray(slot_expert)] = np.arange(E) // L
+    iu = np.triu_indices(E, 1)
+    c = counts[iu].astype(np.int64)
+    same = dev[iu[0]] == dev[iu[1]]
+    return float(c[same].sum()) / max(float(c.sum()), 1.0)
+
+
+def other_workload(name, steps, warmup, torch, placements=("contiguous",)):
+    """A secondary workload: whole-step time and per-stage times for each
+    placement (a fresh layer per placement, freed afterwards)."""
+    import workloads as W
+    from expert_top_router_amd.layer import MoELayer, upload_inputs
+    cfg = W.CONFIGS[name]
+    inp = W.make_layer(cfg, seed=0)
+    weights = upload_inputs(inp)
+    out = {"T": cfg.T, "d": cfg.d, "E": cfg.E, "I": cfg.I, "k": cfg.k, "D": cfg.D,
+           "n_shared": cfg.n_shared}
+    for pl in placements:
+        rec = {}
+        se = inp.slot_expert
+        if pl == "greedy":
+            se, counts = greedy_placement(cfg, torch)
+            rec["intra_share"] = intra_share(counts, se, cfg.D)
+            rec["contiguous_intra_share"] = intra_share(counts, inp.slot_expert, cfg.D)
+        lay = MoELayer(cfg, weights, se)
+        for _ in range(warmup):
+            step(lay)
+        el = timed_steps(lay, steps, torch)
+        S = int(lay.host("S")[0])
+        rec.update({"ms_per_step": el / steps * 1e3, "tokens_per_s": cfg.T * steps / el,
+                    "sfd_rows": S, "sfd_over_tk": S / max(cfg.R, 1),
+                    "stages": stage_times(lay, cfg, max(5, min(steps, 20)), torch)})
+        out[pl] = rec
+        del lay
+        torch.cuda.empty_cache()
+    del weights
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -418,17 +568,7 @@ def main():
     cfg = W.CONFIGS[args.config]
     inp = W.make_layer(cfg, seed=0)
     if args.placement == "greedy":
-        # correlated placement from a calibration batch (token seed 1)
-        import expert_top_router_amd as occ
-        cal = W.make_layer(cfg, seed=0, token_seed=1, experts=False)
-        lay_cal = MoELayer(cfg, upload_inputs(W.LayerInputs(cfg, cal.x, cal.w_router, None, None,
-                                                            None, None, cal.slot_expert)),
-                           cal.slot_expert)
-        lay_cal.route()
-        lay_cal.coactivation()
-        torch.cuda.synchronize()
-        inp.slot_expert = occ.occ_place_greedy(cfg.E, cfg.D, lay_cal.host("counts"))
-        del lay_cal
+        inp.slot_expert, _ = greedy_placement(cfg, torch)
     lay = MoELayer(cfg, upload_inputs(inp), inp.slot_expert)
     torch.cuda.synchronize()
 
@@ -479,40 +619,11 @@ def main():
 
     # Per-stage mean times in the same sequence (separate pass, an event
     # between every two stages), and the co-activation side output alone.
-    n = max(10, min(args.steps, 50))
-    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
-             for _ in range(n)]
-    for i in range(n):
-        step(lay, marks[i])
-    ca = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ca[0].record()
-    for _ in range(n):
-        lay.coactivation()
-    ca[1].record()
-    torch.cuda.synchronize()
-    t = {name: float(np.mean([m[j].elapsed_time(m[j + 1]) for m in marks])) / 1e3
-         for j, name in enumerate(STAGES)}
-    t["coactivation"] = ca[0].elapsed_time(ca[1]) / 1e3 / n
+    stages = stage_times(lay, cfg, max(10, min(args.steps, 50)), torch)
     S = int(lay.host("S")[0])
     alg = algorithmic(cfg, S)
     peak_mfma = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     up_tf = alg["up_flop"] / up_s / 1e12
-    stages = {
-        "route_us": t["route"] * 1e6,
-        "route_valu_frac": alg["route_flop"] / t["route"] / 1e12 / PEAK_F32_VALU_TFLOPS,
-        "route_hbm_frac": alg["route_bytes"] / t["route"] / 1e9 / PEAK_HBM_GBS,
-        "build_brim_us": t["build_brim"] * 1e6,
-        "build_brim_hbm_frac": alg["brim_bytes"] / t["build_brim"] / 1e9 / PEAK_HBM_GBS,
-        "dispatch_us": t["dispatch"] * 1e6,
-        "dispatch_hbm_frac": alg["dispatch_bytes"] / t["dispatch"] / 1e9 / PEAK_HBM_GBS,
-        "expert_up_us": t["expert_up"] * 1e6,
-        "expert_up_mfma_frac": alg["up_flop"] / t["expert_up"] / 1e12 / peak_mfma,
-        "expert_down_us": t["expert_down"] * 1e6,
-        "expert_down_mfma_frac": alg["down_flop"] / t["expert_down"] / 1e12 / peak_mfma,
-        "combine_us": t["combine"] * 1e6,
-        "combine_hbm_frac": alg["combine_bytes"] / t["combine"] / 1e9 / PEAK_HBM_GBS,
-        "coactivation_us": t["coactivation"] * 1e6,
-    }
     out = {
         "metric": METRIC,
         "value": value,
@@ -537,6 +648,11 @@ def main():
                      "flop_per_launch": alg["up_flop"]},
         "stages": stages,
     }
+    # where the step's wall time goes: kernels (stage pass) against the rest
+    # (launch gaps), and the same step replayed from a HIP graph
+    out["step_breakdown"] = {"kernel_sum_us": stages["sum_us"],
+                             "wall_minus_kernels_us": ms_per_step * 1e3 - stages["sum_us"],
+                             "graph_ms_per_step": graph_replay(lay, args.steps, torch)}
     out["conventional"] = conventional(lay, cfg, args.steps, torch)
     if cfg.D >= 4:
         out["pruned"] = pruned(cfg, lay.w, inp.slot_expert, max(1, cfg.D // 4), args.steps, torch)
@@ -545,8 +661,18 @@ def main():
         out["backward"] = backward(lay, cfg, args.steps, torch)
     if cfg.dtype == "bf16":
         out["calibration"] = dense_library_rate(cfg, torch)
+    del lay
+    torch.cuda.empty_cache()
+    if not args.no_others:
+        others = {}
+        for name in ("olmoe_bf16", "mixtral_bf16", "dsv2lite_bf16", "stress_bf16"):
+            if name == cfg.name:
+                continue
+            pls = ("contiguous", "greedy") if name == "dsv2lite_bf16" else ("contiguous",)
+            others[name] = other_workload(name, args.steps, args.warmup, torch, pls)
+        out["workloads"] = others
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_route_tokens, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)
 
 

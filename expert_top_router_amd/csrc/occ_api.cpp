@@ -332,6 +332,10 @@ static occ_status check_backward(const occ_layer_desc *desc) {
   OCC_TRY(check_desc(desc));
   if (desc->dtype != OCC_BF16) return fail(OCC_EUNSUP, "the backward pass is for bf16 layers");
   if (desc->n_shared != 0) return fail(OCC_EUNSUP, "the backward pass has no shared experts");
+  // [G | U] and [dG | dU] (R x 2I bf16) are GEMM operands addressed with
+  // 32-bit byte offsets, like every operand check_desc bounds
+  if ((int64_t)desc->T * desc->k * 2 * desc->I * 2 > 0xffffffffll)
+    return fail(OCC_EUNSUP, "the backward's [G | U] rows exceed 4 GiB");
   return OCC_OK;
 }
 

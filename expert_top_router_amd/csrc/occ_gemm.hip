@@ -23,6 +23,8 @@
 // written out as 16-byte row segments.  For training steps the SwiGLU GEMM
 // can also keep its pre-activations [G | U] (KEEP), staged and written the
 // same way before h, so the backward need not recompute them.
+#include <atomic>
+
 #include "occ_gemm_common.h"
 
 namespace occ {
@@ -380,10 +382,8 @@ hipError_t run_gemm(const GemmArgs &a, int dtype, int max_rows, hipStream_t st) 
         a, max_rows);
     return hipGetLastError();
   }
-  int dev = 0, n_cu = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return hipGetLastError();
+  const int n_cu = device_cu_count();
+  if (n_cu <= 0) return hipGetLastError();
   // 8 waves (2 x 4, two per SIMD, 128 x 64 wave tiles): against 4 waves of
   // 128 x 128 the LDS serves about 1.7 times the fragment bandwidth, which
   // bounds the k loop (same-process A/B on the OLMoE-shaped layer: gate/up
@@ -396,6 +396,25 @@ hipError_t run_gemm(const GemmArgs &a, int dtype, int max_rows, hipStream_t st) 
 }
 
 }  // namespace
+
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];  // 0: not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= kMaxDevices) {
+    int n = 0;
+    return hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess
+               ? n : 0;
+  }
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return 0;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 hipError_t launch_expert_up(const occ_layer_desc &L, const void *epd, const int32_t *slot_offset,
                             const Placement &pl, const void *w_gate_up, void *h, const void *x,

@@ -411,10 +411,8 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bwd_kernel(GemmArgs a) {
 template <int ALAY, int BLAY, bool GK, int EPI, int NWN>
 hipError_t launch_bwd(const GemmArgs &a, int64_t tiles, hipStream_t st) {
   if (tiles <= 0) return hipSuccess;
-  int dev = 0, n_cu = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return hipGetLastError();
+  const int n_cu = device_cu_count();
+  if (n_cu <= 0) return hipGetLastError();
   const int64_t grid = tiles < n_cu ? tiles : n_cu;
   gemm_bwd_kernel<ALAY, BLAY, GK, EPI, NWN><<<(unsigned)grid, 2 * NWN * kWave, 0, st>>>(a);
   return hipGetLastError();

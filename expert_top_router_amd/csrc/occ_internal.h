@@ -69,6 +69,10 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 }
 
+// Compute units of the current device, queried once per device and cached
+// (the persistent GEMMs launch one block per CU).  Returns 0 on a HIP error.
+int device_cu_count();
+
 // ---- launchers (each returns hipGetLastError() of its launches) -----------
 hipError_t launch_route_topk(const occ_layer_desc &L, const void *x, const float *wr,
                              int32_t *idx, float *w, float *logits, hipStream_t st);

@@ -113,6 +113,8 @@ class MoELayer:
     def route(self, stream=None):
         occ_route_topk(self.desc, self.w.x, self.w.w_router, self.topk_idx, self.topk_w,
                        self.logits, stream)
+        # the router gradient needs the logits of the forward it differentiates
+        self._routed_with_logits = self.logits is not None
 
     def build_brim(self, stream=None):
         if self.budget is None:
@@ -227,7 +229,9 @@ class MoELayer:
                                  self.dw_gate_up, self.dw_down, stream)
 
     def forward_keep(self, stream=None):
-        """forward() with the expert FFN keeping [G | U] for backward_kept()."""
+        """forward() with the expert FFN keeping [G | U] for backward_kept()
+        (and the logits the router gradient needs)."""
+        self._grad_buffers()
         self.route(stream)
         self.build_brim(stream)
         self.dispatch(stream)
@@ -237,6 +241,7 @@ class MoELayer:
     def backward_kept(self, dy=None, stream=None):
         """backward() after forward_keep(): the expert backward reads the kept
         [G | U] instead of recomputing it."""
+        self._require_logits()
         self._grad_buffers()
         if dy is not None:
             self.dy.copy_(dy)
@@ -258,6 +263,7 @@ class MoELayer:
         """Gradients of the last forward (which must have kept its logits:
         construct with with_logits=True, or call prepare_backward() first)
         for the upstream gradient dy (bf16 [T, d]; self.dy when None)."""
+        self._require_logits()
         self._grad_buffers()
         if dy is not None:
             self.dy.copy_(dy)
@@ -265,6 +271,12 @@ class MoELayer:
         self.expert_backward(stream)
         self.router_backward(stream)
         self.grad_dispatch(stream)
+
+    def _require_logits(self):
+        if not getattr(self, "_routed_with_logits", False):
+            raise RuntimeError("the last forward did not keep its logits: construct the layer "
+                               "with with_logits=True or call prepare_backward() (or use "
+                               "forward_keep()) before the forward")
 
     def prepare_backward(self):
         """Allocate the gradient buffers (and the logits the router gradient needs)."""

@@ -33,8 +33,9 @@
  *   - Arguments are validated on the host before anything is launched.  On
  *     an error nothing is launched and no output is touched; the return code
  *     says why and occ_last_error() gives the text.
- *   - The library holds no state besides the per-thread error text; calls on
- *     different streams are independent.
+ *   - The library holds no state besides the per-thread error text and the
+ *     per-device compute-unit count it caches; calls on different streams
+ *     are independent.
  */
 #ifndef OCC_H
 #define OCC_H

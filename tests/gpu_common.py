@@ -125,8 +125,52 @@ def as_f32(a, dtype):
     return W.to_f32(a, dtype)
 
 
-def compare(g, o, inp, full=True):
-    """Stage-by-stage comparison; integer work bit-exact, floats by TOL."""
+def prune_decisions(idx, w_oracle, w_gpu, gpu_brim0, slot_expert, E, D, budget):
+    """Tokens whose pruning decision lies within the weights' rounding.
+
+    Pruning ranks a token's devices by the fp32 sum (pick order) of its
+    routing weights there.  The oracle's weights (fp64 softmax, one rounding)
+    and the GPU's (fp32 softmax) differ in the last bits, so where the
+    budget-th and the next device score differ by less than what those
+    differences can move a sum (delta = 2k * max |w_gpu - w_oracle| plus a
+    few fp32 ulps), either decision is correct.  Returns (near, delta): the
+    near-tie tokens, each certified here -- the GPU kept exactly `budget`
+    devices, none scoring (oracle weights) more than delta below the
+    oracle's budget-th score and none dropped more than delta above it."""
+    T, k = idx.shape
+    L = E // D
+    slot_of = np.empty(E, np.int64)
+    slot_of[np.asarray(slot_expert)] = np.arange(E)
+    dev = slot_of[idx] // L
+    maxdiff = float(np.max(np.abs(w_gpu.astype(np.float64) - w_oracle))) if T else 0.0
+    delta = 2 * k * maxdiff + 8 * k * float(np.finfo(np.float32).eps)
+    near = []
+    for t in range(T):
+        sc = {}
+        for j in range(k):  # fp32 sums in pick order, as the pruning rule states
+            dv = int(dev[t, j])
+            sc[dv] = np.float32(sc.get(dv, np.float32(0)) + np.float32(w_oracle[t, j]))
+        if len(sc) <= budget:
+            continue
+        order = sorted(sc, key=lambda dv: (-float(sc[dv]), dv))
+        sb, snext = float(sc[order[budget - 1]]), float(sc[order[budget]])
+        if sb - snext > delta:
+            continue
+        kept = {dv for dv in sc if gpu_brim0[dv, t] >= 0}
+        assert len(kept) == budget, (t, kept)
+        for dv in sc:
+            if dv in kept:
+                assert float(sc[dv]) >= sb - delta, (t, dv, sc, kept)
+            else:
+                assert float(sc[dv]) <= sb + delta, (t, dv, sc, kept)
+        near.append(t)
+    return np.array(near, dtype=np.int64), delta
+
+
+def compare(g, o, inp, full=True, pruned_w_exact=True):
+    """Stage-by-stage comparison; integer work bit-exact, floats by TOL.
+    pruned_w_exact: pruned layers' rescaled weights bit for bit (both sides
+    pruned from the same fp32 weights), else within the fp32 tolerance."""
     cfg = inp.cfg
     dt = cfg.dtype
     T, k, D, E = cfg.T, cfg.k, cfg.D, cfg.E
@@ -144,10 +188,12 @@ def compare(g, o, inp, full=True):
     assert np.array_equal(g["sfd_token"][:S], b["sfd_token"][:S]), "sfd_token"
     assert np.array_equal(g["epd_token"][:Rp], b["epd_token"]), "epd_token"
     assert np.array_equal(g["epd_sfd"][:Rp], b["epd_sfd"]), "epd_sfd"
-    if pruned:
+    if pruned and pruned_w_exact:
         # the same fp32 scores and rescaling on both sides: bit for bit
         assert np.array_equal(g["epd_w"][:Rp].view(np.uint32), b["epd_w"].view(np.uint32)), \
             "epd_w (pruned)"
+    elif pruned:
+        assert_close(g["epd_w"][:Rp], b["epd_w"], "f32", "epd_w (pruned, own weights)")
     else:
         # epd_w is a copy of the GPU's own routing weights
         assert np.array_equal(g["epd_w"], g["topk_w"].reshape(-1)[

@@ -147,6 +147,17 @@ def test_backward_arguments_are_checked(occ):
                                       FAKE, FAKE, hb, FAKE, FAKE, FAKE, ws - 1, FAKE, FAKE, FAKE,
                                       None)
     assert rc == -3
+    # [G | U] of T*k rows x 2I bf16 beyond 4 GiB (the backward GEMMs address
+    # it with 32-bit offsets), although every forward operand fits
+    wide = _desc(occ, T=65536, k=8, d=2048, E=64, D=8, I=3072)
+    assert lib.occ_expert_ffn(C.byref(wide), None, None, None, None, None, None, 0, None, None,
+                              None, None, None, None) == -1  # forward: passes the shape check
+    assert occ.occ_backward_workspace_bytes(wide) == 0
+    rc = lib.occ_expert_backward(C.byref(wide), FAKE, C.byref(brim), se.ctypes.data, FAKE, FAKE,
+                                 FAKE, hb, FAKE, FAKE, ws, FAKE, FAKE, FAKE, None)
+    assert rc == -2
+    assert lib.occ_grad_combine(C.byref(wide), FAKE, C.byref(brim), FAKE, None, FAKE, FAKE,
+                                None) == -2
     # a long batch splits dW_r over token chunks, whose partial sums need the workspace
     big = _desc(occ, T=8192)
     rc = lib.occ_router_backward(C.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, se.ctypes.data,

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from tests.gpu_common import compare, gpu_layer, oracle_layer, say
+from tests.gpu_common import compare, gpu_layer, oracle_layer, prune_decisions, say
 
 pytestmark = pytest.mark.gpu
 
@@ -118,6 +118,45 @@ def test_pruned_layer_parity(orc, name, budget, rescale):
     compare(g, o, inp)
 
 
+def _pruned_end_to_end(orc, cfg, inp, budget, rescale, tokens_of=None):
+    """The pruned layer with the oracle deciding from its own routing
+    weights.  Tokens whose decision lies within the weights' rounding are
+    certified (prune_decisions) and take the GPU's weights for the oracle's
+    decision; every other token is pruned from the oracle's softmax."""
+    g = gpu_layer(inp, budget=budget, rescale=rescale)
+    o0 = oracle_layer(orc, W.LayerInputs(cfg, inp.x, inp.w_router, None, None, None, None,
+                                         inp.slot_expert))
+    assert np.array_equal(g["topk_idx"], o0["idx"]), "topk_idx"
+    near, delta = prune_decisions(o0["idx"], o0["w"], g["topk_w"], g["brim0"], inp.slot_expert,
+                                  cfg.E, cfg.D, budget)
+    w_mix = o0["w"].copy()
+    w_mix[near] = g["topk_w"][near]
+    say(f"  {len(near)} of {cfg.T} tokens within delta={delta:.2e} of a tie: certified")
+    tok = None
+    if tokens_of is not None:
+        ob = oracle_layer(orc, W.LayerInputs(cfg, inp.x, inp.w_router, None, None, None, None,
+                                             inp.slot_expert), budget=budget, rescale=rescale,
+                          w_route=w_mix)
+        tok = tokens_of(ob["brim"])
+    o = oracle_layer(orc, inp, tokens=tok, budget=budget, rescale=rescale, w_route=w_mix)
+    assert o["brim"]["R"] < cfg.R  # pairs were dropped
+    compare(g, o, inp, full=tok is None, pruned_w_exact=False)
+    return o
+
+
+@pytest.mark.parametrize("name,budget,rescale", [
+    ("bf16_ragged", 1, 1), ("bf16_ragged", 2, 0), ("bf16_e128_pairs", 2, 1),
+    ("f32_e12", 1, 1), ("bf16_shared", 1, 1),
+])
+def test_pruned_layer_end_to_end(orc, name, budget, rescale):
+    """Collaboration pruning decided by the oracle from its own softmax
+    weights (not the GPU's): BRIMs bit for bit, weights and layer outputs
+    by tolerance; near-tie decisions certified."""
+    cfg = SMALL[name]
+    say(f"case pruned end to end {name} budget={budget} rescale={rescale}")
+    _pruned_end_to_end(orc, cfg, W.make_layer(cfg, seed=7), budget, rescale)
+
+
 def _two_layer_routing(orc, cfg, token_seed=None):
     """Oracle routing of a synthetic two-layer stack: the same clustered
     tokens through two independently drawn routers."""
@@ -210,3 +249,69 @@ def test_full_size_pruned_layer_parity(orc):
     o = oracle_layer(orc, inp, tokens=tok, budget=2, w_route=g["topk_w"])
     compare(g, o, inp, full=False)
     say(f"case full pruned: S={o['brim']['S']}, R'={o['brim']['R']} of T*k={cfg.R}")
+
+
+def test_full_size_pruned_layer_end_to_end(orc):
+    """The OLMoE-shaped layer under a budget of 2 of its 8 devices, pruned by
+    the oracle from its own softmax weights (near ties certified)."""
+    cfg = W.CONFIGS["olmoe_bf16"]
+    say("case full pruned end to end olmoe_bf16 budget=2: generating inputs")
+    inp = W.make_layer(cfg, seed=0)
+    o = _pruned_end_to_end(orc, cfg, inp, 2, 1, tokens_of=lambda b: _sample_tokens(cfg, b))
+    say(f"case full pruned end to end: S={o['brim']['S']}, R'={o['brim']['R']} of T*k={cfg.R}")
+
+
+def test_full_size_correlated_placement(orc):
+    """The DeepSeek-V2-Lite-shaped layer under correlated placement, run end
+    to end by the product: a calibration batch (token seed 1) through
+    occ_route_topk and occ_coactivation, occ_place_greedy on those counts,
+    then the layer on the seed-0 batch with that placement.  Counts and
+    placement bit for bit against the oracle's own chain; S, BRIMs and the
+    dispatch bit for bit, the outputs by tolerance; Y within tolerance of
+    the contiguous-placement run (placement moves no arithmetic but the
+    order of the per-device sums)."""
+    import torch
+    import expert_top_router_amd as occ
+    from expert_top_router_amd.layer import MoELayer, upload_inputs
+    from tests.gpu_common import oracle_logits_parallel
+    from tests.tolerance import assert_close
+    cfg = W.CONFIGS["dsv2lite_bf16"]
+    say("case correlated placement dsv2lite_bf16: calibration batch")
+    cal = W.make_layer(cfg, seed=0, token_seed=1, experts=False)
+    lay = MoELayer(cfg, upload_inputs(cal), cal.slot_expert)
+    lay.route()
+    lay.coactivation()
+    torch.cuda.synchronize()
+    counts = lay.host("counts")
+    del lay
+    se = occ.occ_place_greedy(cfg.E, cfg.D, counts)
+    idx_c, _ = orc.topk(oracle_logits_parallel(orc, cal.x, cal.w_router, cfg.dtype), cfg.k,
+                        cfg.renorm)
+    C_o = orc.coactivation(idx_c, cfg.E)
+    assert np.array_equal(counts, C_o), "calibration co-activation counts"
+    assert np.array_equal(se, orc.greedy_placement(C_o, cfg.D)), "greedy placement"
+    assert not np.array_equal(se, np.arange(cfg.E)), "the placement moved experts"
+    say("case correlated placement dsv2lite_bf16: layer with the greedy placement")
+    inp = W.make_layer(cfg, seed=0)
+    contiguous = inp.slot_expert.copy()
+    inp.slot_expert = np.asarray(se, dtype=np.int32)
+    o_route = oracle_layer(orc, W.LayerInputs(cfg, inp.x, inp.w_router, None, None, None, None,
+                                              inp.slot_expert))
+    tok = _sample_tokens(cfg, o_route["brim"])
+    o = oracle_layer(orc, inp, tokens=tok)
+    g = gpu_layer(inp)
+    compare(g, o, inp, full=False)
+    inp.slot_expert = contiguous
+    g_c = gpu_layer(inp)
+    S_c = int(g_c["S"][0])
+    b_c = orc.brim(o["idx"], o["w"], contiguous, cfg.E, cfg.D)
+    assert S_c == b_c["S"], "S under contiguous placement"
+    assert_close(W.to_f32(g["y"], cfg.dtype), W.to_f32(g_c["y"], cfg.dtype), cfg.dtype,
+                 "y (greedy vs contiguous placement)")
+    intra_g = orc.intra_share(C_o, se, cfg.D)
+    intra_c = orc.intra_share(C_o, contiguous, cfg.D)
+    say(f"case correlated placement: S/(T*k) greedy {o['brim']['S'] / cfg.R:.3f} "
+        f"({o['brim']['S']}), contiguous {S_c / cfg.R:.3f} ({S_c}); intra-device share of "
+        f"co-selections {intra_g[0] / max(intra_g[1], 1):.3f} vs "
+        f"{intra_c[0] / max(intra_c[1], 1):.3f}")
+    assert o["brim"]["S"] < S_c, "correlated placement sends fewer rows"

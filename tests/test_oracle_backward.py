@@ -178,3 +178,52 @@ def test_pruned_expert_gradients_match_finite_differences(orc, rescale):
     dl_all = ob.router_grads(lg, idx, w, 0, full_pick, np.arange(cfg.T))
     dropped_tokens = np.flatnonzero(np.any(ik < 0, axis=1))
     assert not np.allclose(dl[dropped_tokens], dl_all[dropped_tokens])
+
+
+def test_slot_weight_grads_pinned(orc):
+    """slot_weight_grads (the reference for the weight gradients of sampled
+    slots at full size) under a non-identity placement: for every slot it
+    equals the slice of full() for the slot's expert, and for two slots it
+    matches central finite differences of the plain fp64 layer in the
+    weights of that slot's expert (a slot/expert mix-up, a wrong row set or
+    a transposed product fails here)."""
+    ob = _ob()
+    cfg, inp = _layer(seed=7, T=40, d=16, E=8, I=12, k=3, D=4)
+    se = np.array([5, 2, 7, 0, 3, 6, 1, 4], dtype=np.int32)
+    x, wr, wgu, wdn = (np.asarray(a, np.float64) for a in (inp.x, inp.w_router, inp.w_gate_up,
+                                                           inp.w_down))
+    lg, idx, w = orc.route(inp.x, inp.w_router, cfg.k, 0, "f32")
+    b = orc.brim(idx, w, se, cfg.E, cfg.D)
+    rng = np.random.default_rng(8)
+    dy = rng.standard_normal(x.shape)
+    g = ob.full(x, wr, wgu, wdn, lg, idx, w, 0, b, se, dy, cfg.D, "f64")
+    counts = np.diff(b["slot_offset"])
+    for slot in range(cfg.E):
+        dgu, ddn = ob.slot_weight_grads(x, wgu, wdn, b, se, dy, slot, "f64")
+        e = se[slot]
+        assert np.allclose(dgu, g["dW_gate_up"][e], rtol=1e-12, atol=1e-12), slot
+        assert np.allclose(ddn, g["dW_down"][e], rtol=1e-12, atol=1e-12), slot
+        if counts[slot] == 0:
+            assert not dgu.any() and not ddn.any()
+
+    def loss(wgu_, wdn_):
+        return float(np.sum(dy * fwd64(x, wr, wgu_, wdn_, idx, 0)))
+
+    eps = 1e-6
+    busy = [int(s) for s in np.argsort(-counts, kind="stable")[:2]]
+    for slot in busy:
+        dgu, ddn = ob.slot_weight_grads(x, wgu, wdn, b, se, dy, slot, "f64")
+        e = int(se[slot])
+        for _ in range(5):
+            # a gate row, an up row, and a down entry of this slot's expert
+            for name, arr, grad in [("w_gate_up", wgu, dgu), ("w_down", wdn, ddn)]:
+                pos = tuple(int(rng.integers(0, s)) for s in arr.shape[1:])
+                plus, minus = arr.copy(), arr.copy()
+                plus[(e,) + pos] += eps
+                minus[(e,) + pos] -= eps
+                if name == "w_gate_up":
+                    fd = (loss(plus, wdn) - loss(minus, wdn)) / (2 * eps)
+                else:
+                    fd = (loss(wgu, plus) - loss(wgu, minus)) / (2 * eps)
+                assert abs(fd - grad[pos]) <= 1e-6 * max(1.0, abs(fd)), (slot, name, pos, fd,
+                                                                          grad[pos])
