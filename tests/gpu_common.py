@@ -8,7 +8,7 @@ import numpy as np
 
 import workloads as W
 from tests.checks import check_brim_invariants
-from tests.tolerance import TOL, assert_close
+from tests.tolerance import TOL, assert_close, assert_close_sum
 
 _POOL = cf.ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1)))
 
@@ -211,16 +211,51 @@ def compare(g, o, inp, full=True, pruned_w_exact=True):
     if "y" not in o:
         return
     rows = o["epd_rows"]
-    assert_close(as_f32(g["out_epd"][rows], dt), o["out_epd_rows"], dt, "out_epd")
+    g_rows = as_f32(g["out_epd"][rows], dt)
+    assert_close(g_rows, o["out_epd_rows"], dt, "out_epd")
     tok = o["tokens"]
+    g_sh = None
     if cfg.n_shared:
-        assert_close(as_f32(g["shared_out"][tok], dt), o["shared"], dt, "shared_out")
+        g_sh = as_f32(g["shared_out"][tok], dt)
+        assert_close(g_sh, o["shared"], dt, "shared_out")
     srows = np.unique(b["brim0"][:, tok][b["brim0"][:, tok] >= 0])
-    assert_close(as_f32(g["out_sfd"][srows], dt), o["out_sfd"][srows], dt, "out_sfd")
-    assert_close(as_f32(g["y"][tok], dt), o["y"], dt, "y")
+    # the combine's own arithmetic: the oracle's pre-reduction and scatter of
+    # the GPU's expert outputs
+    import oracle as orc
+    L = E // D
+    epd_row = np.full(max(Rp, 1), -1, np.int32)
+    epd_row[rows] = np.arange(rows.size, dtype=np.int32)
+    y_s, osfd_s = orc.combine(tok, b, T, D, L, cfg.d, dt, g_rows, epd_row, g_sh, want_sfd=True)
+    assert_close(as_f32(g["out_sfd"][srows], dt), osfd_s[srows], dt, "out_sfd (combine alone)")
+    assert_close(as_f32(g["y"][tok], dt), y_s, dt, "y (combine alone)")
+    # end to end, each element against the size of its summands
+    mag_sfd, mag_y = summand_magnitudes(o, b, srows, cfg.d)
+    assert_close_sum(as_f32(g["out_sfd"][srows], dt), o["out_sfd"][srows], mag_sfd, dt, "out_sfd")
+    assert_close_sum(as_f32(g["y"][tok], dt), o["y"], mag_y, dt, "y")
     if "y_direct" in g:
         assert np.array_equal(g["epd_direct"][:Rp], xs[b["epd_token"]]), "epd (direct dispatch)"
-        assert_close(as_f32(g["y_direct"][tok], dt), o["y_direct"], dt, "y (direct combine)")
+        yd_s = orc.combine_direct(tok, b, T, D, L, cfg.d, dt, g_rows, epd_row, g_sh)
+        assert_close(as_f32(g["y_direct"][tok], dt), yd_s, dt, "y (direct combine alone)")
+        assert_close_sum(as_f32(g["y_direct"][tok], dt), o["y_direct"], mag_y, dt,
+                         "y (direct combine)")
+
+
+def summand_magnitudes(o, b, srows, d):
+    """Per element: sum over an SFD row's EPD rows of |w * out_epd| (for the
+    rows srows), and over a token's EPD rows plus |shared_out| (for the
+    oracle's tokens), from the oracle's values."""
+    rows = o["epd_rows"]
+    term = (np.abs(o["out_epd_rows"].astype(np.float64))
+            * np.abs(b["epd_w"][rows].astype(np.float64))[:, None])
+    mag_sfd = np.zeros((len(srows), d))
+    pos_s = np.searchsorted(srows, b["epd_sfd"][rows])
+    np.add.at(mag_sfd, pos_s, term)
+    tok = o["tokens"]
+    mag_y = np.zeros((len(tok), d))
+    np.add.at(mag_y, np.searchsorted(tok, b["epd_token"][rows]), term)
+    if o.get("shared") is not None:
+        mag_y += np.abs(o["shared"].astype(np.float64))
+    return mag_sfd, mag_y
 
 
 def _flat_pos(idx, b, slot_expert, k):
