@@ -52,6 +52,7 @@ def _load(path: str = LIB_PATH):
         "occ_route_topk": (I32, [DP, P, P, P, P, P, P]),
         "occ_build_brim": (I32, [DP, P, P, P, BP, P, SZ, P]),
         "occ_build_brim_pruned": (I32, [DP, P, P, P, I32, I32, BP, P, SZ, P]),
+        "occ_build_brim_noalloc": (I32, [DP, P, P, P, BP, P]),
         "occ_dispatch": (I32, [DP, P, BP, P, P, P]),
         "occ_expert_ffn": (I32, [DP, P, BP, P, P, P, P, SZ, P, P, P, P, P, P]),
         "occ_expert_up": (I32, [DP, P, BP, P, P, P, SZ, P, P, P]),
@@ -84,7 +85,7 @@ _lib = _load()
 
 # Every symbol the C header declares (checked by the tests).
 EXPORTED = ("occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk", "occ_build_brim",
-            "occ_build_brim_pruned",
+            "occ_build_brim_pruned", "occ_build_brim_noalloc",
             "occ_dispatch", "occ_expert_ffn", "occ_expert_up", "occ_expert_down", "occ_combine",
             "occ_dispatch_direct", "occ_combine_direct", "occ_backward_workspace_bytes",
             "occ_grad_combine", "occ_expert_backward", "occ_router_backward",
@@ -165,6 +166,15 @@ def occ_build_brim(desc, topk_idx, topk_w, slot_expert_host, brim: occ_brim, ws,
     _check(_lib.occ_build_brim(C.byref(desc), _ptr(topk_idx), _ptr(topk_w), se.ctypes.data,
                                C.byref(brim), _ptr(ws), ws_bytes, _stream(stream)),
            "occ_build_brim")
+
+
+def occ_build_brim_noalloc(desc, topk_idx, topk_w, slot_expert_host, brim: occ_brim,
+                           stream=None):
+    import numpy as np
+    se = np.ascontiguousarray(slot_expert_host, dtype=np.int32)
+    _check(_lib.occ_build_brim_noalloc(C.byref(desc), _ptr(topk_idx), _ptr(topk_w),
+                                       se.ctypes.data, C.byref(brim), _stream(stream)),
+           "occ_build_brim_noalloc")
 
 
 def occ_build_brim_pruned(desc, topk_idx, topk_w, slot_expert_host, budget, rescale,
@@ -328,7 +338,7 @@ from .layer import MoELayer  # noqa: E402  (buffers + the call sequence)
 
 __all__ = ["MoELayer", "OccError", "occ_layer_desc", "occ_brim", "make_desc", "desc_of",
            "make_brim", "occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk",
-           "occ_build_brim", "occ_build_brim_pruned", "occ_dispatch", "occ_expert_ffn", "occ_expert_up",
+           "occ_build_brim", "occ_build_brim_noalloc", "occ_build_brim_pruned", "occ_dispatch", "occ_expert_ffn", "occ_expert_up",
            "occ_expert_down", "occ_combine", "occ_dispatch_direct", "occ_combine_direct",
            "occ_backward_workspace_bytes", "occ_grad_combine", "occ_expert_backward",
            "occ_router_backward", "occ_grad_dispatch", "occ_expert_ffn_keep",

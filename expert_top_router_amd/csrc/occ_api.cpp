@@ -175,6 +175,31 @@ occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *topk_idx,
                     ws_bytes, stream, OCC_MAX_D, 0);
 }
 
+occ_status occ_build_brim_noalloc(const occ_layer_desc *desc, const int32_t *topk_idx,
+                                  const float *topk_w, const int32_t *slot_expert_host,
+                                  const occ_brim *brim, hipStream_t stream) {
+  // the same checks as occ_build_brim, then the library's fixed array as
+  // the workspace; nothing is allocated
+  OCC_TRY(check_desc(desc));
+  OCC_TRY(check_brim(*desc, brim, true));
+  const int64_t Tk = (int64_t)desc->T * desc->k;
+  if (missing(topk_idx, Tk) || missing(topk_w, Tk))
+    return fail(OCC_EINVAL, "topk_idx and topk_w must be set");
+  occ::Placement pl;
+  OCC_TRY(make_placement(*desc, slot_expert_host, pl));
+  const size_t need = occ::brim_workspace_bytes(desc->T, desc->D, desc->E);
+  if (need > occ::kBrimScratchBytes)
+    return fail(OCC_EUNSUP, "occ_build_brim_noalloc: the layer needs %zu bytes of workspace, "
+                "more than the %zu of its fixed array (use occ_build_brim)", need,
+                occ::kBrimScratchBytes);
+  void *ws = nullptr;
+  const hipError_t e = occ::brim_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "occ_build_brim_noalloc (scratch address)");
+  return hip_status(occ::launch_build_brim(*desc, topk_idx, topk_w, pl, *brim, ws, stream,
+                                           OCC_MAX_D, 0),
+                    "occ_build_brim_noalloc");
+}
+
 occ_status occ_build_brim_pruned(const occ_layer_desc *desc, const int32_t *topk_idx,
                                  const float *topk_w, const int32_t *slot_expert_host,
                                  int32_t budget, int32_t rescale, const occ_brim *brim, void *ws,

@@ -24,6 +24,8 @@
 // the kept ones) so the token's total gate mass is unchanged.  Counting and
 // filling apply the same rule, so the layouts stay consistent, and EPD then
 // holds fewer than T*k rows (slot_offset[E]).
+#include <mutex>
+
 #include "occ_internal.h"
 
 namespace occ {
@@ -280,6 +282,35 @@ void launch_kmax(int T, int k, int D, int E, int L, int nblk, int ld, const int3
 }
 
 }  // namespace
+
+// Workspace of occ_build_brim_noalloc: one fixed device array per GPU, held
+// until the process ends.  In host code `scratch` is only a stand-in for the
+// symbol; its device address comes from hipGetSymbolAddress, once per device
+// (each GPU has its own copy at its own address).
+static __device__ __align__(256) int32_t scratch[kBrimScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];  // device address per device, null until queried
+}  // namespace
+
+hipError_t brim_scratch(void **ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t brim_workspace_bytes(int T, int D, int E) {
   return (brim_count_elems(T, D, E) + OCC_MAX_D + OCC_MAX_E) * sizeof(int32_t);

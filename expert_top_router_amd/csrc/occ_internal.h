@@ -81,6 +81,11 @@ hipError_t launch_route_topk(const occ_layer_desc &L, const void *x, const float
 size_t brim_workspace_bytes(int T, int D, int E);
 // budget >= D: the plain layouts; budget < D: collaboration pruning (at most
 // `budget` devices per token, kept weights rescaled when `rescale` is 1)
+// The fixed workspace of occ_build_brim_noalloc (per GPU) and its device
+// address on the current device (looked up once per device, then cached).
+constexpr size_t kBrimScratchBytes = OCC_NOALLOC_BRIM_SCRATCH_BYTES;
+static_assert(kBrimScratchBytes % 256 == 0, "whole 256-byte lines");
+hipError_t brim_scratch(void **ptr);
 hipError_t launch_build_brim(const occ_layer_desc &L, const int32_t *idx, const float *w,
                              const Placement &pl, const occ_brim &b, void *ws, hipStream_t st,
                              int budget, int rescale);

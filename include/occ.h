@@ -33,9 +33,10 @@
  *   - Arguments are validated on the host before anything is launched.  On
  *     an error nothing is launched and no output is touched; the return code
  *     says why and occ_last_error() gives the text.
- *   - The library holds no state besides the per-thread error text and the
- *     per-device compute-unit count it caches; calls on different streams
- *     are independent.
+ *   - The library holds no state besides the per-thread error text, the
+ *     per-device compute-unit count it caches and the fixed workspace of
+ *     occ_build_brim_noalloc; calls on different streams are independent
+ *     (except overlapping occ_build_brim_noalloc calls, see there).
  */
 #ifndef OCC_H
 #define OCC_H
@@ -134,6 +135,22 @@ occ_status occ_route_topk(const occ_layer_desc *desc, const void *x, const float
 occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *topk_idx,
                           const float *topk_w, const int32_t *slot_expert_host,
                           const occ_brim *brim, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* occ_build_brim for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments and outputs as occ_build_brim
+ * without ws / ws_bytes: the workspace is a fixed device array inside the
+ * library, OCC_NOALLOC_BRIM_SCRATCH_BYTES bytes on each GPU the library runs
+ * on (held until the process ends; its address is looked up once per
+ * device).  Nothing is allocated.  OCC_EUNSUP when occ_workspace_bytes(desc)
+ * exceeds that size (about 100 K tokens with D + E = 160 keys).  Every call
+ * on one GPU shares that array, so calls that overlap on one GPU (other
+ * streams or threads) race and must be serialised by the caller; a call
+ * fully overwrites what it reads, so nothing needs clearing between calls. */
+#define OCC_NOALLOC_BRIM_SCRATCH_BYTES (1u << 20)
+occ_status occ_build_brim_noalloc(const occ_layer_desc *desc, const int32_t *topk_idx,
+                                  const float *topk_w, const int32_t *slot_expert_host,
+                                  const occ_brim *brim, hipStream_t stream);
 
 /* BRIM build under an all-to-all budget: routing-score-based collaboration
  * pruning (Occult, TL;DR: pruning by routing score to minimise the budget

@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(occ):
     names = declared_symbols()
-    assert len(names) == 25, names
+    assert len(names) == 26, names
     lib = C.CDLL(occ.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -87,6 +87,36 @@ def test_null_pointers_and_workspace(occ):
     rc = lib.occ_build_brim(C.byref(d), FAKE, FAKE, se.ctypes.data, C.byref(partial), FAKE,
                             need, None)
     assert rc == -1
+
+
+def test_noalloc_brim_arguments_are_checked(occ):
+    """occ_build_brim_noalloc: occ_build_brim's checks, and layers whose
+    workspace exceeds the library's fixed array are refused (no launch)."""
+    lib = occ.lib()
+    brim = occ.make_brim(brim0=FAKE, brim1=FAKE, sfd_offset=FAKE, slot_offset=FAKE,
+                         sfd_token=FAKE, epd_token=FAKE, epd_sfd=FAKE, epd_w=FAKE, S=FAKE)
+    se = np.arange(8, dtype=np.int32)
+    d = _desc(occ)
+    assert lib.occ_build_brim_noalloc(None, FAKE, FAKE, se.ctypes.data, C.byref(brim), None) == -1
+    assert lib.occ_build_brim_noalloc(C.byref(d), None, FAKE, se.ctypes.data, C.byref(brim),
+                                      None) == -1
+    bad = np.array([0, 1, 2, 3, 4, 5, 6, 6], dtype=np.int32)
+    assert lib.occ_build_brim_noalloc(C.byref(d), FAKE, FAKE, bad.ctypes.data, C.byref(brim),
+                                      None) == -1
+    partial = occ.make_brim(brim0=FAKE, brim1=FAKE, slot_offset=FAKE)
+    assert lib.occ_build_brim_noalloc(C.byref(d), FAKE, FAKE, se.ctypes.data, C.byref(partial),
+                                      None) == -1
+    # 2^20 tokens with 16 devices and 128 experts: (16 + 128) keys x 16384
+    # blocks of counts, far beyond the 1 MiB array
+    big = _desc(occ, T=1 << 20, E=128, D=16, k=6)
+    assert occ.occ_workspace_bytes(big) > 1 << 20
+    se128 = np.arange(128, dtype=np.int32)
+    rc = lib.occ_build_brim_noalloc(C.byref(big), FAKE, FAKE, se128.ctypes.data, C.byref(brim),
+                                    None)
+    assert rc == -2 and "occ_build_brim" in occ.last_error()
+    # the largest workload of the suite (65536 tokens, 16 + 128 keys) fits
+    c5 = _desc(occ, T=65536, d=2048, E=128, D=16, k=6, I=768)
+    assert 0 < occ.occ_workspace_bytes(c5) <= 1 << 20
 
 
 def test_pruned_brim_arguments_are_checked(occ):
