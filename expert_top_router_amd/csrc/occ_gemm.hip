@@ -24,6 +24,7 @@
 // can also keep its pre-activations [G | U] (KEEP), staged and written the
 // same way before h, so the backward need not recompute them.
 #include <atomic>
+#include <type_traits>
 
 #include "occ_gemm_common.h"
 
@@ -124,18 +125,6 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
   asm volatile("" : "+v"(tid));
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave / NWN, wn = wave % NWN;
-  int a_dst[A_CH], b_dst[B_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + NT * i;
-    a_dst[i] = (c >> 3) * kLdsK + (c & 7) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + NT * i;
-    b_dst[i] = BM * kLdsK + (c >> 3) * kLdsK + (c & 7) * 8;
-  }
-
   f32x16 acc[MI][NI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -153,30 +142,39 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
     else
       brow[ni] = wn * WN + ni * 32;
   }
+  // LDS element offsets: one lane-dependent base for the stores of the
+  // staged chunks and one per operand for the fragment reads.  The chunk,
+  // fragment, k-step and stage parts are compile-time constants (the k loop
+  // is unrolled over the two stages), so each LDS access is a base register
+  // plus an immediate offset and the per-lane addresses take few registers.
+  const int w_base = (tid >> 3) * kLdsK + (tid & 7) * 8;  // chunk 0 of this thread
+  constexpr int W_CHUNK = (NT / 8) * kLdsK;               // chunk i: NT/8 * i rows on
   const int frag_r = lane & 31, frag_k = (lane >> 5) * 8;
-  int a_frag[MI], b_frag[NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) a_frag[mi] = (wm * WM + mi * 32 + frag_r) * kLdsK + frag_k;
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) b_frag[ni] = BM * kLdsK + (brow[ni] + frag_r) * kLdsK + frag_k;
+  const int a_rd = (wm * WM + frag_r) * kLdsK + frag_k;
+  const int b_rd = BM * kLdsK + ((SWIGLU ? wn * (WN / 2) : wn * WN) + frag_r) * kLdsK + frag_k;
+  constexpr auto a_fo = [](int mi) { return mi * 32 * kLdsK; };
+  constexpr auto b_fo = [](int ni) {
+    return (SWIGLU ? (ni < NI / 2 ? ni * 32 : BN / 2 + (ni - NI / 2) * 32) : ni * 32) * kLdsK;
+  };
 
 #define OCC_STORE_LDS(buf_, set_)                                                   \
   do {                                                                              \
-    uint16_t *s_ = smem + (buf_) * STAGE;                                           \
     _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                \
-        *reinterpret_cast<u32x4 *>(s_ + a_dst[i]) = ra[set_][i];                    \
+        *reinterpret_cast<u32x4 *>(smem + w_base + ((buf_) * STAGE + i * W_CHUNK)) = \
+            ra[set_][i];                                                            \
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                \
-        *reinterpret_cast<u32x4 *>(s_ + b_dst[i]) = rb[set_][i];                    \
+        *reinterpret_cast<u32x4 *>(smem + w_base +                                  \
+                                   ((buf_) * STAGE + BM * kLdsK + i * W_CHUNK)) =   \
+            rb[set_][i];                                                            \
   } while (0)
 
-  // nk % PF == 0 (the launcher picks PF so); loads past the last tile re-read
-  // the last tile (in bounds, L2-resident), which keeps the loop branch-free.
-  // Step kt multiplies tile kt from one LDS buffer while, during k steps
-  // 0..KSTEPS-2, it stores tile kt+1 (register set (u+1) % PF) into the other
-  // buffer and refills those registers with tile kt+1+PF (A and B chunks as
-  // one sequence, spread evenly).  The step's one barrier follows those
-  // stores, and the last k step's MFMAs then cover the LDS latency of tile
-  // kt+1's first fragments.
+  // Loads past the last k-tile re-read the last one (in bounds, L2-resident),
+  // which keeps the loop branch-free.  k-tile kt multiplies from LDS stage
+  // kt % 2 while, during k steps 0..KSTEPS-2, it stores k-tile kt+1 (staged
+  // in registers) into the other stage and refills those registers with
+  // k-tile kt+2 (A and B chunks as one sequence, spread evenly).  The k-tile's
+  // one barrier follows those stores, and the last k step's MFMAs then cover
+  // the LDS latency of k-tile kt+1's first fragments.
   constexpr int WSTEPS = KSTEPS - 1;
   constexpr int C_PER = (A_CH + B_CH + WSTEPS - 1) / WSTEPS;  // chunks per k step
   const int nk = a.K / kBK;
@@ -185,58 +183,71 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bf16_kernel(GemmArgs a) 
   OCC_LOAD_REGS(min(PF, nk - 1), 0);
   bf16x8v af[2][MI], bfr[2][NI];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) af[0][mi] = *reinterpret_cast<const bf16x8v *>(smem + a_frag[mi]);
+  for (int mi = 0; mi < MI; ++mi)
+    af[0][mi] = *reinterpret_cast<const bf16x8v *>(smem + a_rd + a_fo(mi));
 #pragma unroll
-  for (int ni = 0; ni < NI; ++ni) bfr[0][ni] = *reinterpret_cast<const bf16x8v *>(smem + b_frag[ni]);
+  for (int ni = 0; ni < NI; ++ni)
+    bfr[0][ni] = *reinterpret_cast<const bf16x8v *>(smem + b_rd + b_fo(ni));
   __builtin_amdgcn_sched_barrier(0);
-  for (int kb = 0; kb < nk; kb += PF) {
+  auto k_tile = [&](auto stage, int kt) {
+    constexpr int P = decltype(stage)::value;  // LDS stage of this k-tile
+    const int kn = min(kt + 1 + PF, nk - 1);    // k-tile refilled in this one
+    const int k0n = kn * kBK;
+    const int ksn = k0n / a.kseg;
+    const int64_t bkn = (int64_t)ksn * a.kseg_stride + (k0n - ksn * a.kseg);
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int kt = kb + u;
-      const uint16_t *S = smem + (kt & 1) * STAGE;
-      uint16_t *Wn = smem + ((kt + 1) & 1) * STAGE;
-      const int kn = min(kt + 1 + PF, nk - 1);  // tile refilled in this step
-      const int k0n = kn * kBK;
-      const int ksn = k0n / a.kseg;
-      const int64_t bkn = (int64_t)ksn * a.kseg_stride + (k0n - ksn * a.kseg);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int q = ks & 1;
+      // fragments of the next k step (of the next k-tile in the last step:
+      // after the barrier, from the other stage) while these multiply
+      const int fo = ks + 1 < KSTEPS ? P * STAGE + (ks + 1) * 16 : (1 - P) * STAGE;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int q = ks & 1;
-        // fragments of the next k step (of the next tile in the last step:
-        // after the barrier, from the other buffer) while these multiply
-        const uint16_t *Fs = ks + 1 < KSTEPS ? S + (ks + 1) * 16 : Wn;
+      for (int mi = 0; mi < MI; ++mi)
+        af[q ^ 1][mi] = *reinterpret_cast<const bf16x8v *>(smem + a_rd + (fo + a_fo(mi)));
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-          af[q ^ 1][mi] = *reinterpret_cast<const bf16x8v *>(Fs + a_frag[mi]);
+      for (int ni = 0; ni < NI; ++ni)
+        bfr[q ^ 1][ni] = *reinterpret_cast<const bf16x8v *>(smem + b_rd + (fo + b_fo(ni)));
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
-          bfr[q ^ 1][ni] = *reinterpret_cast<const bf16x8v *>(Fs + b_frag[ni]);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[q][ni], af[q][mi],
+                                                               acc[mi][ni], 0, 0, 0);
+      if (ks < WSTEPS) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[q][ni], af[q][mi],
-                                                                 acc[mi][ni], 0, 0, 0);
-        if (ks < WSTEPS) {
-#pragma unroll
-          for (int j = 0; j < C_PER; ++j) {
-            const int c = ks * C_PER + j;
-            if (c < A_CH) {
-              *reinterpret_cast<u32x4 *>(Wn + a_dst[c]) = ra[(u + 1) % PF][c];
-              ra[(u + 1) % PF][c] = __builtin_bit_cast(
-                  u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[c], k0n * 2, 0));
-            } else if (c < A_CH + B_CH) {
-              const int i = c - A_CH;
-              *reinterpret_cast<u32x4 *>(Wn + b_dst[i]) = rb[(u + 1) % PF][i];
-              rb[(u + 1) % PF][i] = __builtin_bit_cast(
-                  u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[i], (int)bkn * 2, 0));
-            }
+        for (int j = 0; j < C_PER; ++j) {
+          const int c = ks * C_PER + j;
+          if (c < A_CH) {
+            *reinterpret_cast<u32x4 *>(smem + w_base + ((1 - P) * STAGE + c * W_CHUNK)) =
+                ra[0][c];
+            ra[0][c] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[c], k0n * 2, 0));
+          } else if (c < A_CH + B_CH) {
+            const int i = c - A_CH;
+            *reinterpret_cast<u32x4 *>(smem + w_base +
+                                       ((1 - P) * STAGE + BM * kLdsK + i * W_CHUNK)) = rb[0][i];
+            rb[0][i] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[i], (int)bkn * 2, 0));
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks == WSTEPS - 1) __syncthreads();
       }
+      // issue order inside the k step: the next step's fragment reads first
+      // (so their latency hides under this step's MFMAs), two MFMAs, the
+      // staging stores and refill loads, then the remaining MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, MI + NI, 0);  // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);        // MFMA
+      if (ks < WSTEPS) {
+        __builtin_amdgcn_sched_group_barrier(0x200, C_PER, 0);  // DS writes
+        __builtin_amdgcn_sched_group_barrier(0x020, C_PER, 0);  // buffer loads
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - 2, 0);  // MFMA
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks == WSTEPS - 1) __syncthreads();
     }
+  };
+  for (int kb = 0; kb < nk; kb += 2) {
+    k_tile(std::integral_constant<int, 0>{}, kb);
+    if (kb + 1 < nk) k_tile(std::integral_constant<int, 1>{}, kb + 1);
   }
   const TileCoord cur = tc;
   if (logical + nbx < x1) {  // the next tile's first k-tile, during this epilogue
