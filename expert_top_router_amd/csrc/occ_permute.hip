@@ -119,7 +119,11 @@ template <> struct Chunk<OCC_F32> {
   static __device__ __forceinline__ float stored(float f) { return f; }
 };
 
-template <int DT, int NCH, bool PRE>
+// CSPLIT waves share a token, each owning a contiguous range of its row's
+// 16-byte chunks (the per-lane fp32 sums of a wide row would otherwise limit
+// the waves, hence the rows, in flight); each walks the token's BRIM entries
+// itself.
+template <int DT, int NCH, bool PRE, int CSPLIT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     int T, int D, int L, int ld, int row16, const u32x4 *__restrict__ out_epd,
     const int32_t *__restrict__ brim0, const int32_t *__restrict__ brim1,
@@ -128,13 +132,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   using CK = Chunk<DT>;
   constexpr int VE = CK::N;
   const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * kTokPerBlock + threadIdx.x / kWave;
+  const int gw = blockIdx.x * kTokPerBlock + threadIdx.x / kWave;
+  const int t = gw / CSPLIT, part = gw - t * CSPLIT;
   if (t >= T) return;
+  // this wave's chunks: [cb, ce) of the row
+  const int cb = part * row16 / CSPLIT, ce = (part + 1) * row16 / CSPLIT;
+  const int i0 = cb + lane;
   float yacc[NCH][VE], acc[NCH][VE];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int i = lane + kWave * c;
-    if (shared != nullptr && i < row16) {
+    const int i = i0 + kWave * c;
+    if (shared != nullptr && i < ce) {
       CK::unpack(shared[(size_t)t * row16 + i], yacc[c]);
     } else {
 #pragma unroll
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     }
     // an fp32 term (the backward's dx_router), first in the sum; loaded here
     // so that its latency overlaps the EPD row loads
-    if (add32 != nullptr && i < row16) {
+    if (add32 != nullptr && i < ce) {
       const float *ap = add32 + ((size_t)t * row16 + i) * VE;
 #pragma unroll
       for (int u = 0; u < VE; ++u) yacc[c][u] += ap[u];
@@ -156,14 +164,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     u32x4 *dst = out_sfd + (size_t)cur_s * row16;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int i = lane + kWave * c;
+      const int i = i0 + kWave * c;
 #pragma unroll
       for (int u = 0; u < VE; ++u) {
         const float v = CK::stored(acc[c][u]);
         acc[c][u] = v;
       }
       // the return payload is not read again by this step (non-temporal)
-      if (i < row16) __builtin_nontemporal_store(CK::pack(acc[c]), dst + i);
+      if (i < ce) __builtin_nontemporal_store(CK::pack(acc[c]), dst + i);
 #pragma unroll
       for (int u = 0; u < VE; ++u) {
         yacc[c][u] += acc[c][u];
@@ -201,14 +209,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
       u32x4 v[NCH];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const int i = lane + kWave * c;
-        if (i < row16) v[c] = srcp[i];
+        const int i = i0 + kWave * c;
+        if (i < ce) v[c] = srcp[i];
       }
       const float wb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(wr), b));
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const int i = lane + kWave * c;
-        if (i < row16) {
+        const int i = i0 + kWave * c;
+        if (i < ce) {
           float f[VE];
           CK::unpack(v[c], f);
 #pragma unroll
@@ -223,8 +231,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   if (PRE && cur_dev >= 0) finish_device();
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int i = lane + kWave * c;
-    if (i < row16) y[(size_t)t * row16 + i] = CK::pack(yacc[c]);
+    const int i = i0 + kWave * c;
+    if (i < ce) y[(size_t)t * row16 + i] = CK::pack(yacc[c]);
   }
 }
 
@@ -271,28 +279,29 @@ static hipError_t combine_dt(const occ_layer_desc &Ld, const void *out_epd, cons
   const int row16 = Ld.d * es / 16;
   const int L = Ld.E / Ld.D;
   const int ld = Ld.T * (Ld.k < Ld.D ? Ld.k : Ld.D);
-  const dim3 grid((Ld.T + kTokPerBlock - 1) / kTokPerBlock);
   const u32x4 *oe = static_cast<const u32x4 *>(out_epd);
   const u32x4 *sh = static_cast<const u32x4 *>(shared_out);
   u32x4 *os = static_cast<u32x4 *>(out_sfd);
   u32x4 *yp = static_cast<u32x4 *>(y);
+  // rows of more than 4 KiB go to two waves (4 chunks per lane each): the
+  // fp32 sums of 8 chunks per lane limit the waves in flight (d = 4096
+  // bf16: 0.52 of the HBM peak with one wave per token)
   const int nch = chunks_per_lane(row16);
-#define OCC_COMBINE(N)                                                                    \
+  const int split = nch > 4 ? 2 : 1;
+  const dim3 grid(((int64_t)Ld.T * split + kTokPerBlock - 1) / kTokPerBlock);
+#define OCC_COMBINE(N, CS)                                                                \
   do {                                                                                    \
     if (os != nullptr)                                                                    \
-      combine_kernel<DT, N, true><<<grid, kThreads, 0, st>>>(Ld.T, Ld.D, L, ld, row16, oe, \
-                                                             b.brim0, b.brim1, ew, sh, os, \
-                                                             yp, add32);                   \
+      combine_kernel<DT, N, true, CS><<<grid, kThreads, 0, st>>>(                         \
+          Ld.T, Ld.D, L, ld, row16, oe, b.brim0, b.brim1, ew, sh, os, yp, add32);         \
     else                                                                                  \
-      combine_kernel<DT, N, false><<<grid, kThreads, 0, st>>>(Ld.T, Ld.D, L, ld, row16,    \
-                                                              oe, b.brim0, b.brim1, ew,    \
-                                                              sh, os, yp, add32);          \
+      combine_kernel<DT, N, false, CS><<<grid, kThreads, 0, st>>>(                        \
+          Ld.T, Ld.D, L, ld, row16, oe, b.brim0, b.brim1, ew, sh, os, yp, add32);         \
   } while (0)
-  if (nch <= 1) OCC_COMBINE(1);
-  else if (nch <= 2) OCC_COMBINE(2);
-  else if (nch <= 4) OCC_COMBINE(4);
-  else if (nch <= 8) OCC_COMBINE(8);
-  else OCC_COMBINE(8);
+  if (nch <= 1) OCC_COMBINE(1, 1);
+  else if (nch <= 2) OCC_COMBINE(2, 1);
+  else if (nch <= 4) OCC_COMBINE(4, 1);
+  else OCC_COMBINE(4, 2);  // row16 <= 512 (rows of at most 8 KiB)
 #undef OCC_COMBINE
   return hipGetLastError();
 }
