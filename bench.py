@@ -241,14 +241,17 @@ def affinity(cfg, lay, torch):
             **us}
 
 
-BACKWARD_STAGES = ("grad_combine", "expert_backward", "router_backward", "grad_dispatch")
+BACKWARD_STAGES = ("grad_combine", "expert_backward", "router_backward", "shared_backward",
+                   "grad_dispatch")
 
 
 def backward(lay, cfg, steps, torch):
-    """Forward + backward step (bf16 layers without shared experts): the
-    backward walks the BRIMs in reverse (grad-combine, expert backward GEMMs,
-    router gradient, grad-dispatch) for a seeded upstream gradient.  Times K
-    whole steps, then each backward stage with events between stages."""
+    """Forward + backward step (bf16 layers): the backward walks the BRIMs in
+    reverse (grad-combine, expert backward GEMMs, router gradient, the shared
+    experts' backward when there are any, grad-dispatch) for a seeded
+    upstream gradient.  Times K whole steps, then each backward stage with
+    events between stages; without shared experts also the step that keeps
+    the experts' pre-activations."""
     lay.prepare_backward()
     g = torch.Generator(device="cuda")
     g.manual_seed(0)
@@ -286,23 +289,30 @@ def backward(lay, cfg, steps, torch):
     gc_bytes = (T + S + 2 * R) * d * b + 4.0 * R + 4.0 * cfg.D * T + 4.0 * (E // cfg.D) * S
     gd_bytes = (R + S + T) * d * b + 4.0 * T * d + 4.0 * cfg.D * T + 4.0 * (E // cfg.D) * S
     rb_flop = 4.0 * T * E * d
+    # shared experts: [G | U] 4, dh 2, dW_down 2, dW_gate_up 4, dx 4 (units of T d I_sh n_sh)
+    sh_flop = 16.0 * T * d * cfg.I_shared * cfg.n_shared
+    out = {"ms_per_step": elapsed / steps * 1e3, "tokens_per_s": T * steps / elapsed}
+    if cfg.n_shared == 0:
+        # the same step with the forward keeping [G | U] for the expert backward
+        def fwd_bwd_kept():
+            lay.forward_keep()
+            lay.backward_kept()
 
-    # the same step with the forward keeping [G | U] for the expert backward
-    def fwd_bwd_kept():
-        lay.forward_keep()
-        lay.backward_kept()
-
-    for _ in range(3):
-        fwd_bwd_kept()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        fwd_bwd_kept()
-    torch.cuda.synchronize()
-    kept = time.perf_counter() - t0
-    return {"ms_per_step": elapsed / steps * 1e3, "tokens_per_s": T * steps / elapsed,
-            "kept_gu_ms_per_step": kept / steps * 1e3,
-            "kept_gu_tokens_per_s": T * steps / kept,
+        for _ in range(3):
+            fwd_bwd_kept()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fwd_bwd_kept()
+        torch.cuda.synchronize()
+        kept = time.perf_counter() - t0
+        out.update(kept_gu_ms_per_step=kept / steps * 1e3,
+                   kept_gu_tokens_per_s=T * steps / kept)
+    else:
+        out.update(shared_backward_us=t["shared_backward"] * 1e6, shared_backward_flop=sh_flop,
+                   shared_backward_mfma_frac=sh_flop / t["shared_backward"] / 1e12
+                   / PEAK_BF16_TFLOPS)
+    return {**out,
             "grad_combine_us": t["grad_combine"] * 1e6,
             "grad_combine_hbm_frac": gc_bytes / t["grad_combine"] / 1e9 / PEAK_HBM_GBS,
             "expert_backward_us": t["expert_backward"] * 1e6,
@@ -519,9 +529,10 @@ def intra_share(counts, slot_expert, D):
     return float(c[same].sum()) / max(float(c.sum()), 1.0)
 
 
-def other_workload(name, steps, warmup, torch, placements=("contiguous",)):
+def other_workload(name, steps, warmup, torch, placements=("contiguous",), with_backward=False):
     """A secondary workload: whole-step time and per-stage times for each
-    placement (a fresh layer per placement, freed afterwards)."""
+    placement (a fresh layer per placement, freed afterwards); with_backward:
+    the forward + backward step as well (first placement)."""
     import workloads as W
     from expert_top_router_amd.layer import MoELayer, upload_inputs
     cfg = W.CONFIGS[name]
@@ -544,6 +555,8 @@ def other_workload(name, steps, warmup, torch, placements=("contiguous",)):
         rec.update({"ms_per_step": el / steps * 1e3, "tokens_per_s": cfg.T * steps / el,
                     "sfd_rows": S, "sfd_over_tk": S / max(cfg.R, 1),
                     "stages": stage_times(lay, cfg, max(5, min(steps, 20)), torch)})
+        if with_backward and pl == placements[0]:
+            rec["backward"] = backward(lay, cfg, steps, torch)
         out[pl] = rec
         del lay
         torch.cuda.empty_cache()
@@ -657,7 +670,7 @@ def main():
     if cfg.D >= 4:
         out["pruned"] = pruned(cfg, lay.w, inp.slot_expert, max(1, cfg.D // 4), args.steps, torch)
     out["affinity"] = affinity(cfg, lay, torch)
-    if cfg.dtype == "bf16" and cfg.n_shared == 0:
+    if cfg.dtype == "bf16":
         out["backward"] = backward(lay, cfg, args.steps, torch)
     if cfg.dtype == "bf16":
         out["calibration"] = dense_library_rate(cfg, torch)
@@ -669,7 +682,8 @@ def main():
             if name == cfg.name:
                 continue
             pls = ("contiguous", "greedy") if name == "dsv2lite_bf16" else ("contiguous",)
-            others[name] = other_workload(name, args.steps, args.warmup, torch, pls)
+            others[name] = other_workload(name, args.steps, args.warmup, torch, pls,
+                                          with_backward=name == "dsv2lite_bf16")
         out["workloads"] = others
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_route_tokens, args.cpu_sample_tokens)

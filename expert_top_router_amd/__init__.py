@@ -67,7 +67,8 @@ def _load(path: str = LIB_PATH):
         "occ_expert_ffn_keep": (I32, [DP, P, BP, P, P, P, P, SZ, P, P, P]),
         "occ_expert_backward_kept": (I32, [DP, P, BP, P, P, P, P, SZ, P, P, P, SZ, P, P, P, P]),
         "occ_router_backward": (I32, [DP, P, P, P, P, P, P, BP, P, P, P, P, P, SZ, P]),
-        "occ_grad_dispatch": (I32, [DP, P, BP, P, P, P, P]),
+        "occ_grad_dispatch": (I32, [DP, P, BP, P, P, P, P, P]),
+        "occ_shared_backward": (I32, [DP, P, P, P, P, SZ, P, P, SZ, P, P, P, P]),
         "occ_cross_coactivation": (I32, [I32, I32, I32, P, I32, I32, P, P, I32, P]),
         "occ_home_device": (I32, [I32, I32, I32, P, I32, I32, P, P, P, P]),
         "occ_local_hits": (I32, [I32, I32, I32, P, I32, P, P, P, I32, P]),
@@ -89,7 +90,7 @@ EXPORTED = ("occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk", 
             "occ_dispatch", "occ_expert_ffn", "occ_expert_up", "occ_expert_down", "occ_combine",
             "occ_dispatch_direct", "occ_combine_direct", "occ_backward_workspace_bytes",
             "occ_grad_combine", "occ_expert_backward", "occ_router_backward",
-            "occ_grad_dispatch", "occ_expert_ffn_keep", "occ_expert_backward_kept",
+            "occ_grad_dispatch", "occ_shared_backward", "occ_expert_ffn_keep", "occ_expert_backward_kept",
             "occ_coactivation",
             "occ_cross_coactivation", "occ_home_device", "occ_local_hits", "occ_place_greedy",
             "occ_last_error")
@@ -299,9 +300,19 @@ def occ_router_backward(desc, x, w_router, logits, topk_idx, topk_w, slot_expert
                                     _stream(stream)), "occ_router_backward")
 
 
-def occ_grad_dispatch(desc, d_epd, brim: occ_brim, dx_router, d_sfd, dx, stream=None):
+def occ_grad_dispatch(desc, d_epd, brim: occ_brim, dx_router, d_sfd, dx, stream=None,
+                      dx_shared=None):
     _check(_lib.occ_grad_dispatch(C.byref(desc), _ptr(d_epd), C.byref(brim), _ptr(dx_router),
-                                  _ptr(d_sfd), _ptr(dx), _stream(stream)), "occ_grad_dispatch")
+                                  _ptr(dx_shared), _ptr(d_sfd), _ptr(dx), _stream(stream)),
+           "occ_grad_dispatch")
+
+
+def occ_shared_backward(desc, x, w_gate_up_sh, w_down_sh, h_ws, h_ws_bytes, dy, bwd_ws,
+                        bwd_ws_bytes, dx_shared, dw_gate_up_sh, dw_down_sh, stream=None):
+    _check(_lib.occ_shared_backward(C.byref(desc), _ptr(x), _ptr(w_gate_up_sh), _ptr(w_down_sh),
+                                    _ptr(h_ws), h_ws_bytes, _ptr(dy), _ptr(bwd_ws), bwd_ws_bytes,
+                                    _ptr(dx_shared), _ptr(dw_gate_up_sh), _ptr(dw_down_sh),
+                                    _stream(stream)), "occ_shared_backward")
 
 
 def occ_cross_coactivation(T, k1, E1, idx1, k2, E2, idx2, counts, accumulate=0, stream=None):
@@ -341,6 +352,6 @@ __all__ = ["MoELayer", "OccError", "occ_layer_desc", "occ_brim", "make_desc", "d
            "occ_build_brim", "occ_build_brim_noalloc", "occ_build_brim_pruned", "occ_dispatch", "occ_expert_ffn", "occ_expert_up",
            "occ_expert_down", "occ_combine", "occ_dispatch_direct", "occ_combine_direct",
            "occ_backward_workspace_bytes", "occ_grad_combine", "occ_expert_backward",
-           "occ_router_backward", "occ_grad_dispatch", "occ_expert_ffn_keep",
+           "occ_router_backward", "occ_grad_dispatch", "occ_shared_backward", "occ_expert_ffn_keep",
            "occ_expert_backward_kept", "occ_coactivation", "occ_cross_coactivation", "occ_home_device", "occ_local_hits",
            "occ_place_greedy", "last_error"]

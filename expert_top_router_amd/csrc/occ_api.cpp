@@ -356,21 +356,34 @@ occ_status occ_coactivation(const occ_layer_desc *desc, const int32_t *topk_idx,
 static occ_status check_backward(const occ_layer_desc *desc) {
   OCC_TRY(check_desc(desc));
   if (desc->dtype != OCC_BF16) return fail(OCC_EUNSUP, "the backward pass is for bf16 layers");
-  if (desc->n_shared != 0) return fail(OCC_EUNSUP, "the backward pass has no shared experts");
-  // [G | U] and [dG | dU] (R x 2I bf16) are GEMM operands addressed with
-  // 32-bit byte offsets, like every operand check_desc bounds
-  if ((int64_t)desc->T * desc->k * 2 * desc->I * 2 > 0xffffffffll)
+  // [G | U] and [dG | dU] (R x 2I bf16, and T x n_shared 2 I_shared for the
+  // shared experts) are GEMM operands addressed with 32-bit byte offsets,
+  // like every operand check_desc bounds
+  if ((int64_t)desc->T * desc->k * 2 * desc->I * 2 > 0xffffffffll ||
+      (int64_t)desc->T * desc->n_shared * 2 * desc->I_shared * 2 > 0xffffffffll)
     return fail(OCC_EUNSUP, "the backward's [G | U] rows exceed 4 GiB");
+  return OCC_OK;
+}
+
+// The pair that keeps [G | U] runs the routed experts only.
+static occ_status check_keep(const occ_layer_desc *desc) {
+  OCC_TRY(check_backward(desc));
+  if (desc->n_shared != 0)
+    return fail(OCC_EUNSUP, "kept pre-activations are for layers without shared experts");
   return OCC_OK;
 }
 
 static size_t gu_bytes(const occ_layer_desc &L) {
   return align256((size_t)L.T * L.k * 2 * L.I * 2);
 }
+static size_t gu_sh_bytes(const occ_layer_desc &L) {
+  return align256((size_t)L.T * L.n_shared * 2 * L.I_shared * 2);
+}
 
 size_t occ_backward_workspace_bytes(const occ_layer_desc *desc) {
   if (check_backward(desc) != OCC_OK) return 0;
-  return std::max(2 * gu_bytes(*desc), occ::router_backward_ws_bytes(*desc));
+  return std::max(std::max(2 * gu_bytes(*desc), 2 * gu_sh_bytes(*desc)),
+                  occ::router_backward_ws_bytes(*desc));
 }
 
 occ_status occ_grad_combine(const occ_layer_desc *desc, const void *dy, const occ_brim *brim,
@@ -420,7 +433,7 @@ occ_status occ_expert_ffn_keep(const occ_layer_desc *desc, const void *epd, cons
                                const int32_t *slot_expert_host, const void *w_gate_up,
                                const void *w_down, void *h_ws, size_t h_ws_bytes, void *gu,
                                void *out_epd, hipStream_t stream) {
-  OCC_TRY(check_backward(desc));
+  OCC_TRY(check_keep(desc));
   OCC_TRY(check_brim(*desc, brim, false));
   const occ_layer_desc &L = *desc;
   const int64_t Rd = (int64_t)L.T * L.k * L.d;
@@ -446,7 +459,7 @@ occ_status occ_expert_backward_kept(const occ_layer_desc *desc, const void *epd,
                                     size_t h_ws_bytes, const void *gu, const void *d_out_epd,
                                     void *bwd_ws, size_t bwd_ws_bytes, void *d_epd,
                                     float *dw_gate_up, float *dw_down, hipStream_t stream) {
-  OCC_TRY(check_backward(desc));
+  OCC_TRY(check_keep(desc));
   OCC_TRY(check_brim(*desc, brim, false));
   const occ_layer_desc &L = *desc;
   const int64_t Rd = (int64_t)L.T * L.k * L.d;
@@ -495,14 +508,45 @@ occ_status occ_router_backward(const occ_layer_desc *desc, const void *x, const 
                     "occ_router_backward");
 }
 
+occ_status occ_shared_backward(const occ_layer_desc *desc, const void *x,
+                               const void *w_gate_up_sh, const void *w_down_sh, const void *h_ws,
+                               size_t h_ws_bytes, const void *dy, void *bwd_ws,
+                               size_t bwd_ws_bytes, void *dx_shared, float *dw_gate_up_sh,
+                               float *dw_down_sh, hipStream_t stream) {
+  OCC_TRY(check_backward(desc));
+  const occ_layer_desc &L = *desc;
+  if (L.n_shared == 0) return fail(OCC_EINVAL, "occ_shared_backward: the layer has no shared experts");
+  const int64_t Td = (int64_t)L.T * L.d;
+  if (missing(x, Td) || !w_gate_up_sh || !w_down_sh || missing(dy, Td) ||
+      missing(dx_shared, Td) || !dw_gate_up_sh || !dw_down_sh ||
+      missing(h_ws, (int64_t)(h_bytes(L) + h_sh_bytes(L))) ||
+      missing(bwd_ws, (int64_t)(2 * gu_sh_bytes(L))))
+    return fail(OCC_EINVAL, "shared backward: an operand is NULL");
+  if (h_ws_bytes < h_bytes(L) + h_sh_bytes(L))
+    return fail(OCC_ENOSPC, "h workspace of %zu bytes < %zu", h_ws_bytes,
+                h_bytes(L) + h_sh_bytes(L));
+  if (bwd_ws_bytes < 2 * gu_sh_bytes(L))
+    return fail(OCC_ENOSPC, "backward workspace of %zu bytes < %zu", bwd_ws_bytes,
+                2 * gu_sh_bytes(L));
+  char *ws = static_cast<char *>(bwd_ws);
+  const char *h = static_cast<const char *>(h_ws);
+  return hip_status(occ::launch_shared_backward(L, x, w_gate_up_sh, w_down_sh, h + h_bytes(L), dy,
+                                                ws, ws + gu_sh_bytes(L), dx_shared,
+                                                dw_gate_up_sh, dw_down_sh, stream),
+                    "occ_shared_backward");
+}
+
 occ_status occ_grad_dispatch(const occ_layer_desc *desc, const void *d_epd, const occ_brim *brim,
-                             const float *dx_router, void *d_sfd, void *dx, hipStream_t stream) {
+                             const float *dx_router, const void *dx_shared, void *d_sfd, void *dx,
+                             hipStream_t stream) {
   OCC_TRY(check_backward(desc));
   OCC_TRY(check_brim(*desc, brim, false));
   const int64_t Td = (int64_t)desc->T * desc->d;
   if (missing(d_epd, Td * desc->k) || missing(d_sfd, s_max(*desc)) || missing(dx, Td))
     return fail(OCC_EINVAL, "d_epd, d_sfd and dx must be set");
-  return hip_status(occ::launch_grad_dispatch(*desc, d_epd, *brim, dx_router, d_sfd, dx, stream),
+  OCC_TRY(check_shared_args(*desc, {dx_shared}, "dx_shared"));
+  return hip_status(occ::launch_grad_dispatch(*desc, d_epd, *brim, dx_router, dx_shared, d_sfd, dx,
+                                              stream),
                     "occ_grad_dispatch");
 }
 

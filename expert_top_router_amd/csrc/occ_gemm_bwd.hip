@@ -98,7 +98,9 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bwd_kernel(GemmArgs a) {
     // slot's row count.  Slots are ranked by rows (descending, lower slot on
     // ties) and dealt to the groups in snake order (0..nx-1, nx-1..0, ...):
     // the j-th slot of group x has rank nx j + (j even ? x : nx - 1 - x).
-    for (int g = threadIdx.x; g <= a.G; g += blockDim.x) ro[g] = a.row_offset[g];
+    // no row offsets: one group of dense_rows rows (the shared experts)
+    for (int g = threadIdx.x; g <= a.G; g += blockDim.x)
+      ro[g] = a.row_offset != nullptr ? a.row_offset[g] : (g == 0 ? 0 : a.dense_rows);
     __syncthreads();
     for (int g = threadIdx.x; g < a.G; g += blockDim.x) {
       const int rg = ro[g + 1] - ro[g];
@@ -110,10 +112,17 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bwd_kernel(GemmArgs a) {
       byrank[r] = g;
     }
     __syncthreads();
-    int nslot = 0;
-    for (int j = 0; nx * j + ((j & 1) ? nx - 1 - xcd : xcd) < a.G; ++j) ++nslot;
-    x0 = 0;
-    x1 = nslot * ntm * ntn;
+    if (a.row_offset != nullptr) {
+      int nslot = 0;
+      for (int j = 0; nx * j + ((j & 1) ? nx - 1 - xcd : xcd) < a.G; ++j) ++nslot;
+      x0 = 0;
+      x1 = nslot * ntm * ntn;
+    } else {
+      // one group: its tiles in contiguous ranges per XCD group
+      const int ntiles = ntm * ntn;
+      x0 = xcd * (ntiles / nx) + min(xcd, ntiles % nx);
+      x1 = x0 + ntiles / nx + (xcd < ntiles % nx ? 1 : 0);
+    }
   } else {
     // tiles in slot order, contiguous ranges per group
     const int ntiles = tile_table<BM, BN>(a, ts, ro);
@@ -130,8 +139,8 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bwd_kernel(GemmArgs a) {
   // tile: output rows [m0, m0 + mrows), columns [n0, ...), K rows [k_lo, k_hi)
   int group, m0, mrows, n0, k_lo, k_hi;
   if (GK) {
-    const int j = logical / (ntm * ntn);
-    group = byrank[nx * j + ((j & 1) ? nx - 1 - xcd : xcd)];
+    const int j = a.row_offset != nullptr ? logical / (ntm * ntn) : 0;
+    group = a.row_offset != nullptr ? byrank[nx * j + ((j & 1) ? nx - 1 - xcd : xcd)] : 0;
     const int rem = logical - j * ntm * ntn;
     const int nt = rem / ntm, mt = rem - nt * ntm;
     m0 = mt * BM;
@@ -326,6 +335,9 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bwd_kernel(GemmArgs a) {
   // ---- epilogue (lane l: output row l % 32, columns 8q + 4(l/32) + j) -------
   const int crow = lane & 31, ccol = (lane >> 5) * 4;
   if (EPI == EPI_F32) {
+    // nseg > 0: output column n is column n % nseg of the matrix at
+    // (n / nseg) * nseg_stride (a product over several matrices side by side;
+    // nseg is a multiple of 4, so a lane's run of 4 columns stays in one)
     float *Cg = static_cast<float *>(a.C) + (int64_t)expert * a.c_group_stride;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
@@ -335,8 +347,10 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bwd_kernel(GemmArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = wn * WN + ni * 32 + ccol + 8 * q;
-          if (row < mrows && n0 + col < a.N)
-            *reinterpret_cast<float4 *>(Cg + (int64_t)(m0 + row) * a.ldc + n0 + col) =
+          const int n = n0 + col;
+          const int64_t co = a.nseg > 0 ? (int64_t)(n / a.nseg) * a.nseg_stride + n % a.nseg : n;
+          if (row < mrows && n < a.N)
+            *reinterpret_cast<float4 *>(Cg + (int64_t)(m0 + row) * a.ldc + co) =
                 make_float4(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
                             acc[mi][ni][4 * q + 3]);
         }
@@ -529,4 +543,117 @@ hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_o
   a.ldc = d;
   return launch_bwd<0, 1, false, EPI_BF16, 4>(a, grouped_tiles((int)R, L.E, a.N), st);
 }
+
+// Backward of the shared experts (always active, weight 1, on the ORI rows
+// X): per shared expert s, on its own columns of the [T][n_sh * 2 I_sh]
+// buffers gu and dgu,
+//   [G | U]_s = X W_gate_up_sh[s]^T                      (recomputed, bf16)
+//   dh_s      = dY W_down_sh[s];  [dG | dU]_s by the SwiGLU backward (bf16)
+//   dW_down_sh[s]    = dY^T h_s            (fp32 [d][I_sh]; h_s: the forward's)
+//   dW_gate_up_sh[s] = [dG | dU]_s^T X     (fp32 [2 I_sh][d])
+// then dx_shared = [dG | dU] W_gate_up_sh as one product over K = n_sh * 2 I_sh
+// (bf16 [T][d]): the sum over the shared experts of their input gradients.
+hipError_t launch_shared_backward(const occ_layer_desc &L, const void *x, const void *w_gate_up_sh,
+                                  const void *w_down_sh, const void *h_sh, const void *dy,
+                                  void *gu, void *dgu, void *dx_shared, float *dw_gate_up_sh,
+                                  float *dw_down_sh, hipStream_t st) {
+  // (T = 0: the products over no rows launch no tiles; the weight gradients,
+  // sums over no rows, are written as zeros)
+  const int64_t T = L.T, d = L.d, Is = L.I_shared, ns = L.n_shared, W2 = ns * 2 * Is;
+  const uint16_t *wdn = static_cast<const uint16_t *>(w_down_sh);
+  uint16_t *gub = static_cast<uint16_t *>(gu);
+  uint16_t *dgub = static_cast<uint16_t *>(dgu);
+  hipError_t err;
+  const Placement none{};
+  auto dense = [&]() {
+    GemmArgs a = base_args(none);
+    a.row_offset = nullptr;
+    a.G = 1;
+    a.dense_rows = (int)T;
+    return a;
+  };
+  // 1. [G | U] of every shared expert: X times the stacked W_gate_up_sh
+  //    ([n_sh 2 I_sh][d]), one product
+  GemmArgs a = dense();
+  a.A = x;
+  a.lda = d;
+  a.a_bytes = T * d * 2;
+  a.B = w_gate_up_sh;
+  a.ldb = d;
+  a.b_bytes = W2 * d * 2;
+  a.K = (int)d;
+  a.N = (int)W2;
+  a.C = gub;
+  a.ldc = W2;
+  if ((err = launch_bwd<0, 0, false, EPI_BF16, 4>(a, grouped_tiles((int)T, 1, a.N), st)) !=
+      hipSuccess)
+    return err;
+  // 2. per shared expert: dh_s = dY W_down_sh[s] ([d][I_sh]); SwiGLU backward
+  //    into its [dG | dU] columns
+  for (int64_t s = 0; s < ns; ++s) {
+    a = dense();
+    a.A = dy;
+    a.lda = d;
+    a.a_bytes = T * d * 2;
+    a.B = wdn + s * d * Is;
+    a.ldb = Is;
+    a.b_bytes = d * Is * 2;
+    a.K = (int)d;
+    a.N = (int)Is;
+    a.aux = gub + s * 2 * Is;
+    a.ldaux = W2;
+    a.C = dgub + s * 2 * Is;
+    a.ldc = W2;
+    if ((err = launch_bwd<0, 1, false, EPI_SWIGLU_BWD, 4>(a, grouped_tiles((int)T, 1, a.N), st)) !=
+        hipSuccess)
+      return err;
+  }
+  // 3. dW_down_sh[s] = dY^T h_s for every s at once: output columns of the
+  //    [d][n_sh I_sh] product go to matrix s = column / I_sh (K: the T rows)
+  a = dense();
+  a.A = dy;
+  a.lda = d;
+  a.a_bytes = T * d * 2;
+  a.M = (int)d;
+  a.B = h_sh;
+  a.ldb = ns * Is;
+  a.b_bytes = T * ns * Is * 2;
+  a.N = (int)(ns * Is);
+  a.nseg = (int)Is;
+  a.nseg_stride = d * Is;
+  a.C = dw_down_sh;
+  a.ldc = Is;
+  if ((err = launch_bwd<1, 1, true, EPI_F32, 2>(a, ((d + 255) / 256) * ((a.N + 255) / 256), st)) !=
+      hipSuccess)
+    return err;
+  // 4. dW_gate_up_sh = [dG | dU]^T X, the stacked [n_sh 2 I_sh][d] at once
+  a = dense();
+  a.A = dgub;
+  a.lda = W2;
+  a.a_bytes = T * W2 * 2;
+  a.M = (int)W2;
+  a.B = x;
+  a.ldb = d;
+  a.b_bytes = T * d * 2;
+  a.N = (int)d;
+  a.C = dw_gate_up_sh;
+  a.ldc = d;
+  if ((err = launch_bwd<1, 1, true, EPI_F32, 2>(a, ((W2 + 255) / 256) * ((d + 255) / 256), st)) !=
+      hipSuccess)
+    return err;
+  // 5. dx_shared = [dG | dU] W_gate_up_sh over all shared experts at once
+  a = dense();
+  a.A = dgub;
+  a.lda = W2;
+  a.a_bytes = T * W2 * 2;
+  a.B = w_gate_up_sh;
+  a.ldb = d;
+  a.b_bytes = W2 * d * 2;
+  a.K = (int)W2;
+  a.N = (int)d;
+  a.C = dx_shared;
+  a.ldc = d;
+  return launch_bwd<0, 1, false, EPI_BF16, 4>(a, grouped_tiles((int)T, 1, a.N), st);
+}
+
 }  // namespace occ

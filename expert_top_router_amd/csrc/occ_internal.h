@@ -101,7 +101,8 @@ hipError_t launch_grad_combine(const occ_layer_desc &L, const void *dy, const oc
                                const void *out_epd, void *d_out_sfd, void *d_out_epd, float *dw,
                                hipStream_t st);
 hipError_t launch_grad_dispatch(const occ_layer_desc &L, const void *d_epd, const occ_brim &b,
-                                const float *add32, void *d_sfd, void *dx, hipStream_t st);
+                                const float *add32, const void *dx_shared, void *d_sfd, void *dx,
+                                hipStream_t st);
 hipError_t launch_router_backward(const occ_layer_desc &L, const Placement &pl, const void *x,
                                   const float *w_router, const float *logits,
                                   const int32_t *idx, const float *topk_w, const occ_brim &b,
@@ -136,6 +137,12 @@ hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_o
                                   const void *w_down, const void *h, const void *d_out_epd,
                                   void *gu, void *dgu, void *d_epd, float *dw_gate_up,
                                   float *dw_down, hipStream_t st, bool recompute_gu = true);
+// Shared experts' backward (bf16): gu and dgu are [T][n_sh * 2 I_sh] bf16
+// workspaces; h_sh the forward's shared activations [T][n_sh * I_sh].
+hipError_t launch_shared_backward(const occ_layer_desc &L, const void *x, const void *w_gate_up_sh,
+                                  const void *w_down_sh, const void *h_sh, const void *dy,
+                                  void *gu, void *dgu, void *dx_shared, float *dw_gate_up_sh,
+                                  float *dw_down_sh, hipStream_t st);
 // gu: when set (bf16 layers without shared experts), the [G | U] rows are
 // also written (bf16 [R][2I])
 hipError_t launch_expert_up(const occ_layer_desc &L, const void *epd, const int32_t *slot_offset,

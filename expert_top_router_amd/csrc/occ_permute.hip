@@ -316,13 +316,15 @@ hipError_t launch_combine(const occ_layer_desc &Ld, const void *out_epd, const o
 }
 
 // Gradient of the dispatch (the same walk, unit weights): d_sfd[s] = sum over
-// l of d_epd[r], dx[t] = add32[t] (fp32) + sum over devices of d_sfd[s].
+// l of d_epd[r], dx[t] = dx_shared[t] (stored rows, may be null) + add32[t]
+// (fp32, may be null) + sum over devices of d_sfd[s].
 hipError_t launch_grad_dispatch(const occ_layer_desc &Ld, const void *d_epd, const occ_brim &b,
-                                const float *add32, void *d_sfd, void *dx, hipStream_t st) {
+                                const float *add32, const void *dx_shared, void *d_sfd, void *dx,
+                                hipStream_t st) {
   if (Ld.T == 0) return hipSuccess;
   return Ld.dtype == OCC_F32
-             ? combine_dt<OCC_F32>(Ld, d_epd, b, nullptr, d_sfd, dx, st, nullptr, add32)
-             : combine_dt<OCC_BF16>(Ld, d_epd, b, nullptr, d_sfd, dx, st, nullptr, add32);
+             ? combine_dt<OCC_F32>(Ld, d_epd, b, dx_shared, d_sfd, dx, st, nullptr, add32)
+             : combine_dt<OCC_BF16>(Ld, d_epd, b, dx_shared, d_sfd, dx, st, nullptr, add32);
 }
 
 }  // namespace occ

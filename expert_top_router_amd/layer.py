@@ -15,7 +15,7 @@ import numpy as np
 from . import (desc_of, make_brim, occ_backward_workspace_bytes, occ_build_brim,
                occ_build_brim_pruned, occ_coactivation, occ_combine, occ_expert_backward,
                occ_expert_backward_kept, occ_expert_ffn_keep,
-               occ_grad_combine, occ_grad_dispatch, occ_router_backward,
+               occ_grad_combine, occ_grad_dispatch, occ_router_backward, occ_shared_backward,
                occ_combine_direct, occ_dispatch, occ_dispatch_direct, occ_expert_down,
                occ_expert_ffn, occ_expert_up, occ_ffn_workspace_bytes, occ_route_topk,
                occ_workspace_bytes)
@@ -174,7 +174,7 @@ class MoELayer:
         self.expert_ffn(stream)
         self.combine_direct(stream)
 
-    # ---- backward (bf16, no shared experts) -------------------------------
+    # ---- backward (bf16) -----------------------------------------------------
     def _grad_buffers(self):
         if getattr(self, "dy", None) is not None:
             return
@@ -206,6 +206,12 @@ class MoELayer:
         self.d_sfd = buf((S_max, d), el)
         self.dx = buf((T, d), el)
         self.gu = buf((R, 2 * cfg.I), el)  # kept [G | U] (forward_keep)
+        if cfg.n_shared:
+            self.dx_shared = buf((T, d), el)
+            self.dw_gate_up_sh = buf((cfg.n_shared, 2 * cfg.I_shared, d), f32)
+            self.dw_down_sh = buf((cfg.n_shared, d, cfg.I_shared), f32)
+        else:
+            self.dx_shared = self.dw_gate_up_sh = self.dw_down_sh = None
 
     def grad_combine(self, stream=None):
         occ_grad_combine(self.desc, self.dy, self.brim, self.out_epd, self.d_out_sfd,
@@ -255,9 +261,16 @@ class MoELayer:
                             self.topk_w, self.slot_expert, self.brim, self.dw_epd, self.dlogits,
                             self.dx_router, self.dw_router, self.bwd_ws, self.bwd_bytes, stream)
 
+    def shared_backward(self, stream=None):
+        """The shared experts' gradients (layers with shared experts)."""
+        if self.cfg.n_shared:
+            occ_shared_backward(self.desc, self.w.x, self.w.w_gate_up_sh, self.w.w_down_sh,
+                                self.h_ws, self.h_bytes, self.dy, self.bwd_ws, self.bwd_bytes,
+                                self.dx_shared, self.dw_gate_up_sh, self.dw_down_sh, stream)
+
     def grad_dispatch(self, stream=None):
         occ_grad_dispatch(self.desc, self.d_epd, self.brim, self.dx_router, self.d_sfd, self.dx,
-                          stream)
+                          stream, dx_shared=self.dx_shared)
 
     def backward(self, dy=None, stream=None):
         """Gradients of the last forward (which must have kept its logits:
@@ -270,6 +283,7 @@ class MoELayer:
         self.grad_combine(stream)
         self.expert_backward(stream)
         self.router_backward(stream)
+        self.shared_backward(stream)
         self.grad_dispatch(stream)
 
     def _require_logits(self):

@@ -238,14 +238,15 @@ occ_status occ_combine_direct(const occ_layer_desc *desc, const void *out_epd, c
 occ_status occ_coactivation(const occ_layer_desc *desc, const int32_t *topk_idx,
                             int32_t *counts, int32_t accumulate, hipStream_t stream);
 
-/* ---- Backward pass through the BRIMs (bf16 layers without shared experts;
- * EUNSUP otherwise).  Expert Coupling in MoE Pretraining, Abstract: every
- * MoE layer runs its all-to-alls in the forward and the backward pass;
- * Occult, Figure 4 caption: the moves between ORI, SFD and EPD are guided by
- * the BRIMs, walked here in the opposite direction.  Call order after a
- * forward (occ_route_topk with logits, occ_build_brim, occ_dispatch,
- * occ_expert_ffn, occ_combine): occ_grad_combine, occ_expert_backward,
- * occ_router_backward, occ_grad_dispatch.  Top-k selection is a constant. */
+/* ---- Backward pass through the BRIMs (bf16 layers; EUNSUP for fp32).
+ * Expert Coupling in MoE Pretraining, Abstract: every MoE layer runs its
+ * all-to-alls in the forward and the backward pass; Occult, Figure 4
+ * caption: the moves between ORI, SFD and EPD are guided by the BRIMs,
+ * walked here in the opposite direction.  Call order after a forward
+ * (occ_route_topk with logits, occ_build_brim, occ_dispatch, occ_expert_ffn,
+ * occ_combine): occ_grad_combine, occ_expert_backward, occ_router_backward,
+ * (with shared experts) occ_shared_backward, occ_grad_dispatch.  Top-k
+ * selection is a constant. */
 
 /* Bytes of the workspace of occ_expert_backward and occ_router_backward
  * (one buffer may serve both calls in turn; 0 for an invalid or unsupported
@@ -323,14 +324,36 @@ occ_status occ_router_backward(const occ_layer_desc *desc, const void *x, const 
                                float *dx_router, float *dw_router, void *bwd_ws,
                                size_t bwd_ws_bytes, hipStream_t stream);
 
+/* Gradient of the shared experts (always active, weight 1, on the ORI rows;
+ * layers with n_shared > 0, EINVAL otherwise).  For shared expert s, with
+ * X the layer's tokens and dY the layer's output gradient:
+ *   [G | U]_s = X W_gate_up_sh[s]^T recomputed (bf16, in bwd_ws)
+ *   dh_s = dY W_down_sh[s];  dG_s = dh U silu'(G), dU_s = dh silu(G)
+ *             (bf16, in bwd_ws)
+ *   dw_gate_up_sh[s] = [dG | dU]_s^T X     (fp32 [n_shared][2 I_shared][d], written)
+ *   dw_down_sh[s]    = dY^T h_s            (fp32 [n_shared][d][I_shared], written;
+ *                                           h_s: the forward's, from h_ws)
+ *   dx_shared = sum over s of [dG | dU]_s W_gate_up_sh[s]
+ *                                          (bf16 [T][d]; for occ_grad_dispatch)
+ * x, w_gate_up_sh, w_down_sh as given to occ_expert_ffn; h_ws its workspace;
+ * dy bf16 [T][d]; bwd_ws of occ_backward_workspace_bytes(desc) bytes. */
+occ_status occ_shared_backward(const occ_layer_desc *desc, const void *x,
+                               const void *w_gate_up_sh, const void *w_down_sh, const void *h_ws,
+                               size_t h_ws_bytes, const void *dy, void *bwd_ws,
+                               size_t bwd_ws_bytes, void *dx_shared, float *dw_gate_up_sh,
+                               float *dw_down_sh, hipStream_t stream);
+
 /* Gradient of the dispatch (the combine's walk with unit weights):
  *   d_sfd[s] = sum over l ascending with r = brim1[l][s] >= 0 of d_epd[r]
  *              (bf16 [S_max][d], rows < S: the backward return payload)
- *   dx[t]    = dx_router[t] + sum over devices of d_sfd[brim0[dv][t]]
+ *   dx[t]    = dx_shared[t] + dx_router[t] + sum over devices of
+ *              d_sfd[brim0[dv][t]]
  *              (bf16 [T][d]; fp32 accumulation, one rounding; dx_router may
- *              be NULL) */
+ *              be NULL; dx_shared, from occ_shared_backward, must be set when
+ *              n_shared > 0 and NULL otherwise) */
 occ_status occ_grad_dispatch(const occ_layer_desc *desc, const void *d_epd, const occ_brim *brim,
-                             const float *dx_router, void *d_sfd, void *dx, hipStream_t stream);
+                             const float *dx_router, const void *dx_shared, void *d_sfd, void *dx,
+                             hipStream_t stream);
 
 /* Cross-layer co-activation (Expert Coupling in MoE Pretraining, Abstract:
  * the experts a token selects at one layer predict those it selects at the

@@ -15,7 +15,11 @@ the oracle's own rounding) at the points where the layer stores a tensor:
                  d_epd = round(dG W_g + dU W_u)
                  dW_g = dG^T EPD,  dW_u = dU^T EPD,  dW_d = d_out_epd^T h
   grad-dispatch  d_sfd[s] = round(sum over the SFD row's EPD rows of d_epd)
-                 dx[t] = round(dx_router[t] + sum over its SFD rows of d_sfd)
+                 dx[t] = round(dx_router[t] + dx_shared[t] + sum over its SFD rows
+                 of d_sfd)
+  shared experts G, U = round(X W_g^T), round(X W_u^T); dh = dY W_d (weight 1);
+                 dG, dU as above; dx_shared = round(sum over them of dG W_g + dU W_u);
+                 dW_g = dG^T X, dW_u = dU^T X, dW_d = dY^T h
   router         dp from dw (through the renormalisation), then
                  dlogit = p (dp - <p, dp>);  dx_router = dlogit W_r,
                  dW_r = dlogit^T X
@@ -118,13 +122,85 @@ def slot_weight_grads(x, wgu, wdn, b, slot_expert, dy, g, dtype):
     return dWgu, dWd
 
 
-def grad_dispatch(b, d_epd_of, tokens, T, D, L, d, dtype, dx_router=None):
+def shared_backward(x, wgu_sh, wdn_sh, dy, tokens, dtype):
+    """Backward of the shared experts (always active, weight 1, on the ORI
+    rows; their outputs enter Y unweighted) for the ORI rows ``tokens``.
+    Per shared expert s, with the forward's pre-activations a = X Wg^T and
+    b = X Wu^T (fp64) and its stored h = round(silu(a) b):
+        G, U  = round(a), round(b)              (recomputed, stored)
+        dh    = dY Wd[s]                         (the shared output's gradient is dY)
+        dG    = round(dh U silu'(G)),  dU = round(dh G sigmoid(G))
+        dW_gate_up_sh[s] = [dG | dU]^T X,  dW_down_sh[s] = dY^T h
+    and dx_shared = round(sum over s of dG Wg[s] + dU Wu[s]).  Returns
+    dx_shared [n][d], the per-expert G, U, dG, dU, h ([n_sh][n][I_sh]) and the
+    weight gradients summed over the given rows (the exact ones when tokens
+    covers every row)."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    X = _f64(x, dtype)[tokens]
+    Wgu = _f64(wgu_sh, dtype)
+    Wd = _f64(wdn_sh, dtype)
+    n_sh, two_i, d = Wgu.shape
+    Is = two_i // 2
+    g_dy = _f64(dy, dtype)[tokens]
+    out = {k_: np.empty((n_sh, len(tokens), Is)) for k_ in ("G", "U", "dG", "dU", "h")}
+    dxs = np.zeros((len(tokens), d))
+    dWgu = np.zeros((n_sh, two_i, d))
+    dWd = np.zeros((n_sh, d, Is))
+    for sg in range(n_sh):
+        a = X @ Wgu[sg, :Is].T
+        bu = X @ Wgu[sg, Is:].T
+        h = round_array(_silu(a) * bu, dtype)
+        G = round_array(a, dtype)
+        U = round_array(bu, dtype)
+        dh = g_dy @ Wd[sg]
+        sig = 1.0 / (1.0 + np.exp(-G))
+        dG = round_array(dh * U * sig * (1.0 + G * (1.0 - sig)), dtype)
+        dU = round_array(dh * G * sig, dtype)
+        dxs += dG @ Wgu[sg, :Is] + dU @ Wgu[sg, Is:]
+        dWgu[sg] = np.concatenate([dG.T @ X, dU.T @ X], axis=0)
+        dWd[sg] = g_dy.T @ h
+        for k_, v in (("G", G), ("U", U), ("dG", dG), ("dU", dU), ("h", h)):
+            out[k_][sg] = v
+    out.update(dx_shared=round_array(dxs, dtype), dW_gate_up_sh=dWgu, dW_down_sh=dWd)
+    return out
+
+
+def shared_weight_grad_columns(x, wgu_sh, wdn_sh, dy, s, cols, dtype):
+    """The shared expert s's weight gradients at the intermediate columns
+    ``cols`` (every ORI row): the gate rows dW_gate_up_sh[s][cols], the up
+    rows dW_gate_up_sh[s][I_sh + cols] and the columns dW_down_sh[s][:, cols].
+    Each intermediate column's G, U, dh, dG, dU and h depend on that column
+    alone, so this is shared_backward's formula restricted to those columns.
+    Returns (gate rows [n][d], up rows [n][d], down columns [d][n])."""
+    cols = np.asarray(cols, dtype=np.int64)
+    X = _f64(x, dtype)
+    Wgu = _f64(wgu_sh, dtype)[s]
+    Wd = _f64(wdn_sh, dtype)[s]
+    Is = Wgu.shape[0] // 2
+    g_dy = _f64(dy, dtype)
+    a = X @ Wgu[cols].T
+    bu = X @ Wgu[Is + cols].T
+    h = round_array(_silu(a) * bu, dtype)
+    G = round_array(a, dtype)
+    U = round_array(bu, dtype)
+    dh = g_dy @ Wd[:, cols]
+    sig = 1.0 / (1.0 + np.exp(-G))
+    dG = round_array(dh * U * sig * (1.0 + G * (1.0 - sig)), dtype)
+    dU = round_array(dh * G * sig, dtype)
+    return dG.T @ X, dU.T @ X, g_dy.T @ h
+
+
+def grad_dispatch(b, d_epd_of, tokens, T, D, L, d, dtype, dx_router=None, dx_shared=None):
     """d_sfd for the tokens' SFD rows and dx for the tokens; d_epd_of maps an
-    EPD row to its d_epd (fp64 [d]).  Returns (dx [n][d], {s: d_sfd[s]})."""
+    EPD row to its d_epd (fp64 [d]); dx_router (fp32) and dx_shared (the
+    shared experts' stored input gradient) are rows of the tokens, added into
+    dx with the SFD rows.  Returns (dx [n][d], {s: d_sfd[s]})."""
     dx = np.zeros((len(tokens), d))
     dsfd = {}
     for q, t in enumerate(tokens):
         acc_t = np.zeros(d) if dx_router is None else np.array(dx_router[q], dtype=np.float64)
+        if dx_shared is not None:
+            acc_t = acc_t + np.asarray(dx_shared[q], dtype=np.float64)
         for dv in range(D):
             s = b["brim0"][dv, t]
             if s < 0:
@@ -164,11 +240,13 @@ def router_grads(logits, idx, w, renorm, dw_of, tokens):
     return out
 
 
-def full(x, wr, wgu, wdn, logits, idx, w, renorm, b, slot_expert, dy, D, dtype):
+def full(x, wr, wgu, wdn, logits, idx, w, renorm, b, slot_expert, dy, D, dtype, shared=None):
     """The whole backward for every token and expert (small layers).
+    shared: (w_gate_up_sh, w_down_sh) of the shared experts, or None.
     Returns dict: d_out_epd, dw, dG, dU, G, U, d_epd (per EPD row), dW_gate_up
     [E][2I][d], dW_down [E][d][I], dlogits [T][E], dx_router [T][d],
-    dW_router [E][d], d_sfd {s: row}, dx [T][d]."""
+    dW_router [E][d], d_sfd {s: row}, dx [T][d]; with shared experts also
+    dx_shared [T][d], dW_gate_up_sh, dW_down_sh and their G, U, dG, dU, h."""
     T, k = idx.shape
     E = wgu.shape[0]
     d = x.shape[1]
@@ -206,8 +284,16 @@ def full(x, wr, wgu, wdn, logits, idx, w, renorm, b, slot_expert, dy, D, dtype):
     X = _f64(x, dtype)
     dxr = dl @ np.asarray(wr, np.float64)
     dWr = dl.T @ X
-    dx, dsfd = grad_dispatch(b, lambda rr: r["d_epd"][rr], tokens, T, D, L, d, dtype, dxr)
+    sh = None
+    if shared is not None:
+        sh = shared_backward(x, shared[0], shared[1], dy, tokens, dtype)
+    dx, dsfd = grad_dispatch(b, lambda rr: r["d_epd"][rr], tokens, T, D, L, d, dtype, dxr,
+                             None if sh is None else sh["dx_shared"])
     out = {k_: r[k_] for k_ in ("d_out_epd", "dw", "dG", "dU", "G", "U", "d_epd", "out_epd", "h")}
     out.update(dW_gate_up=dWgu, dW_down=dWd, dlogits=dl, dx_router=dxr, dW_router=dWr,
                d_sfd=dsfd, dx=dx)
+    if sh is not None:
+        out.update({k_ + "_sh": sh[k_] for k_ in ("G", "U", "dG", "dU", "h")})
+        out.update(dx_shared=sh["dx_shared"], dW_gate_up_sh=sh["dW_gate_up_sh"],
+                   dW_down_sh=sh["dW_down_sh"])
     return out

@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(occ):
     names = declared_symbols()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     lib = C.CDLL(occ.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -147,7 +147,24 @@ def test_backward_arguments_are_checked(occ):
     assert lib.occ_grad_combine(C.byref(f32), FAKE, C.byref(brim), FAKE, None, FAKE, FAKE,
                                 None) == -2
     sh = _desc(occ, n_shared=1, I_shared=64)
-    assert lib.occ_grad_dispatch(C.byref(sh), FAKE, C.byref(brim), None, FAKE, FAKE, None) == -2
+    # shared experts: grad-dispatch needs their input gradient, and only then
+    assert lib.occ_grad_dispatch(C.byref(sh), FAKE, C.byref(brim), None, None, FAKE, FAKE,
+                                 None) == -1
+    assert lib.occ_grad_dispatch(C.byref(d), FAKE, C.byref(brim), None, FAKE, FAKE, FAKE,
+                                 None) == -1
+    assert lib.occ_grad_dispatch(C.byref(f32), FAKE, C.byref(brim), None, None, FAKE, FAKE,
+                                 None) == -2
+    # occ_shared_backward: only for layers with shared experts; workspace checked
+    hb_sh = occ.occ_ffn_workspace_bytes(sh)
+    ws_sh = occ.occ_backward_workspace_bytes(sh)
+    assert ws_sh >= 2 * 64 * 2 * 64 * 2
+    assert lib.occ_shared_backward(C.byref(d), FAKE, FAKE, FAKE, FAKE, hb_sh, FAKE, FAKE, ws_sh,
+                                   FAKE, FAKE, FAKE, None) == -1
+    assert lib.occ_shared_backward(C.byref(sh), FAKE, FAKE, FAKE, FAKE, hb_sh, FAKE, FAKE,
+                                   ws_sh, None, FAKE, FAKE, None) == -1
+    assert lib.occ_shared_backward(C.byref(sh), FAKE, FAKE, FAKE, FAKE, hb_sh, FAKE, FAKE, 1,
+                                   FAKE, FAKE, FAKE, None) == -3
+    # the pair that keeps [G | U] stays without shared experts
     assert lib.occ_grad_combine(C.byref(d), None, C.byref(brim), FAKE, None, FAKE, FAKE,
                                 None) == -1
     ws = occ.occ_backward_workspace_bytes(d)

@@ -312,3 +312,136 @@ def test_kept_preactivations_match_recompute(name):
     assert torch.equal(bits(lay.gu.view(-1)[:R * I2]), gu_ref), "kept [G | U]"
     for n in names:
         assert torch.equal(bits(getattr(lay, n)), ref[n]), n
+
+
+SHARED = {
+    # two shared experts beside the routed ones, renormalised routing
+    "bf16_shared": W.LayerConfig("bf16_shared", T=200, d=128, E=8, I=64, k=2, D=2,
+                                 dtype="bf16", n_shared=2, I_shared=64, renorm=1),
+    # more rows than one GEMM tile, a shared intermediate of two weight tiles
+    "bf16_shared_wide": W.LayerConfig("bf16_shared_wide", T=300, d=128, E=16, I=64, k=4, D=4,
+                                      dtype="bf16", n_shared=2, I_shared=384, clusters=4),
+}
+
+
+def _run_gpu_shared(cfg, inp, dy_bits):
+    """Forward, then the whole backward with the shared experts; returns the
+    gradients and the shared experts' recomputed [G | U] and [dG | dU]."""
+    import torch
+    from expert_top_router_amd.layer import MoELayer, to_device, upload_inputs
+    lay = MoELayer(cfg, upload_inputs(inp), inp.slot_expert, with_logits=True)
+    lay.prepare_backward()
+    say(f"  gpu forward+backward {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} "
+        f"n_shared={cfg.n_shared} I_shared={cfg.I_shared}")
+    for t in (lay.dx_shared, lay.dw_gate_up_sh, lay.dw_down_sh, lay.dx):
+        t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).fill_(-1)
+    lay.forward()
+    lay.dy.copy_(to_device(dy_bits))
+    lay.grad_combine()
+    lay.expert_backward()
+    lay.router_backward()
+    lay.shared_backward()
+    torch.cuda.synchronize()
+    W2 = cfg.n_shared * 2 * cfg.I_shared
+    ws = lay.bwd_ws.view(torch.int16)
+    half = -(-cfg.T * W2 * 2 // 256) * 256 // 2
+    g = {"gu_sh": ws[:cfg.T * W2].cpu().numpy().view(np.uint16).reshape(cfg.T, W2),
+         "dgu_sh": ws[half:half + cfg.T * W2].cpu().numpy().view(np.uint16).reshape(cfg.T, W2)}
+    lay.grad_dispatch()
+    torch.cuda.synchronize()
+    for n in ("topk_idx", "topk_w", "logits", "epd_token", "d_epd", "dx_router", "dx_shared",
+              "dw_gate_up_sh", "dw_down_sh", "dx", "dw_gate_up", "dw_down"):
+        g[n] = lay.host(n)
+    del lay
+    torch.cuda.empty_cache()
+    return g
+
+
+@pytest.mark.parametrize("name", list(SHARED))
+def test_shared_expert_backward_parity(orc, name):
+    """Layers with shared experts: the shared experts' recomputed [G | U],
+    [dG | dU], input gradient and weight gradients against the oracle end
+    to end, the routed experts' weight gradients beside them, and dx (the
+    dispatch gradient plus the router's and the shared experts' terms)."""
+    import oracle.backward as ob
+    cfg = SHARED[name]
+    say(f"case shared backward {name}")
+    inp = W.make_layer(cfg, seed=13)
+    dy = W.from_f64(np.random.default_rng(13).standard_normal((cfg.T, cfg.d)), "bf16")
+    g = _run_gpu_shared(cfg, inp, dy)
+    lg = oracle_logits_parallel(orc, inp.x, inp.w_router, "bf16")
+    assert np.array_equal(g["logits"].view(np.uint32), lg.view(np.uint32))
+    idx = g["topk_idx"]
+    b = orc.brim(idx, g["topk_w"], inp.slot_expert, cfg.E, cfg.D)
+    assert np.array_equal(g["epd_token"], b["epd_token"])
+    o = ob.full(_bf(inp.x), _bf(inp.w_router), _bf(inp.w_gate_up), _bf(inp.w_down), lg, idx,
+                g["topk_w"], cfg.renorm, b, inp.slot_expert, _bf(dy), cfg.D, "bf16",
+                shared=(_bf(inp.w_gate_up_sh), _bf(inp.w_down_sh)))
+    Is = cfg.I_shared
+    for s in range(cfg.n_shared):
+        c0 = s * 2 * Is
+        assert_close(_bf(g["gu_sh"][:, c0:c0 + Is]), o["G_sh"][s], "bf16", f"G_sh[{s}]")
+        assert_close(_bf(g["gu_sh"][:, c0 + Is:c0 + 2 * Is]), o["U_sh"][s], "bf16", f"U_sh[{s}]")
+        assert_close(_bf(g["dgu_sh"][:, c0:c0 + Is]), o["dG_sh"][s], "bf16", f"dG_sh[{s}]")
+        assert_close(_bf(g["dgu_sh"][:, c0 + Is:c0 + 2 * Is]), o["dU_sh"][s], "bf16",
+                     f"dU_sh[{s}]")
+    assert_close(_bf(g["dx_shared"]), o["dx_shared"], "bf16", "dx_shared")
+    assert_close(g["dw_gate_up_sh"], o["dW_gate_up_sh"], "bf16", "dW_gate_up_sh")
+    assert_close(g["dw_down_sh"], o["dW_down_sh"], "bf16", "dW_down_sh")
+    assert_close(g["dw_gate_up"], o["dW_gate_up"], "bf16", "dW_gate_up")
+    assert_close(g["dw_down"], o["dW_down"], "bf16", "dW_down")
+    # dx on the GPU's own d_epd, dx_router and dx_shared, then end to end
+    dx, _ = ob.grad_dispatch(b, lambda r: _bf(g["d_epd"][r]), np.arange(cfg.T), cfg.T, cfg.D,
+                             cfg.E // cfg.D, cfg.d, "bf16", g["dx_router"], _bf(g["dx_shared"]))
+    assert_close(_bf(g["dx"]), dx, "bf16", "dx")
+    assert_close(_bf(g["dx"]), o["dx"], "bf16", "dx (oracle chain)")
+
+
+def test_full_size_shared_expert_backward(orc):
+    """DeepSeek-V2-Lite-shaped layer (64 routed + 2 shared experts, T = 16384):
+    the shared experts' input gradient on sampled tokens, their weight
+    gradients at sampled intermediate columns (every row contributes), the
+    routed backward on the sampled tokens' EPD rows, and dx on those tokens."""
+    import oracle.backward as ob
+    cfg = W.CONFIGS["dsv2lite_bf16"]
+    say("case shared backward full dsv2lite_bf16: generating inputs")
+    inp = W.make_layer(cfg, seed=0)
+    dy = W.from_f64(np.random.default_rng(14).standard_normal((cfg.T, cfg.d)), "bf16")
+    g = _run_gpu_shared(cfg, inp, dy)
+    idx = g["topk_idx"]
+    b = orc.brim(idx, g["topk_w"], inp.slot_expert, cfg.E, cfg.D)
+    assert np.array_equal(g["epd_token"], b["epd_token"])
+    X, WGU, WD, DY = (_bf(a) for a in (inp.x, inp.w_gate_up, inp.w_down, dy))
+    WGS, WDS = _bf(inp.w_gate_up_sh), _bf(inp.w_down_sh)
+    rng = np.random.default_rng(15)
+    tok = np.sort(rng.choice(cfg.T, size=16, replace=False))
+    sh = ob.shared_backward(X, WGS, WDS, DY, tok, "bf16")
+    Is = cfg.I_shared
+    for s in range(cfg.n_shared):
+        c0 = s * 2 * Is
+        assert_close(_bf(g["dgu_sh"][tok, c0:c0 + Is]), sh["dG"][s], "bf16", f"dG_sh[{s}]")
+        assert_close(_bf(g["dgu_sh"][tok, c0 + Is:c0 + 2 * Is]), sh["dU"][s], "bf16",
+                     f"dU_sh[{s}]")
+    assert_close(_bf(g["dx_shared"][tok]), sh["dx_shared"], "bf16", "dx_shared")
+    cols = np.array(sorted({0, 1, Is - 1, *rng.choice(Is, size=3, replace=False).tolist()}))
+    for s in range(cfg.n_shared):
+        say(f"  shared expert {s}: weight gradients at intermediate columns {cols.tolist()}")
+        gr, ur, dc = ob.shared_weight_grad_columns(X, WGS, WDS, DY, s, cols, "bf16")
+        assert_close(g["dw_gate_up_sh"][s][cols], gr, "bf16", f"dW_gate_sh[{s}]")
+        assert_close(g["dw_gate_up_sh"][s][Is + cols], ur, "bf16", f"dW_up_sh[{s}]")
+        assert_close(g["dw_down_sh"][s][:, cols], dc, "bf16", f"dW_down_sh[{s}]")
+    # dx of the sampled tokens from the GPU's d_epd, dx_router and dx_shared
+    L = cfg.E // cfg.D
+    dx, _ = ob.grad_dispatch(b, lambda r: _bf(g["d_epd"][r]), tok, cfg.T, cfg.D, L, cfg.d,
+                             "bf16", g["dx_router"][tok], _bf(g["dx_shared"][tok]))
+    assert_close(_bf(g["dx"][tok]), dx, "bf16", "dx")
+    # the routed backward of the sampled tokens' EPD rows, end to end
+    rows = []
+    for t in tok:
+        for dv in range(cfg.D):
+            s_ = b["brim0"][dv, t]
+            if s_ >= 0:
+                rows += [r for r in b["brim1"][:, s_] if r >= 0]
+    rows = np.array(sorted(rows), dtype=np.int64)
+    o = ob.expert_rows(X, WGU, WD, b, inp.slot_expert, DY, rows, "bf16")
+    assert_close(_bf(g["d_epd"][rows]), o["d_epd"], "bf16", "d_epd")

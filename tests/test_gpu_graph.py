@@ -36,6 +36,8 @@ def _grads(lay):
                                     "dw_router", "dx")}
     out["d_epd"] = lay.host("d_epd")[:R]
     out["d_sfd"] = lay.host("d_sfd")[:S]
+    if lay.cfg.n_shared:
+        out.update({n: lay.host(n) for n in ("dx_shared", "dw_gate_up_sh", "dw_down_sh")})
     return out
 
 
@@ -48,7 +50,7 @@ def _same(a, b, what):
 
 @pytest.mark.parametrize("name,budget,backward", [
     ("bf16_ragged", None, False), ("bf16_shared", None, False), ("f32_e12", None, False),
-    ("bf16_ragged", 2, False), ("bf16_ragged", None, True),
+    ("bf16_ragged", 2, False), ("bf16_ragged", None, True), ("bf16_shared", None, True),
 ])
 def test_graph_replays_match_eager(name, budget, backward):
     import torch
@@ -90,8 +92,10 @@ def test_graph_replays_match_eager(name, budget, backward):
         lay.poison()
         if backward:
             for n in ("d_epd", "dw_gate_up", "dw_down", "dlogits", "dx_router", "dw_router",
-                      "d_sfd", "dx"):
+                      "d_sfd", "dx", "dx_shared", "dw_gate_up_sh", "dw_down_sh"):
                 t = getattr(lay, n)
+                if t is None:
+                    continue
                 t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).fill_(-1)
         torch.cuda.synchronize()
         graph.replay()

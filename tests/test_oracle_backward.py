@@ -227,3 +227,103 @@ def test_slot_weight_grads_pinned(orc):
                     fd = (loss(wgu, plus) - loss(wgu, minus)) / (2 * eps)
                 assert abs(fd - grad[pos]) <= 1e-6 * max(1.0, abs(fd)), (slot, name, pos, fd,
                                                                           grad[pos])
+
+
+def shared64(x, wgu_sh, wdn_sh):
+    """The shared experts' output in fp64: sum over them of W_d (silu(W_g x) * W_u x)."""
+    Is = wgu_sh.shape[1] // 2
+    y = np.zeros_like(x)
+    for sg in range(wgu_sh.shape[0]):
+        a = x @ wgu_sh[sg, :Is].T
+        u = x @ wgu_sh[sg, Is:].T
+        y += (a / (1.0 + np.exp(-a)) * u) @ wdn_sh[sg].T
+    return y
+
+
+def test_shared_expert_gradients_match_finite_differences(orc):
+    """A layer with two shared experts (weight 1, on every token): the
+    input gradient (routed, router and shared paths together) and the
+    shared experts' weight gradients against central finite differences of
+    the plain fp64 layer with the selections held fixed."""
+    ob = _ob()
+    cfg = W.LayerConfig("bwd_shared", T=20, d=16, E=8, I=12, k=2, D=2, dtype="f32",
+                        n_shared=2, I_shared=8, clusters=3)
+    inp = W.make_layer(cfg, seed=9)
+    x, wr, wgu, wdn, wgs, wds = (np.asarray(a, np.float64) for a in (
+        inp.x, inp.w_router, inp.w_gate_up, inp.w_down, inp.w_gate_up_sh, inp.w_down_sh))
+    lg, idx, w = orc.route(inp.x, inp.w_router, cfg.k, 0, "f32")
+    b = orc.brim(idx, w, inp.slot_expert, cfg.E, cfg.D)
+    # the plain fp64 forward with shared experts agrees with the C oracle's layer
+    y_c = orc.layer(inp)["y"]
+    assert rel_err(y_c, fwd64(x, wr, wgu, wdn, idx, 0) + shared64(x, wgs, wds)) <= 1e-5
+    rng = np.random.default_rng(10)
+    dy = rng.standard_normal(x.shape)
+    g = ob.full(x, wr, wgu, wdn, lg, idx, w, 0, b, inp.slot_expert, dy, cfg.D, "f64",
+                shared=(wgs, wds))
+
+    def loss(x_, wgs_, wds_):
+        return float(np.sum(dy * (fwd64(x_, wr, wgu, wdn, idx, 0) + shared64(x_, wgs_, wds_))))
+
+    eps = 1e-6
+    for name, arr, grad in [("x", x, g["dx"]), ("w_gate_up_sh", wgs, g["dW_gate_up_sh"]),
+                            ("w_down_sh", wds, g["dW_down_sh"])]:
+        for _ in range(8):
+            pos = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            args = {"x": x, "w_gate_up_sh": wgs, "w_down_sh": wds}
+            plus = {k_: v.copy() for k_, v in args.items()}
+            minus = {k_: v.copy() for k_, v in args.items()}
+            plus[name][pos] += eps
+            minus[name][pos] -= eps
+            fd = (loss(plus["x"], plus["w_gate_up_sh"], plus["w_down_sh"]) -
+                  loss(minus["x"], minus["w_gate_up_sh"], minus["w_down_sh"])) / (2 * eps)
+            assert abs(fd - grad[pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+
+
+def test_two_shared_experts_backward_equal_one_concatenated(orc):
+    """Two shared SwiGLU experts are one with their intermediate rows
+    concatenated (an exact identity of the forward); so are their gradients:
+    the concatenated expert's weight gradients are the two experts' side by
+    side, and the input gradients agree (rounded, bf16)."""
+    ob = _ob()
+    rng = np.random.default_rng(11)
+    T, d, Is = 24, 32, 16
+    x = W.from_f64(rng.standard_normal((T, d)), "bf16")
+    wgs = W.from_f64(rng.standard_normal((2, 2 * Is, d)) / np.sqrt(d), "bf16")
+    wds = W.from_f64(rng.standard_normal((2, d, Is)) / np.sqrt(d), "bf16")
+    dy = W.from_f64(rng.standard_normal((T, d)), "bf16")
+    tok = np.arange(T)
+    two = ob.shared_backward(x, wgs, wds, dy, tok, "bf16")
+    # one expert of intermediate 2 Is: gate rows of both, then up rows of both
+    wg1 = np.concatenate([wgs[0, :Is], wgs[1, :Is], wgs[0, Is:], wgs[1, Is:]], axis=0)[None]
+    wd1 = np.concatenate([wds[0], wds[1]], axis=1)[None]
+    one = ob.shared_backward(x, wg1, wd1, dy, tok, "bf16")
+    dWg = one["dW_gate_up_sh"][0]
+    same = lambda u, v: np.allclose(u, v, rtol=1e-12, atol=1e-12)  # noqa: E731
+    assert same(dWg[:Is], two["dW_gate_up_sh"][0, :Is])
+    assert same(dWg[Is:2 * Is], two["dW_gate_up_sh"][1, :Is])
+    assert same(dWg[2 * Is:3 * Is], two["dW_gate_up_sh"][0, Is:])
+    assert same(dWg[3 * Is:], two["dW_gate_up_sh"][1, Is:])
+    assert same(one["dW_down_sh"][0], np.concatenate([two["dW_down_sh"][0],
+                                                      two["dW_down_sh"][1]], axis=1))
+    # the input gradient is one rounded sum either way (summation order only)
+    assert rel_err(one["dx_shared"], two["dx_shared"]) <= 1e-2
+
+
+def test_shared_weight_grad_columns_are_slices_of_the_full_gradient():
+    """The column-restricted shared weight gradients (the reference for
+    full-size layers) equal the slices of shared_backward's full result."""
+    ob = _ob()
+    rng = np.random.default_rng(12)
+    T, d, Is = 40, 32, 24
+    x = W.from_f64(rng.standard_normal((T, d)), "bf16")
+    wgs = W.from_f64(rng.standard_normal((2, 2 * Is, d)) / np.sqrt(d), "bf16")
+    wds = W.from_f64(rng.standard_normal((2, d, Is)) / np.sqrt(d), "bf16")
+    dy = W.from_f64(rng.standard_normal((T, d)), "bf16")
+    full = ob.shared_backward(x, wgs, wds, dy, np.arange(T), "bf16")
+    for s in range(2):
+        cols = np.array([0, 5, Is - 1])
+        gr, ur, dc = ob.shared_weight_grad_columns(x, wgs, wds, dy, s, cols, "bf16")
+        same = lambda u, v: np.allclose(u, v, rtol=1e-12, atol=1e-12)  # noqa: E731
+        assert same(gr, full["dW_gate_up_sh"][s][cols])
+        assert same(ur, full["dW_gate_up_sh"][s][Is + cols])
+        assert same(dc, full["dW_down_sh"][s][:, cols])
