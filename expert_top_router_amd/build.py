@@ -24,7 +24,8 @@ LIB = os.path.join(PKG, "liboccult.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["occ_api.cpp", "occ_route.hip", "occ_brim.hip", "occ_permute.hip", "occ_coact.hip",
-           "occ_affinity.hip", "occ_backward.hip", "occ_gemm.hip", "occ_gemm_bwd.hip"]
+           "occ_affinity.hip", "occ_backward.hip", "occ_gemm.hip", "occ_gemm_bwd.hip",
+           "occ_bwd_f32.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

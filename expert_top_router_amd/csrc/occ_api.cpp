@@ -355,29 +355,31 @@ occ_status occ_coactivation(const occ_layer_desc *desc, const int32_t *topk_idx,
 // ---- backward -------------------------------------------------------------
 static occ_status check_backward(const occ_layer_desc *desc) {
   OCC_TRY(check_desc(desc));
-  if (desc->dtype != OCC_BF16) return fail(OCC_EUNSUP, "the backward pass is for bf16 layers");
   // [G | U] and [dG | dU] (R x 2I bf16, and T x n_shared 2 I_shared for the
   // shared experts) are GEMM operands addressed with 32-bit byte offsets,
   // like every operand check_desc bounds
-  if ((int64_t)desc->T * desc->k * 2 * desc->I * 2 > 0xffffffffll ||
-      (int64_t)desc->T * desc->n_shared * 2 * desc->I_shared * 2 > 0xffffffffll)
+  if (desc->dtype == OCC_BF16 &&
+      ((int64_t)desc->T * desc->k * 2 * desc->I * 2 > 0xffffffffll ||
+       (int64_t)desc->T * desc->n_shared * 2 * desc->I_shared * 2 > 0xffffffffll))
     return fail(OCC_EUNSUP, "the backward's [G | U] rows exceed 4 GiB");
   return OCC_OK;
 }
 
-// The pair that keeps [G | U] runs the routed experts only.
+// The pair that keeps [G | U] runs the routed bf16 experts only.
 static occ_status check_keep(const occ_layer_desc *desc) {
   OCC_TRY(check_backward(desc));
+  if (desc->dtype != OCC_BF16)
+    return fail(OCC_EUNSUP, "kept pre-activations are for bf16 layers");
   if (desc->n_shared != 0)
     return fail(OCC_EUNSUP, "kept pre-activations are for layers without shared experts");
   return OCC_OK;
 }
 
 static size_t gu_bytes(const occ_layer_desc &L) {
-  return align256((size_t)L.T * L.k * 2 * L.I * 2);
+  return align256((size_t)L.T * L.k * 2 * L.I * elem_bytes(L));
 }
 static size_t gu_sh_bytes(const occ_layer_desc &L) {
-  return align256((size_t)L.T * L.n_shared * 2 * L.I_shared * 2);
+  return align256((size_t)L.T * L.n_shared * 2 * L.I_shared * elem_bytes(L));
 }
 
 size_t occ_backward_workspace_bytes(const occ_layer_desc *desc) {

@@ -1,5 +1,5 @@
-// Backward pass through the BRIMs (bf16 layers): gradient of the combine and
-// of the routing.
+// Backward pass through the BRIMs: gradient of the combine and of the
+// routing (bf16 and fp32 layers).
 //
 // Expert Coupling in MoE Pretraining, Abstract: every MoE layer runs its
 // all-to-alls in the forward and in the backward pass; Occult, Figure 4
@@ -8,7 +8,7 @@
 // dY [T][d]:
 //   grad-combine (one wave per ORI token, rows found through BRIM_0/BRIM_1):
 //     d_out_sfd[s] = dY[t]                       (the backward send buffer)
-//     d_out_epd[r] = w[r] * dY[t]                (rounded to bf16)
+//     d_out_epd[r] = w[r] * dY[t]                (rounded to the layer dtype)
 //     dw[r]        = sum_c dY[t][c] out_epd[r][c] (fp32, the weight's gradient)
 //   router: for the token's picks, dp from dw (through the renormalisation
 //     when the weights were renormalised), then the softmax backward
@@ -39,22 +39,45 @@ __device__ __forceinline__ u32x4 pack_bf16(const float *f) {
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <int NCH>
+// 16-byte chunks of the layer dtype <-> fp32
+template <int DT> struct Vec;
+template <> struct Vec<OCC_BF16> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void unpack(const u32x4 &u, float *f) { unpack_bf16(u, f); }
+  static __device__ __forceinline__ u32x4 pack(const float *f) { return pack_bf16(f); }
+};
+template <> struct Vec<OCC_F32> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void unpack(const u32x4 &u, float *f) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+  }
+  static __device__ __forceinline__ u32x4 pack(const float *f) {
+    return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                 __float_as_uint(f[3])};
+  }
+};
+
+template <int DT, int NCH>
 __global__ __launch_bounds__(kThreads) void grad_combine_kernel(
     int T, int D, int L, int ld, int row16, const u32x4 *__restrict__ dy,
     const int32_t *__restrict__ brim0, const int32_t *__restrict__ brim1,
     const float *__restrict__ epd_w, const u32x4 *__restrict__ out_epd,
     u32x4 *__restrict__ d_out_sfd, u32x4 *__restrict__ d_out_epd, float *__restrict__ dw) {
+  using V = Vec<DT>;
+  constexpr int VE = V::N;
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * kTokPerBlock + threadIdx.x / kWave;
   if (t >= T) return;  // whole wave leaves together
   u32x4 v[NCH];
-  float g[NCH][8];
+  float g[NCH][VE];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int i = lane + kWave * c;
     v[c] = i < row16 ? dy[(size_t)t * row16 + i] : u32x4{0u, 0u, 0u, 0u};
-    unpack_bf16(v[c], g[c]);
+    V::unpack(v[c], g[c]);
   }
   const int npairs = D * L;
   for (int p0 = 0; p0 < npairs; p0 += kWave) {
@@ -101,14 +124,14 @@ __global__ __launch_bounds__(kThreads) void grad_combine_kernel(
       for (int c = 0; c < NCH; ++c) {
         const int i = lane + kWave * c;
         if (i < row16) {
-          float o[8], d[8];
-          unpack_bf16(ov[c], o);
+          float o[VE], d[VE];
+          V::unpack(ov[c], o);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
+          for (int u = 0; u < VE; ++u) {
             dot = __builtin_fmaf(g[c][u], o[u], dot);
             d[u] = wb * g[c][u];
           }
-          d_out_epd[(size_t)row * row16 + i] = pack_bf16(d);
+          d_out_epd[(size_t)row * row16 + i] = V::pack(d);
         }
       }
 #pragma unroll
@@ -313,20 +336,27 @@ hipError_t launch_grad_combine(const occ_layer_desc &Ld, const void *dy, const o
                                const void *out_epd, void *d_out_sfd, void *d_out_epd, float *dw,
                                hipStream_t st) {
   if (Ld.T == 0) return hipSuccess;
-  const int row16 = Ld.d * 2 / 16;
+  const int row16 = Ld.d * (Ld.dtype == OCC_F32 ? 4 : 2) / 16;
   const int L = Ld.E / Ld.D;
   const int ld = Ld.T * (Ld.k < Ld.D ? Ld.k : Ld.D);
   const dim3 grid((Ld.T + kTokPerBlock - 1) / kTokPerBlock);
   const int nch = chunks_per_lane(row16);
-#define OCC_GC(N)                                                                            \
-  grad_combine_kernel<N><<<grid, kThreads, 0, st>>>(                                         \
+#define OCC_GC(DT, N)                                                                        \
+  grad_combine_kernel<DT, N><<<grid, kThreads, 0, st>>>(                                     \
       Ld.T, Ld.D, L, ld, row16, static_cast<const u32x4 *>(dy), b.brim0, b.brim1, b.epd_w,   \
       static_cast<const u32x4 *>(out_epd), static_cast<u32x4 *>(d_out_sfd),                  \
       static_cast<u32x4 *>(d_out_epd), dw)
-  if (nch <= 1) OCC_GC(1);
-  else if (nch <= 2) OCC_GC(2);
-  else if (nch <= 4) OCC_GC(4);
-  else OCC_GC(8);
+  if (Ld.dtype == OCC_F32) {
+    if (nch <= 1) OCC_GC(OCC_F32, 1);
+    else if (nch <= 2) OCC_GC(OCC_F32, 2);
+    else if (nch <= 4) OCC_GC(OCC_F32, 4);
+    else OCC_GC(OCC_F32, 8);
+  } else {
+    if (nch <= 1) OCC_GC(OCC_BF16, 1);
+    else if (nch <= 2) OCC_GC(OCC_BF16, 2);
+    else if (nch <= 4) OCC_GC(OCC_BF16, 4);
+    else OCC_GC(OCC_BF16, 8);
+  }
 #undef OCC_GC
   return hipGetLastError();
 }
@@ -357,8 +387,12 @@ hipError_t launch_router_backward(const occ_layer_desc &Ld, const Placement &pl,
   const int chunks = T > 0 ? (T + kc - 1) / kc : 1;
   const dim3 gw((d + kRBN - 1) / kRBN, (E + kRBM - 1) / kRBM, chunks);
   float *dst = chunks > 1 ? static_cast<float *>(ws) : dw_router;
-  router_gemm_kernel<true, OCC_BF16><<<gw, kThreads, 0, st>>>(
-      E, d, T, kc, dlogit, E, static_cast<const BT *>(x), d, dst);
+  if (Ld.dtype == OCC_F32)
+    router_gemm_kernel<true, OCC_F32><<<gw, kThreads, 0, st>>>(
+        E, d, T, kc, dlogit, E, static_cast<const float *>(x), d, dst);
+  else
+    router_gemm_kernel<true, OCC_BF16><<<gw, kThreads, 0, st>>>(
+        E, d, T, kc, dlogit, E, static_cast<const BT *>(x), d, dst);
   if (chunks > 1) {
     const int64_t n4 = (int64_t)E * d / 4;
     chunk_sum_kernel<<<(unsigned)((n4 + kThreads - 1) / kThreads), kThreads, 0, st>>>(

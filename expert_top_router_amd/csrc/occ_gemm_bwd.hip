@@ -444,6 +444,9 @@ hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_o
                                   const void *w_down, const void *h, const void *d_out_epd,
                                   void *gu, void *dgu, void *d_epd, float *dw_gate_up,
                                   float *dw_down, hipStream_t st, bool recompute_gu) {
+  if (L.dtype == OCC_F32)
+    return launch_expert_backward_f32(L, slot_offset, pl, epd, w_gate_up, w_down, h, d_out_epd,
+                                      gu, dgu, d_epd, dw_gate_up, dw_down, st);
   const int64_t d = L.d, I = L.I, R = (int64_t)L.T * L.k, E = L.E;
   hipError_t err;
   // 1. [G | U] = EPD W_gate_up^T, recomputed and stored in bf16
@@ -557,6 +560,9 @@ hipError_t launch_shared_backward(const occ_layer_desc &L, const void *x, const 
                                   const void *w_down_sh, const void *h_sh, const void *dy,
                                   void *gu, void *dgu, void *dx_shared, float *dw_gate_up_sh,
                                   float *dw_down_sh, hipStream_t st) {
+  if (L.dtype == OCC_F32)
+    return launch_shared_backward_f32(L, x, w_gate_up_sh, w_down_sh, h_sh, dy, gu, dgu, dx_shared,
+                                      dw_gate_up_sh, dw_down_sh, st);
   // (T = 0: the products over no rows launch no tiles; the weight gradients,
   // sums over no rows, are written as zeros)
   const int64_t T = L.T, d = L.d, Is = L.I_shared, ns = L.n_shared, W2 = ns * 2 * Is;

@@ -96,7 +96,7 @@ hipError_t launch_dispatch(const occ_layer_desc &L, const void *x, const occ_bri
 hipError_t launch_combine(const occ_layer_desc &L, const void *out_epd, const occ_brim &b,
                           const void *shared_out, void *out_sfd, void *y, hipStream_t st);
 
-// Backward (bf16): grad-combine, grad-dispatch and the router gradient.
+// Backward: grad-combine, grad-dispatch and the router gradient.
 hipError_t launch_grad_combine(const occ_layer_desc &L, const void *dy, const occ_brim &b,
                                const void *out_epd, void *d_out_sfd, void *d_out_epd, float *dw,
                                hipStream_t st);
@@ -129,7 +129,7 @@ hipError_t launch_local_hits(int T, int k2, int E2, const int32_t *idx2, const D
                              const int32_t *home, int32_t *hits, int accumulate, hipStream_t st);
 
 // Expert GEMMs.  up: h = swiglu(A W_gu^T); down: out = h W_dn^T.
-// Expert backward (bf16): recomputes [G | U] into gu ([R][2I]), writes
+// Expert backward: recomputes [G | U] into gu ([R][2I]), writes
 // [dG | dU] into dgu ([R][2I]) and dEPD ([R][d]), and the fp32 weight
 // gradients dW_gate_up [E][2I][d] and dW_down [E][d][I].
 hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_offset,
@@ -137,7 +137,18 @@ hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_o
                                   const void *w_down, const void *h, const void *d_out_epd,
                                   void *gu, void *dgu, void *d_epd, float *dw_gate_up,
                                   float *dw_down, hipStream_t st, bool recompute_gu = true);
-// Shared experts' backward (bf16): gu and dgu are [T][n_sh * 2 I_sh] bf16
+// fp32 layers: the same products, one thread per output (occ_bwd_f32.hip)
+hipError_t launch_expert_backward_f32(const occ_layer_desc &L, const int32_t *slot_offset,
+                                      const Placement &pl, const void *epd, const void *w_gate_up,
+                                      const void *w_down, const void *h, const void *d_out_epd,
+                                      void *gu, void *dgu, void *d_epd, float *dw_gate_up,
+                                      float *dw_down, hipStream_t st);
+hipError_t launch_shared_backward_f32(const occ_layer_desc &L, const void *x,
+                                      const void *w_gate_up_sh, const void *w_down_sh,
+                                      const void *h_sh, const void *dy, void *gu, void *dgu,
+                                      void *dx_shared, float *dw_gate_up_sh, float *dw_down_sh,
+                                      hipStream_t st);
+// Shared experts' backward: gu and dgu are [T][n_sh * 2 I_sh] dtype
 // workspaces; h_sh the forward's shared activations [T][n_sh * I_sh].
 hipError_t launch_shared_backward(const occ_layer_desc &L, const void *x, const void *w_gate_up_sh,
                                   const void *w_down_sh, const void *h_sh, const void *dy,

@@ -182,7 +182,7 @@ class MoELayer:
         cfg = self.cfg
         T, d, E, k, D = cfg.T, cfg.d, cfg.E, cfg.k, cfg.D
         S_max, R = T * min(k, D), T * k
-        el = torch.bfloat16
+        el = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         f32 = torch.float32
 
         def buf(shape, dt):

@@ -143,17 +143,18 @@ def test_backward_arguments_are_checked(occ):
     d = _desc(occ)
     assert occ.occ_backward_workspace_bytes(d) == 2 * 64 * 2 * 2 * 128 * 2
     f32 = _desc(occ, dtype="f32")
-    assert occ.occ_backward_workspace_bytes(f32) == 0
-    assert lib.occ_grad_combine(C.byref(f32), FAKE, C.byref(brim), FAKE, None, FAKE, FAKE,
-                                None) == -2
+    # fp32 layers: [G | U] and [dG | dU] in fp32
+    assert occ.occ_backward_workspace_bytes(f32) == 2 * 64 * 2 * 2 * 128 * 4
+    assert lib.occ_grad_combine(C.byref(f32), None, C.byref(brim), FAKE, None, FAKE, FAKE,
+                                None) == -1
     sh = _desc(occ, n_shared=1, I_shared=64)
     # shared experts: grad-dispatch needs their input gradient, and only then
     assert lib.occ_grad_dispatch(C.byref(sh), FAKE, C.byref(brim), None, None, FAKE, FAKE,
                                  None) == -1
     assert lib.occ_grad_dispatch(C.byref(d), FAKE, C.byref(brim), None, FAKE, FAKE, FAKE,
                                  None) == -1
-    assert lib.occ_grad_dispatch(C.byref(f32), FAKE, C.byref(brim), None, None, FAKE, FAKE,
-                                 None) == -2
+    assert lib.occ_grad_dispatch(C.byref(f32), FAKE, C.byref(brim), None, None, FAKE, None,
+                                 None) == -1
     # occ_shared_backward: only for layers with shared experts; workspace checked
     hb_sh = occ.occ_ffn_workspace_bytes(sh)
     ws_sh = occ.occ_backward_workspace_bytes(sh)

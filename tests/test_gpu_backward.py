@@ -445,3 +445,58 @@ def test_full_size_shared_expert_backward(orc):
     rows = np.array(sorted(rows), dtype=np.int64)
     o = ob.expert_rows(X, WGU, WD, b, inp.slot_expert, DY, rows, "bf16")
     assert_close(_bf(g["d_epd"][rows]), o["d_epd"], "bf16", "d_epd")
+
+
+F32 = {
+    "tiny_fp32": W.CONFIGS["tiny_fp32"],
+    # odd sizes: 12 experts on 3 devices, top-3, a narrow intermediate
+    "f32_e12": W.LayerConfig("f32_e12", T=77, d=64, E=12, I=32, k=3, D=3, dtype="f32"),
+    # shared experts and renormalised routing
+    "f32_shared": W.LayerConfig("f32_shared", T=100, d=64, E=8, I=32, k=2, D=2, dtype="f32",
+                                n_shared=2, I_shared=48, renorm=1, clusters=3),
+}
+
+
+@pytest.mark.parametrize("name", list(F32))
+def test_fp32_layer_backward_parity(orc, name):
+    """fp32 layers: the whole backward (grad-combine, expert backward, router
+    gradient, shared experts, grad-dispatch) against the oracle's chain with
+    fp32 storage, every tensor within the fp32 tolerance."""
+    import torch
+    import oracle.backward as ob
+    from expert_top_router_amd.layer import MoELayer, to_device, upload_inputs
+    cfg = F32[name]
+    say(f"case fp32 backward {name}")
+    inp = W.make_layer(cfg, seed=17)
+    dy = np.random.default_rng(17).standard_normal((cfg.T, cfg.d)).astype(np.float32)
+    lay = MoELayer(cfg, upload_inputs(inp), inp.slot_expert, with_logits=True)
+    lay.prepare_backward()
+    say(f"  gpu forward+backward {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} fp32")
+    lay.forward()
+    lay.backward(to_device(dy))
+    torch.cuda.synchronize()
+    names = ["topk_idx", "topk_w", "logits", "epd_token", "d_out_epd", "dw_epd", "d_epd",
+             "dw_gate_up", "dw_down", "dlogits", "dx_router", "dw_router", "dx"]
+    if cfg.n_shared:
+        names += ["dx_shared", "dw_gate_up_sh", "dw_down_sh"]
+    g = {n: lay.host(n) for n in names}
+    del lay
+    torch.cuda.empty_cache()
+    lg = oracle_logits_parallel(orc, inp.x, inp.w_router, "f32")
+    assert np.array_equal(g["logits"].view(np.uint32), lg.view(np.uint32))
+    idx = g["topk_idx"]
+    b = orc.brim(idx, g["topk_w"], inp.slot_expert, cfg.E, cfg.D)
+    assert np.array_equal(g["epd_token"], b["epd_token"])
+    f64 = lambda a: np.asarray(a, np.float64)  # noqa: E731
+    shared = (f64(inp.w_gate_up_sh), f64(inp.w_down_sh)) if cfg.n_shared else None
+    o = ob.full(f64(inp.x), f64(inp.w_router), f64(inp.w_gate_up), f64(inp.w_down), lg, idx,
+                g["topk_w"], cfg.renorm, b, inp.slot_expert, f64(dy), cfg.D, "f32",
+                shared=shared)
+    for name_g, name_o in [("d_out_epd", "d_out_epd"), ("dw_epd", "dw"), ("d_epd", "d_epd"),
+                           ("dw_gate_up", "dW_gate_up"), ("dw_down", "dW_down"),
+                           ("dlogits", "dlogits"), ("dx_router", "dx_router"),
+                           ("dw_router", "dW_router"), ("dx", "dx")]:
+        assert_close(g[name_g], o[name_o], "f32", name_g)
+    if cfg.n_shared:
+        for name in ("dx_shared", "dw_gate_up_sh", "dw_down_sh"):
+            assert_close(g[name], o[name.replace("dw_", "dW_")], "f32", name)

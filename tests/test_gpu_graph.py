@@ -51,6 +51,7 @@ def _same(a, b, what):
 @pytest.mark.parametrize("name,budget,backward", [
     ("bf16_ragged", None, False), ("bf16_shared", None, False), ("f32_e12", None, False),
     ("bf16_ragged", 2, False), ("bf16_ragged", None, True), ("bf16_shared", None, True),
+    ("f32_e12", None, True),
 ])
 def test_graph_replays_match_eager(name, budget, backward):
     import torch
