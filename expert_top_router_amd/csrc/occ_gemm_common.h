@@ -36,6 +36,10 @@ struct GemmArgs {
   int64_t c_group_stride;  // elements between the outputs of consecutive experts
   const void *aux;         // SwiGLU backward: the recomputed [G | U] rows
   int64_t ldaux;
+  // tile order inside a group: 0 = m-tiles fastest (the n-tiles' weight
+  // panels read once, the rows re-read per pass over the n-tiles),
+  // 1 = n-tiles fastest (the rows read once, the panels re-read per m-tile)
+  int n_inner;
   int32_t expert_of_group[OCC_MAX_E];
 };
 
@@ -92,7 +96,8 @@ __device__ __forceinline__ int tile_table(const GemmArgs &a, int32_t *ts, int32_
   return ts[a.G] * ntn;
 }
 
-// Tile number `logical` (slot-major, then n-tile, m-tile fastest).
+// Tile number `logical`: group-major, then n-tile with the m-tile fastest,
+// or (n_inner) m-tile with the n-tile fastest.
 template <int BM, int BNO>
 __device__ __forceinline__ TileCoord tile_coord(const GemmArgs &a, const int32_t *ts,
                                                 const int32_t *ro, int logical) {
@@ -107,14 +112,16 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmArgs &a, const int32_t
     }
     const int mtg = ts[lo + 1] - ts[lo];
     const int local = logical - ts[lo] * ntn;
-    const int nt = local / mtg, mt = local - nt * mtg;
+    const int nt = a.n_inner ? local % ntn : local / mtg;
+    const int mt = a.n_inner ? local / ntn : local - nt * mtg;
     tc.group = lo;
     tc.row_begin = ro[lo] + mt * BM;
     tc.rows = min(BM, ro[lo + 1] - tc.row_begin);
     tc.n0 = nt * BNO;
   } else {
     const int total_mt = (a.dense_rows + BM - 1) / BM;
-    const int nt = logical / total_mt, mt = logical - nt * total_mt;
+    const int nt = a.n_inner ? logical % ntn : logical / total_mt;
+    const int mt = a.n_inner ? logical / ntn : logical - nt * total_mt;
     tc.group = 0;
     tc.row_begin = mt * BM;
     tc.rows = min(BM, a.dense_rows - tc.row_begin);
