@@ -384,20 +384,6 @@ void launch_bf16(const GemmArgs &a, int max_rows, int n_cu, hipStream_t st) {
   gemm_bf16_kernel<BM, BN, PF, SWIGLU, NWN, KEEP><<<(unsigned)grid, 2 * NWN * kWave, 0, st>>>(a);
 }
 
-// Tile order of a grouped product from its shapes (the host does not know
-// the groups' row counts, so their mean stands in): the 32 CUs of an XCD run
-// neighbouring tiles together.  With the m-tiles fastest a group's rows are
-// re-read once per pass over the n-tiles and each weight panel is read once;
-// with the n-tiles fastest the reverse.  The n-tiles go fastest when a
-// group's weights are at most half the size of its rows (stress layer
-// gate/up GEMM: 12.6 MB of rows against 6.3 MB of weights per slot, 2242 ->
-// 2130 us; the same order on its down GEMM, 4.7 against 3.1 MB, measured 3%
-// slower, and 23% slower on the Mixtral-shaped gate/up GEMM).
-void choose_tile_order(GemmArgs &a, int64_t rows_per_group, int64_t weight_rows) {
-  const int64_t row_bytes = rows_per_group * a.K, weight_bytes = weight_rows * a.K;
-  a.n_inner = 2 * weight_bytes <= row_bytes ? 1 : 0;
-}
-
 template <bool SWIGLU>
 hipError_t run_gemm(const GemmArgs &a, int dtype, int max_rows, hipStream_t st) {
   if (max_rows <= 0) return hipSuccess;

@@ -464,6 +464,7 @@ hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_o
   a.N = (int)(2 * I);
   a.C = gu;
   a.ldc = 2 * I;
+  choose_tile_order(a, R / E, 2 * I);
   // (skipped when the forward kept them: the same products, same rounding)
   if (recompute_gu &&
       (err = launch_bwd<0, 0, false, EPI_BF16, 4>(a, grouped_tiles((int)R, L.E, a.N), st)) !=
@@ -486,6 +487,7 @@ hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_o
   a.ldaux = 2 * I;
   a.C = dgu;
   a.ldc = 2 * I;
+  choose_tile_order(a, R / E, I);
   if ((err = launch_bwd<0, 1, false, EPI_SWIGLU_BWD, 4>(a, grouped_tiles((int)R, L.E, a.N), st)) !=
       hipSuccess)
     return err;
@@ -544,6 +546,7 @@ hipError_t launch_expert_backward(const occ_layer_desc &L, const int32_t *slot_o
   a.N = (int)d;
   a.C = d_epd;
   a.ldc = d;
+  choose_tile_order(a, R / E, d);
   return launch_bwd<0, 1, false, EPI_BF16, 4>(a, grouped_tiles((int)R, L.E, a.N), st);
 }
 
@@ -591,6 +594,7 @@ hipError_t launch_shared_backward(const occ_layer_desc &L, const void *x, const 
   a.N = (int)W2;
   a.C = gub;
   a.ldc = W2;
+  choose_tile_order(a, T, W2);
   if ((err = launch_bwd<0, 0, false, EPI_BF16, 4>(a, grouped_tiles((int)T, 1, a.N), st)) !=
       hipSuccess)
     return err;
@@ -610,6 +614,7 @@ hipError_t launch_shared_backward(const occ_layer_desc &L, const void *x, const 
     a.ldaux = W2;
     a.C = dgub + s * 2 * Is;
     a.ldc = W2;
+    choose_tile_order(a, T, Is);
     if ((err = launch_bwd<0, 1, false, EPI_SWIGLU_BWD, 4>(a, grouped_tiles((int)T, 1, a.N), st)) !=
         hipSuccess)
       return err;
@@ -659,6 +664,7 @@ hipError_t launch_shared_backward(const occ_layer_desc &L, const void *x, const 
   a.N = (int)d;
   a.C = dx_shared;
   a.ldc = d;
+  choose_tile_order(a, T, d);
   return launch_bwd<0, 1, false, EPI_BF16, 4>(a, grouped_tiles((int)T, 1, a.N), st);
 }
 
