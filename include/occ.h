@@ -238,7 +238,8 @@ occ_status occ_combine_direct(const occ_layer_desc *desc, const void *out_epd, c
 occ_status occ_coactivation(const occ_layer_desc *desc, const int32_t *topk_idx,
                             int32_t *counts, int32_t accumulate, hipStream_t stream);
 
-/* ---- Backward pass through the BRIMs (bf16 layers; EUNSUP for fp32).
+/* ---- Backward pass through the BRIMs (bf16 and fp32 layers: in an fp32
+ * layer every tensor marked bf16 below is fp32 and no step rounds to bf16).
  * Expert Coupling in MoE Pretraining, Abstract: every MoE layer runs its
  * all-to-alls in the forward and the backward pass; Occult, Figure 4
  * caption: the moves between ORI, SFD and EPD are guided by the BRIMs,
@@ -312,9 +313,10 @@ occ_status occ_expert_backward_kept(const occ_layer_desc *desc, const void *epd,
  * Both products accumulate in fp32; dw_router sums its token chunks in a
  * fixed order (deterministic).  The gradient is exact for a BRIM from
  * occ_build_brim.  With one from occ_build_brim_pruned it takes dw_epd (the
- * gradient of each stored, possibly rescaled, weight) as the gradient of
- * that pick's routing weight and gives dropped picks none: an approximation
- * that ignores the pruning and the rescaling factor.  bwd_ws: device workspace of at least
+ * gradient of each stored weight) as the gradient of that pick's routing
+ * weight and gives dropped picks none: with rescale = 0 the exact gradient
+ * of the pruned layer (the pruning decision held fixed), with rescale = 1 an
+ * approximation that ignores the rescaling factor.  bwd_ws: device workspace of at least
  * occ_backward_workspace_bytes(desc) bytes for the partial sums (ENOSPC when
  * smaller; its contents are not kept). */
 occ_status occ_router_backward(const occ_layer_desc *desc, const void *x, const float *w_router,
