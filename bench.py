@@ -39,7 +39,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
-PEAK_F32_VALU_TFLOPS = 78.6  # fp32 FMA without packed math (256 CU x 64 lanes x 2 x 2.4 GHz)
+# fp32 vector peak as published (256 CU x 4 SIMD x 32 FMA x 2 flop x 2.4 GHz); plain
+# v_fmac_f32 reaches it without packed math once two waves share a SIMD
+PEAK_F32_VALU_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE-layer tokens/sec (route+dispatch+FFN+combine); % HBM and % MFMA peak"
 DEFAULT_WORKLOAD = "stress_bf16"

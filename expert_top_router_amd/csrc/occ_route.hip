@@ -404,8 +404,21 @@ hipError_t launch_dt(const occ_layer_desc &L, const void *x, const float *wr, in
   if (L.E <= 8) return launch_tpl<DT, 8, 1>(L, x, wr, idx, w, logits, st);
   if (L.E <= 16) return launch_tpl<DT, 16, 1>(L, x, wr, idx, w, logits, st);
   if (L.E <= 32) return launch_tpl<DT, 32, 1>(L, x, wr, idx, w, logits, st);
-  if (L.E <= 64) return launch_tpl<DT, 64, 1>(L, x, wr, idx, w, logits, st);
-  return launch_tpl<DT, 64, 2>(L, x, wr, idx, w, logits, st);
+  // Wider routers: each 16-byte LDS read (4 columns of one router row, or of
+  // one token's X broadcast to a segment) feeds more FMAs when a lane holds
+  // several experts and several tokens, and per CU the LDS serves about one
+  // 16-byte wave read per ~5 cycles against one wave FMA per ~2 cycles.  So
+  // 16-lane segments with 4 or 8 experts per lane when there are tokens
+  // enough for two waves per SIMD (DeepSeek-V2-Lite-shaped layer, T = 16384:
+  // 111 -> 95 us; stress layer, 128 experts: 537 -> 456 us, same-process
+  // A/B; logits and indices identical, the gate weights within 3e-7, their
+  // softmax sums taken in another order).  With fewer tokens (T = 4096) the
+  // whole-wave segments with DPP broadcasts stay faster (42 against 48 us).
+  if (L.E <= 64) {
+    if (L.T >= 16384) return launch_tpl<DT, 16, 4>(L, x, wr, idx, w, logits, st);
+    return launch_tpl<DT, 64, 1>(L, x, wr, idx, w, logits, st);
+  }
+  return launch_tpl<DT, 16, 8>(L, x, wr, idx, w, logits, st);
 }
 
 }  // namespace

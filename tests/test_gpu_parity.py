@@ -87,6 +87,43 @@ def test_routing_ties_lower_index_first(orc):
     compare(g, o, inp)
 
 
+@pytest.mark.parametrize("T,E,k,renorm", [
+    (16384, 64, 16, 0),   # 16-lane segments, 4 experts per lane (T >= 16384)
+    (16383, 64, 6, 1),    # the same with a ragged last block
+    (4096, 64, 8, 0),     # whole-wave segments with DPP broadcasts
+    (3001, 128, 16, 0),   # 16-lane segments, 8 experts per lane, k = segment width
+    (20000, 100, 6, 1),   # 8 experts per lane, lanes past E idle
+])
+def test_routing_lane_mappings(orc, T, E, k, renorm):
+    """Routing alone on the token and expert counts that select each lane
+    mapping of the routing kernel: logits and indices bit for bit, weights
+    within the fp32 tolerance."""
+    import torch
+
+    import expert_top_router_amd as etr
+    from expert_top_router_amd.layer import router_f32, to_device
+    from tests.tolerance import assert_close
+
+    d = 192  # an odd number of LDS chunks
+    cfg = W.LayerConfig("route_map", T=T, d=d, E=E, I=64, k=k, D=4, dtype="bf16",
+                        renorm=renorm)
+    inp = W.make_layer(cfg, seed=11)
+    say(f"routing T={T} E={E} k={k}")
+    lg, idx, w = orc.route(inp.x, inp.w_router, k, renorm, "bf16")
+    dev = torch.device("cuda")
+    x = to_device(inp.x)
+    wr = to_device(router_f32(inp.w_router))
+    g_idx = torch.full((T, k), -7, dtype=torch.int32, device=dev)
+    g_w = torch.zeros((T, k), dtype=torch.float32, device=dev)
+    g_lg = torch.zeros((T, E), dtype=torch.float32, device=dev)
+    etr.occ_route_topk(etr.desc_of(cfg), x, wr, g_idx, g_w, g_lg)
+    torch.cuda.synchronize()
+    assert np.array_equal(g_lg.cpu().numpy().view(np.uint32),
+                          np.asarray(lg, np.float32).view(np.uint32))
+    assert np.array_equal(g_idx.cpu().numpy(), idx)
+    assert_close(g_w.cpu().numpy(), w, "f32", "topk_w")
+
+
 def test_coactivation_accumulates(orc):
     import torch
     from expert_top_router_amd.layer import MoELayer, upload_inputs
