@@ -210,25 +210,39 @@ __global__ __launch_bounds__(kTB * kWB) void brim_fill_kernel(
     int32_t *slot_offset, int32_t *S_out) {
   __shared__ int32_t base[OCC_MAX_D + OCC_MAX_E];
   const int lane = threadIdx.x % kTB, wv = threadIdx.x / kTB;
-  // key prefixes (wave 0): devices and slots are two separate exclusive scans
-  int32_t S = 0, R = 0;
-  if (wv == 0) {
-    S = wave_exclusive(tot, D, base);
-    R = wave_exclusive(tot + D, E, base + D);
-  }
-  __syncthreads();
-  if (wv == 0 && blockIdx.x == 0) {
-    for (int c = lane; c <= D; c += kTB) sfd_offset[c] = c == D ? S : base[c];
-    for (int c = lane; c <= E; c += kTB) slot_offset[c] = c == E ? R : base[D + c];
-    if (lane == 0) S_out[0] = S;
-  }
-  if (nblk == 0) return;  // no tokens: only the offsets above (uniform over the block)
-  if (wv == 0)
-    for (int c = lane; c < D + E; c += kTB) base[c] += within[(size_t)c * nblk + blockIdx.x];
-  __syncthreads();
+  // The token's keys and this block's per-key prefixes are loaded first:
+  // neither depends on the key totals, so their latency overlaps the scans.
   const int t = blockIdx.x * kTB + lane;
   const bool live = t < T;
   const TokenKeys<KMAX> tk = load_keys<KMAX>(t, T, k, L, idx, w, pl, pr);
+  constexpr int KR = (OCC_MAX_D + OCC_MAX_E + kTB - 1) / kTB;  // keys per lane
+  int32_t win[KR];
+#pragma unroll
+  for (int r = 0; r < KR; ++r) {
+    const int c = lane + kTB * r;
+    win[r] = wv == 0 && nblk > 0 && c < D + E ? within[(size_t)c * nblk + blockIdx.x] : 0;
+  }
+  // key prefixes (wave 0): devices and slots are two separate exclusive
+  // scans; block 0 writes them out, then each key's base moves on by this
+  // block's prefix inside the key
+  if (wv == 0) {
+    const int32_t S = wave_exclusive(tot, D, base);
+    const int32_t R = wave_exclusive(tot + D, E, base + D);
+    // other lanes wrote those entries: order the reads after their writes
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (blockIdx.x == 0) {
+      for (int c = lane; c <= D; c += kTB) sfd_offset[c] = c == D ? S : base[c];
+      for (int c = lane; c <= E; c += kTB) slot_offset[c] = c == E ? R : base[D + c];
+      if (lane == 0) S_out[0] = S;
+    }
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+      const int c = lane + kTB * r;
+      if (c < D + E) base[c] += win[r];
+    }
+  }
+  if (nblk == 0) return;  // no tokens: only the offsets above (uniform over the block)
+  __syncthreads();
   const uint64_t lt = lanemask_lt();
   for (int dv = wv; dv < D; dv += kWB) {
     const bool hasd = live && ((tk.dmask >> dv) & 1u);
