@@ -59,7 +59,7 @@ def parse():
                    help="skip the secondary workloads (the other bf16 layers)")
     p.add_argument("--cpu-route-tokens", type=int, default=4096,
                    help="oracle baseline: tokens of the sub-batch routed and re-indexed")
-    p.add_argument("--cpu-sample-tokens", type=int, default=448,
+    p.add_argument("--cpu-sample-tokens", type=int, default=768,
                    help="oracle baseline: tokens whose expert FFN and combine are timed")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many forward steps (for rocprofv3), print nothing else")
