@@ -140,10 +140,10 @@ __global__ __launch_bounds__(THR) void route_topk_kernel(
   // general loop measured faster before this loop was software-pipelined.
   // On whole chunks the reads of the next 16 columns are issued before the
   // FMAs of these (scheduling barriers keep the compiler from sinking them):
-  // OLMoE-shaped layer 48 -> 43 us; with it, one expert and 8 tokens per lane
-  // (DeepSeek-V2-Lite-shaped layer) also gain (116 -> 111 us), while two
-  // experts per lane (128 experts) stay on the general loop (543 against
-  // 680 us).  jn is a multiple of 8.
+  // OLMoE-shaped layer 48 -> 43 us.  A DPP-broadcast FMA issues at about
+  // half the rate of a plain one, so routers with tokens enough for several
+  // per lane take 16-lane segments instead (the launcher).  jn is a multiple
+  // of 8.
   constexpr bool BC = ESEG == kWave && (TPL <= 2 || EP == 1);
   auto chunk_bcast = [&](const float *wsc, const float *xsc, int jn) {
     const int xl = lane & 15;
@@ -211,8 +211,8 @@ __global__ __launch_bounds__(THR) void route_topk_kernel(
   // (TPL * EP <= 4) the loop is latency-bound, and on whole chunks the reads
   // of the next 4 columns go out before the FMAs of these (two register
   // sets, scheduling barriers keep the order): Mixtral-shaped layer
-  // 73 -> 46 us.  With 16 chains per lane that order measured slower
-  // (544 -> 665 us on the 128-expert layer) and is not used.
+  // 73 -> 46 us.  With more chains per lane it is not used: on the
+  // 128-expert layer 32 chains gain nothing with it and 64 spill.
   auto fma4 = [&](const float4 *wv, const float4 *xv) {
     // j ascending inside every chain; the TPL*EP chains interleave
 #pragma unroll
