@@ -209,10 +209,12 @@ __global__ __launch_bounds__(THR) void route_topk_kernel(
   // General loop: per 4 columns, one 16-byte router read per expert and one
   // segment-broadcast 16-byte X read per token.  With few chains per lane
   // (TPL * EP <= 4) the loop is latency-bound, and on whole chunks the reads
-  // of the next 4 columns go out before the FMAs of these (two register
-  // sets, scheduling barriers keep the order): Mixtral-shaped layer
-  // 73 -> 46 us.  With more chains per lane it is not used: on the
+  // of the 4-column groups up to kAhead ahead go out before the FMAs of this
+  // one (a ring of kAhead + 1 register sets; scheduling barriers keep the
+  // order): Mixtral-shaped layer 73 -> 46 us with one group ahead, 42 with
+  // three (seven: 42).  With more chains per lane it is not used: on the
   // 128-expert layer 32 chains gain nothing with it and 64 spill.
+  constexpr int kAhead = 3;
   auto fma4 = [&](const float4 *wv, const float4 *xv) {
     // j ascending inside every chain; the TPL*EP chains interleave
 #pragma unroll
@@ -242,14 +244,16 @@ __global__ __launch_bounds__(THR) void route_topk_kernel(
         xv[m] = *reinterpret_cast<const float4 *>(&xsc[(wave * TW + q + Q * m) * kLds + jj]);
     };
     if (TPL * EP <= 4 && jn == kJC) {
-      float4 wv[2][EP], xv[2][TPL];
-      load4(0, wv[0], xv[0]);
+      constexpr int kSets = kAhead + 1;
+      float4 wv[kSets][EP], xv[kSets][TPL];
+#pragma unroll
+      for (int s = 0; s < kAhead; ++s) load4(4 * s, wv[s], xv[s]);
 #pragma unroll
       for (int jj = 0; jj < kJC; jj += 4) {
-        const int cs = (jj / 4) & 1;
-        if (jj + 4 < kJC) load4(jj + 4, wv[cs ^ 1], xv[cs ^ 1]);
+        const int gi = jj / 4, nx = (gi + kAhead) % kSets;
+        if (jj + 4 * kAhead < kJC) load4(jj + 4 * kAhead, wv[nx], xv[nx]);
         __builtin_amdgcn_sched_barrier(0);
-        fma4(wv[cs], xv[cs]);
+        fma4(wv[gi % kSets], xv[gi % kSets]);
         __builtin_amdgcn_sched_barrier(0);
       }
       return;
