@@ -19,9 +19,9 @@ arrays.  Steps and their sources (page and passage):
 * brute force without deduplication (O13) -- Occult, Abstract (exact results).
 * co-activation counts (O12) and intra-collaboration share -- Occult,
   Abstract; greedy correlated placement (O-P) -- Expert Coupling, Abstract and
-  Occult TL;DR (expert-placement rescheduling).  The greedy is a heuristic:
-  its optimality is parity unpinned; its output is pinned by properties and a
-  planted-block case.
+  Occult TL;DR (expert-placement rescheduling).  The greedy is a heuristic
+  and no optimality is claimed; the output of the rule is pinned by
+  properties, a hand-worked case and a planted-block case.
 """
 from __future__ import annotations
 

@@ -27,8 +27,10 @@ Top-k selection is a constant of the backward.  dtype "f64" skips every
 rounding (used by the finite-difference pins).  Under collaboration pruning
 the BRIMs hold only the kept picks with their stored (rescaled) weights: the
 expert part is the exact gradient of that layer, and in the routing gradient
-a kept pick carries its stored weight's gradient and a dropped one none
-(the pruning decision and the rescaling factor are held constant).
+a kept pick carries its stored weight's gradient and a dropped one none (the
+pruning decision is held constant and the rescaling factor is ignored: the
+exact derivative of the layer whose kept weights are the routing weights
+plus constants equal to the rescaling's change at the evaluation point).
 """
 from __future__ import annotations
 

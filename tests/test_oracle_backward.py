@@ -232,6 +232,59 @@ def test_pruned_routing_gradient_matches_finite_differences(orc, renorm):
             assert abs(fd - grad[pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
 
 
+
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_rescaled_pruned_routing_gradient_matches_finite_differences(orc, renorm):
+    """Collaboration pruning with rescaling (budget 1 of 2 devices): the
+    routing gradient passes each kept pick's stored-weight gradient through
+    the softmax backward unchanged (the rescaling factor is ignored there).
+    That is the exact derivative of the layer whose kept weights are the
+    routing weights plus constants that make them equal the stored rescaled
+    weights at the base point: dW_router and dx against central finite
+    differences of that layer (the expert part uses the stored weights)."""
+    ob = _ob()
+    cfg, inp = _layer(seed=7, renorm=renorm, k=4, E=8, D=2)
+    x, wr, wgu, wdn = (np.asarray(a, np.float64) for a in (inp.x, inp.w_router, inp.w_gate_up,
+                                                           inp.w_down))
+    lg, idx, w = orc.route(inp.x, inp.w_router, cfg.k, renorm, "f32")
+    ik, wk = orc.prune(idx, w, inp.slot_expert, cfg.E, cfg.D, 1, 1)
+    assert np.any(ik < 0) and np.all((ik < 0) | (ik == idx))
+    b = orc.brim(ik, wk, inp.slot_expert, cfg.E, cfg.D)
+    rng = np.random.default_rng(9)
+    dy = rng.standard_normal(x.shape)
+    g = ob.full(x, wr, wgu, wdn, lg, idx, w, renorm, b, inp.slot_expert, dy, cfg.D, "f64")
+
+    def routing_weights(x_, wr_):
+        lg_ = x_ @ wr_.T
+        p = np.exp(lg_ - lg_.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        ws = np.take_along_axis(p, idx, axis=1)
+        if renorm:
+            ws = ws / ws.sum(axis=1, keepdims=True)
+        return np.where(ik >= 0, ws, 0.0)
+
+    # the constants: stored (rescaled) weight minus routing weight at the base
+    shift = np.where(ik >= 0, np.asarray(wk, np.float64), 0.0) - routing_weights(x, wr)
+    assert np.abs(shift).max() > 1e-3  # rescaling moved the kept weights
+
+    def loss(x_, wr_):
+        return float(np.sum(dy * fwd_kept64(x_, wgu, wdn, ik, routing_weights(x_, wr_) + shift)))
+
+    eps = 1e-6
+    for name, arr, grad in [("w_router", wr, g["dW_router"]), ("x", x, g["dx"])]:
+        for _ in range(8):
+            pos = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            if name == "x":  # a token that lost a device
+                pos = (int(rng.choice(np.flatnonzero(np.any(ik < 0, axis=1)))), pos[1])
+            plus, minus = arr.copy(), arr.copy()
+            plus[pos] += eps
+            minus[pos] -= eps
+            if name == "w_router":
+                fd = (loss(x, plus) - loss(x, minus)) / (2 * eps)
+            else:
+                fd = (loss(plus, wr) - loss(minus, wr)) / (2 * eps)
+            assert abs(fd - grad[pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+
 def test_slot_weight_grads_pinned(orc):
     """slot_weight_grads (the reference for the weight gradients of sampled
     slots at full size) under a non-identity placement: for every slot it
