@@ -447,8 +447,13 @@ def stage_times(lay, cfg, n, torch):
     S = int(lay.host("S")[0])
     alg = algorithmic(cfg, S)
     peak_mfma = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    filtered = bool(lay.logits is None and lay.route_filtered and lay.route_ws is not None)
     return {
         "route_us": t["route"] * 1e6,
+        # the candidate filter (occ_route_topk_ws) runs the chains of only the
+        # certified candidates: against the plain kernel's 2 T d E flop this is
+        # an equivalent rate, not the VALU's own
+        "route_path": "candidate filter" if filtered else "every chain",
         "route_valu_frac": alg["route_flop"] / t["route"] / 1e12 / PEAK_F32_VALU_TFLOPS,
         "route_hbm_frac": alg["route_bytes"] / t["route"] / 1e9 / PEAK_HBM_GBS,
         "build_brim_us": t["build_brim"] * 1e6,

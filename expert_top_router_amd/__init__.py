@@ -50,6 +50,8 @@ def _load(path: str = LIB_PATH):
         "occ_workspace_bytes": (SZ, [DP]),
         "occ_ffn_workspace_bytes": (SZ, [DP]),
         "occ_route_topk": (I32, [DP, P, P, P, P, P, P]),
+        "occ_route_workspace_bytes": (SZ, [DP]),
+        "occ_route_topk_ws": (I32, [DP, P, P, P, P, P, SZ, P]),
         "occ_build_brim": (I32, [DP, P, P, P, BP, P, SZ, P]),
         "occ_build_brim_pruned": (I32, [DP, P, P, P, I32, I32, BP, P, SZ, P]),
         "occ_build_brim_noalloc": (I32, [DP, P, P, P, BP, P]),
@@ -85,7 +87,8 @@ def _load(path: str = LIB_PATH):
 _lib = _load()
 
 # Every symbol the C header declares (checked by the tests).
-EXPORTED = ("occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk", "occ_build_brim",
+EXPORTED = ("occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk",
+            "occ_route_workspace_bytes", "occ_route_topk_ws", "occ_build_brim",
             "occ_build_brim_pruned", "occ_build_brim_noalloc",
             "occ_dispatch", "occ_expert_ffn", "occ_expert_up", "occ_expert_down", "occ_combine",
             "occ_dispatch_direct", "occ_combine_direct", "occ_backward_workspace_bytes",
@@ -158,6 +161,16 @@ def occ_ffn_workspace_bytes(desc: occ_layer_desc) -> int:
 def occ_route_topk(desc, x, w_router, topk_idx, topk_w, logits=None, stream=None):
     _check(_lib.occ_route_topk(C.byref(desc), _ptr(x), _ptr(w_router), _ptr(topk_idx),
                                _ptr(topk_w), _ptr(logits), _stream(stream)), "occ_route_topk")
+
+
+def occ_route_workspace_bytes(desc: occ_layer_desc) -> int:
+    return int(_lib.occ_route_workspace_bytes(C.byref(desc)))
+
+
+def occ_route_topk_ws(desc, x, w_router, topk_idx, topk_w, ws, ws_bytes, stream=None):
+    _check(_lib.occ_route_topk_ws(C.byref(desc), _ptr(x), _ptr(w_router), _ptr(topk_idx),
+                                  _ptr(topk_w), _ptr(ws), int(ws_bytes), _stream(stream)),
+           "occ_route_topk_ws")
 
 
 def occ_build_brim(desc, topk_idx, topk_w, slot_expert_host, brim: occ_brim, ws, ws_bytes,
@@ -349,6 +362,7 @@ from .layer import MoELayer  # noqa: E402  (buffers + the call sequence)
 
 __all__ = ["MoELayer", "OccError", "occ_layer_desc", "occ_brim", "make_desc", "desc_of",
            "make_brim", "occ_workspace_bytes", "occ_ffn_workspace_bytes", "occ_route_topk",
+           "occ_route_workspace_bytes", "occ_route_topk_ws",
            "occ_build_brim", "occ_build_brim_noalloc", "occ_build_brim_pruned", "occ_dispatch", "occ_expert_ffn", "occ_expert_up",
            "occ_expert_down", "occ_combine", "occ_dispatch_direct", "occ_combine_direct",
            "occ_backward_workspace_bytes", "occ_grad_combine", "occ_expert_backward",

@@ -147,6 +147,31 @@ occ_status occ_route_topk(const occ_layer_desc *desc, const void *x, const float
                     "occ_route_topk");
 }
 
+size_t occ_route_workspace_bytes(const occ_layer_desc *desc) {
+  if (check_desc(desc) != OCC_OK) return 0;
+  return occ::route_filter_workspace_bytes(*desc);
+}
+
+occ_status occ_route_topk_ws(const occ_layer_desc *desc, const void *x, const float *w_router,
+                             int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  OCC_TRY(check_desc(desc));
+  const int64_t Td = (int64_t)desc->T * desc->d, Tk = (int64_t)desc->T * desc->k;
+  if (missing(x, Td) || !w_router || missing(topk_idx, Tk) || missing(topk_w, Tk))
+    return fail(OCC_EINVAL, "x, w_router, topk_idx and topk_w must be set");
+  if (!occ::route_filter_applies(*desc))
+    return hip_status(
+        occ::launch_route_topk(*desc, x, w_router, topk_idx, topk_w, nullptr, stream),
+        "occ_route_topk_ws");
+  const size_t need = occ::route_filter_workspace_bytes(*desc);
+  if (ws == nullptr) return fail(OCC_EINVAL, "workspace is NULL");
+  if (ws_bytes < need)
+    return fail(OCC_ENOSPC, "workspace of %zu bytes < %zu required", ws_bytes, need);
+  return hip_status(
+      occ::launch_route_filtered(*desc, x, w_router, topk_idx, topk_w, ws, stream),
+      "occ_route_topk_ws");
+}
+
 static occ_status build_brim(const char *name, const occ_layer_desc *desc,
                              const int32_t *topk_idx, const float *topk_w,
                              const int32_t *slot_expert_host, const occ_brim *brim, void *ws,

@@ -76,6 +76,12 @@ int device_cu_count();
 // ---- launchers (each returns hipGetLastError() of its launches) -----------
 hipError_t launch_route_topk(const occ_layer_desc &L, const void *x, const float *wr,
                              int32_t *idx, float *w, float *logits, hipStream_t st);
+// filtered routing (occ_route_topk_ws): applies to bf16 layers with
+// 32 <= E <= 128, k <= 16, d % 64 == 0
+bool route_filter_applies(const occ_layer_desc &L);
+size_t route_filter_workspace_bytes(const occ_layer_desc &L);
+hipError_t launch_route_filtered(const occ_layer_desc &L, const void *x, const float *wr,
+                                 int32_t *idx, float *w, void *ws, hipStream_t st);
 
 // workspace layout of the BRIM build: counts then scanned offsets
 size_t brim_workspace_bytes(int T, int D, int E);

@@ -1,0 +1,603 @@
+// Routing through a certified candidate filter (bf16 tokens, no logits
+// output).
+//
+// Expert Coupling in MoE Pretraining, Abstract: each token is routed to k of
+// the E experts.  The selection is defined on the in-order fp32 FMA chain
+// l[t][e] = fma(x[t][d-1], w[e][d-1], ... fma(x[t][0], w[e][0], 0)); only
+// the experts that can be among a token's k largest chains need the chain.
+//
+//   prep:    router rows to bf16 (h = RNE(w), residual r = w - h) in the
+//            workspace, and per expert the bound factor
+//            B_e = 1.01 (2 d u |h_e| + 1.01 d u |w_e| + |r_e|), u = 2^-24
+//   approx:  a[t][e] = sum_j x[t][j] h[e][j] with bf16 MFMA (exact products,
+//            fp32 accumulation), and |x_t|
+//   exact:   |a - l| <= |x_t| B_e: the MFMA sum and the chain each carry at
+//            most 2 d u (resp. 1.01 d u) times sum_j |x_j h_j| (|x_j w_j|),
+//            bounded by Cauchy-Schwarz, and the residual adds sum_j |x_j r_j|.
+//            With delta_t = 1.01 |x_t| max_e B_e and a_(k) the k-th largest
+//            a, every expert of the true top k has a >= a_(k) - 2 delta_t
+//            (the true k-th largest chain is >= a_(k) - delta_t), and every
+//            other expert has a chain strictly below it, so the top k of the
+//            chains over those candidates is the top k over all experts, ties
+//            included.  The candidates' chains run in order in fp32 like the
+//            full kernel's, so logits and indices are the same bit for bit.
+//            The softmax denominator takes the candidates' chains and the
+//            other experts' approximate logits (a relative change of the
+//            order of their rounding, as between two summation orders).
+//            A block with a token of more than kCap candidates, or with a
+//            non-finite approximate logit or norm, runs every chain of every
+//            token instead (then identical to the full kernel up to the order
+//            of the softmax sum), and so does every block when a router row is
+//            not bf16-exact (the approximate logits then carry the rows'
+//            rounding, too coarse for the other experts' share of the softmax
+//            sum; correct, but slower than the full kernel).
+#include <type_traits>
+
+#include "occ_internal.h"
+
+namespace occ {
+namespace {
+
+typedef __bf16 fbf16x8 __attribute__((ext_vector_type(8)));
+typedef float ff32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t fu32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kCap = 16;      // candidates per token
+constexpr int kTok = 128;     // tokens per block (approx and exact kernels)
+constexpr int kNT = 512;      // threads per block (8 waves)
+constexpr float kU = 5.9604645e-8f;  // 2^-24
+
+struct FilterWs {
+  uint16_t *wh;  // [E][d] bf16 router
+  float *bnd;    // [E] bound factor B_e
+  int32_t *ex;   // [E] 1 when the row is bf16-exact
+  float *ag;     // [T][E] approximate logits
+  float *xn;     // [T] |x_t|
+};
+
+size_t a256(size_t n) { return (n + 255) / 256 * 256; }
+
+FilterWs carve(const occ_layer_desc &L, void *ws) {
+  char *p = static_cast<char *>(ws);
+  FilterWs f;
+  f.wh = reinterpret_cast<uint16_t *>(p);
+  p += a256((size_t)L.E * L.d * 2);
+  f.bnd = reinterpret_cast<float *>(p);
+  p += a256((size_t)L.E * 4);
+  f.ex = reinterpret_cast<int32_t *>(p);
+  p += a256((size_t)L.E * 4);
+  f.ag = reinterpret_cast<float *>(p);
+  p += a256((size_t)L.T * L.E * 4);
+  f.xn = reinterpret_cast<float *>(p);
+  return f;
+}
+
+// ---- prep: one block per router row ---------------------------------------
+__global__ __launch_bounds__(256) void route_prep_kernel(int d, const float *__restrict__ wr,
+                                                         uint16_t *__restrict__ wh,
+                                                         float *__restrict__ bnd,
+                                                         int32_t *__restrict__ ex) {
+  __shared__ float red[3][4];
+  __shared__ int redx[4];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float sw = 0.0f, sh = 0.0f, sr = 0.0f;
+  int exact = 1;
+  const float4 *src = reinterpret_cast<const float4 *>(wr + (size_t)e * d);
+  fu32x2 *dst = reinterpret_cast<fu32x2 *>(wh + (size_t)e * d);
+  for (int i = tid; i < d / 4; i += 256) {
+    const float4 v = src[i];
+    const float w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t hb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      hb[c] = f32_to_bf16(w[c]);
+      const float h = __uint_as_float(hb[c] << 16), r = w[c] - h;
+      sw = __builtin_fmaf(w[c], w[c], sw);
+      sh = __builtin_fmaf(h, h, sh);
+      sr = __builtin_fmaf(r, r, sr);
+      exact &= r == 0.0f ? 1 : 0;
+    }
+    dst[i] = fu32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    sw += __shfl_xor(sw, off);
+    sh += __shfl_xor(sh, off);
+    sr += __shfl_xor(sr, off);
+    exact &= __shfl_xor(exact, off);
+  }
+  if (lane == 0) {
+    red[0][wave] = sw;
+    red[1][wave] = sh;
+    red[2][wave] = sr;
+    redx[wave] = exact;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const float a = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    const float b = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    const float c = red[2][0] + red[2][1] + red[2][2] + red[2][3];
+    const float du = (float)d * kU;
+    bnd[e] = 1.01f * (2.0f * du * sqrtf(b) + 1.01f * du * sqrtf(a) + sqrtf(c));
+    ex[e] = redx[0] & redx[1] & redx[2] & redx[3];
+  }
+}
+
+// ---- approx: 128 tokens x 32*EB experts per block, bf16 MFMA ---------------
+// v_mfma_f32_32x32x16_bf16 with the token fragment first: lane l supplies
+// row (token or expert) l % 32 and the 8 k values 8*(l/32)..+7 of a 16-deep
+// step; output element r of lane l is token 8*(r/4) + 4*(l/32) + r%4 of the
+// tile, expert l % 32.
+template <int EB>
+__global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
+                                                           const uint16_t *__restrict__ x,
+                                                           const uint16_t *__restrict__ wh,
+                                                           float *__restrict__ ag,
+                                                           float *__restrict__ xn) {
+  constexpr int EPAD = 32 * EB;
+  constexpr int JA = 64, LA = JA + 8;  // k-chunk and padded row stride (bf16)
+  constexpr int XC = kTok * JA / 8 / kNT;
+  constexpr int WCH = EPAD * JA / 8;   // 16-byte router chunks per k-chunk
+  constexpr int WC = (WCH + kNT - 1) / kNT;
+  static_assert(XC * kNT * 8 == kTok * JA, "whole token chunks");
+  __shared__ __attribute__((aligned(16))) uint16_t xa[2][kTok * LA];
+  __shared__ __attribute__((aligned(16))) uint16_t wa[2][EPAD * LA];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * kTok;
+  const int nch = d / JA;
+  constexpr int NTILE = 4 * EB;
+  constexpr int TPW = NTILE >= 8 ? NTILE / 8 : 1;
+  const int id0 = wave * TPW;
+  const bool wact = id0 < NTILE;  // uniform
+  const int tb = id0 / EB;
+
+  u32x4 rx[XC], rw[WC];
+  float sx[XC];
+#pragma unroll
+  for (int u = 0; u < XC; ++u) sx[u] = 0.0f;
+  // Loads are unconditional (rows past T or E re-read the last one; no
+  // output takes them), so the compiler's waits can count them.
+  auto load = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < XC; ++u) {
+      const int c = tid + kNT * u, r = c >> 3, cc = (c & 7) * 8, t = min(t0 + r, T - 1);
+      rx[u] = *reinterpret_cast<const u32x4 *>(x + (size_t)t * d + j0 + cc);
+    }
+#pragma unroll
+    for (int u = 0; u < WC; ++u) {
+      const int c = min(tid + kNT * u, WCH - 1), r = min(c >> 3, E - 1), cc = (c & 7) * 8;
+      rw[u] = *reinterpret_cast<const u32x4 *>(wh + (size_t)r * d + j0 + cc);
+    }
+  };
+  auto store = [&](int st, bool norm) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < XC; ++u) {
+      const int c = tid + kNT * u, r = c >> 3, cc = (c & 7) * 8;
+      *reinterpret_cast<u32x4 *>(&xa[st][r * LA + cc]) = rx[u];
+      if (norm) {  // not for the re-read past the last chunk
+        float f[8];
+        widen<OCC_BF16>(rx[u], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sx[u] = __builtin_fmaf(f[i], f[i], sx[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < WC; ++u) {
+      const int c = tid + kNT * u, r = c >> 3, cc = (c & 7) * 8;
+      if (c < WCH) *reinterpret_cast<u32x4 *>(&wa[st][r * LA + cc]) = rw[u];
+    }
+  };
+  ff32x16 acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+  // the loads past the last chunk re-read it (in bounds), so every iteration
+  // issues the same loads and the compiler's waits stay partial
+  load(0);
+  store(0, true);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    load(min(ch + 1, nch - 1) * JA);
+    const int st = ch & 1;
+    if (wact) {
+#pragma unroll
+      for (int s = 0; s < JA / 16; ++s) {
+        const int ko = s * 16 + (lane >> 5) * 8;
+        const fbf16x8 af =
+            *reinterpret_cast<const fbf16x8 *>(&xa[st][(tb * 32 + (lane & 31)) * LA + ko]);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+          const int eb = (id0 + i) % EB;
+          const fbf16x8 bv =
+              *reinterpret_cast<const fbf16x8 *>(&wa[st][(eb * 32 + (lane & 31)) * LA + ko]);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bv, acc[i], 0, 0, 0);
+        }
+      }
+    }
+    store((ch + 1) & 1, ch + 1 < nch);
+    __syncthreads();
+  }
+  if (wact) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int e = ((id0 + i) % EB) * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + tb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (t < T && e < E) ag[(size_t)t * E + e] = acc[i][r];
+      }
+    }
+  }
+  // |x_t|: the 8 threads of a token row are consecutive lanes
+#pragma unroll
+  for (int u = 0; u < XC; ++u) {
+    float v = sx[u];
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    const int t = t0 + ((tid + kNT * u) >> 3);
+    if ((tid & 7) == 0 && t < T) xn[t] = sqrtf(v);
+  }
+}
+
+// ---- exact: certify, run the candidates' chains, softmax and top-k ---------
+// Chains: lane = token 64 * (wave / 4) + lane, slots q = (wave % 4) + 4 i of
+// that token's candidate list.  X is staged as bf16 (widened when read, one
+// 16-byte read per 8 columns), the router as bf16 when every row is
+// bf16-exact (else fp32), four chunks of loads ahead in registers; 69 KB
+// of LDS lets two blocks share a CU.
+// (four waves per SIMD: two blocks per CU)
+template <int EB>
+__global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
+    int T, int d, int E, int k, int renorm, const uint16_t *__restrict__ x,
+    const float *__restrict__ wr, const uint16_t *__restrict__ wh, const float *__restrict__ bnd,
+    const int32_t *__restrict__ ex, float *__restrict__ agg, const float *__restrict__ xng,
+    int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+  constexpr int EPAD = 32 * EB;
+  constexpr int JB = 32;                     // columns per chunk
+  constexpr int LX = JB + 8, LW = JB + 4;    // row strides: bf16 X, fp32 router
+  constexpr int KPF = 4;                     // register sets of loads in flight
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kTok * LX];
+  __shared__ __attribute__((aligned(16))) float ws[2][EPAD * LW];
+  __shared__ float exl[kTok][kCap];
+  __shared__ uint8_t cl[kTok][kCap];
+  __shared__ int32_t nc[kTok];
+  __shared__ float am[kTok], znc[kTok];
+  __shared__ int all_flag;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * kTok;
+  if (tid == 0) all_flag = 0;
+  float bmax = 0.0f;
+  int rexact = 1;
+  for (int e = lane; e < E; e += 64) {
+    bmax = fmaxf(bmax, bnd[e]);
+    rexact &= ex[e];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    bmax = fmaxf(bmax, __shfl_xor(bmax, off));
+    rexact &= __shfl_xor(rexact, off);
+  }
+  __syncthreads();
+
+  // candidates of each token (16 per wave), from the approximate logits
+  const uint64_t lt = lanemask_lt();
+  for (int tt = wave; tt < kTok; tt += kNT / 64) {
+    const int t = t0 + tt;
+    if (t >= T) {
+      if (lane == 0) nc[tt] = 0;
+      continue;
+    }
+    const int e0 = lane, e1 = lane + 64;
+    const bool l0 = e0 < E, l1 = EPAD > 64 && e1 < E;
+    const float a0 = l0 ? agg[(size_t)t * E + e0] : 0.0f;
+    const float a1 = l1 ? agg[(size_t)t * E + e1] : 0.0f;
+    const bool bad = (l0 && !isfinite(a0)) || (l1 && !isfinite(a1));
+    bool v0 = l0, v1 = l1;
+    float kth = -INFINITY, amax = -INFINITY;
+    for (int j = 0; j < k; ++j) {
+      float m = fmaxf(v0 ? a0 : -INFINITY, v1 ? a1 : -INFINITY);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      if (j == 0) amax = m;
+      kth = m;
+      // retire one expert holding the maximum (the lowest index)
+      const uint64_t h0 = __ballot(v0 && a0 == m), h1 = __ballot(v1 && a1 == m);
+      if (h0 != 0) {
+        if (lane == __ffsll((long long)h0) - 1) v0 = false;
+      } else if (h1 != 0) {
+        if (lane == __ffsll((long long)h1) - 1) v1 = false;
+      }
+    }
+    const float delta = xng[t] * bmax * 1.01f;
+    const float theta = kth - 2.0f * delta;
+    const bool c0 = l0 && a0 >= theta, c1 = l1 && a1 >= theta;
+    const uint64_t m0 = __ballot(c0), m1 = __ballot(c1);
+    const int cnt = __popcll(m0) + __popcll(m1);
+    const bool anybad = __ballot(bad) != 0;
+    if (anybad || !isfinite(theta) || !isfinite(amax) || cnt > kCap) {
+      if (lane == 0) {
+        nc[tt] = -1;
+        all_flag = 1;
+      }
+      continue;
+    }
+    if (c0) cl[tt][__popcll(m0 & lt)] = (uint8_t)e0;
+    if (c1) cl[tt][__popcll(m0) + __popcll(m1 & lt)] = (uint8_t)e1;
+    // the other experts' share of the softmax sum, relative to amax
+    float z = (l0 && !c0 ? expf(a0 - amax) : 0.0f) + (l1 && !c1 ? expf(a1 - amax) : 0.0f);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+    if (lane == 0) {
+      nc[tt] = cnt;
+      am[tt] = amax;
+      znc[tt] = z;
+    }
+  }
+  __syncthreads();
+
+  // every chain when a token could not be certified, or when the router rows
+  // are not bf16-exact: then the approximate logits carry the rows' bf16
+  // rounding, too coarse for the softmax sum of the other experts
+  const bool full = all_flag != 0 || !rexact;  // uniform
+  const int npass = full ? (E + kCap - 1) / kCap : 1;
+  const int tl = 64 * (wave >> 2) + lane, sg = wave & 3;
+  const int ntk = t0 + tl < T ? (full ? E : nc[tl]) : 0;
+  constexpr int XCB = kTok * JB / 8 / kNT;   // 16-byte X loads per thread per chunk
+  static_assert(XCB == 1, "one X load per thread and chunk");
+  const int nchb = d / JB;
+  // one pass over d for the chains of slots p * kCap + sg + 4 i.  The
+  // certified path (one pass) writes only LDS, the every-chain path writes
+  // the exact logits back to global memory: kept apart, so that the
+  // barriers of the certified path need not wait for global stores (which
+  // share the completion counter with the loads in flight)
+  auto pass = [&](int p, auto fullc) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(fullc)::value;
+    int ei[4];
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = p * kCap + sg + 4 * i;
+      const bool v = q < ntk;
+      ei[i] = v ? (FULL ? q : (int)cl[tl][q]) : 0;
+      mine += v ? 1 : 0;
+    }
+    int nmax = mine;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nmax = max(nmax, __shfl_xor(nmax, off));
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // One pass over d.  RB: the router rows are bf16-exact and stream from the
+    // workspace's bf16 copy (one 16-byte LDS read per chain and 8 columns,
+    // widened in registers); otherwise fp32 rows (two reads).
+    auto run = [&](auto rbc) __attribute__((always_inline)) {
+      constexpr bool RB = decltype(rbc)::value;
+      constexpr int WCN = RB ? EPAD * JB / 8 : EPAD * JB / 4;  // 16-byte router loads
+      constexpr int WPN = (WCN + kNT - 1) / kNT;
+      constexpr int WPR = RB ? JB / 8 : JB / 4;                // loads per router row
+      // register ring: set (c % KP) holds chunk c until it is stored to LDS
+      // (four sets for bf16 router rows, two for fp32 ones: registers)
+      constexpr int KP = RB ? KPF : 2;
+      u32x4 bx[KP];
+      u32x4 bw[KP][WPN];
+      // Loads are unconditional (rows past T or E re-read the last one, which
+      // no chain or output uses), so the compiler's waits can count them.
+      auto loadb = [&](int c, int set) __attribute__((always_inline)) {
+        const int j0 = c * JB;
+        {
+          const int r = tid / (JB / 8), cc = (tid % (JB / 8)) * 8, t = min(t0 + r, T - 1);
+          bx[set] = *reinterpret_cast<const u32x4 *>(x + (size_t)t * d + j0 + cc);
+        }
+#pragma unroll
+        for (int u = 0; u < WPN; ++u) {
+          const int cw = min(tid + kNT * u, WCN - 1), r = min(cw / WPR, E - 1);
+          const int cc = (cw % WPR) * (RB ? 8 : 4);
+          if (RB) bw[set][u] = *reinterpret_cast<const u32x4 *>(wh + (size_t)r * d + j0 + cc);
+          else bw[set][u] = *reinterpret_cast<const u32x4 *>(wr + (size_t)r * d + j0 + cc);
+        }
+      };
+      auto storeb = [&](int st, int set) __attribute__((always_inline)) {
+        {
+          const int r = tid / (JB / 8), cc = (tid % (JB / 8)) * 8;
+          *reinterpret_cast<u32x4 *>(&xs[st][r * LX + cc]) = bx[set];
+        }
+#pragma unroll
+        for (int u = 0; u < WPN; ++u) {
+          const int cw = tid + kNT * u, r = cw / WPR, cc = (cw % WPR) * (RB ? 8 : 4);
+          if (cw < WCN) {
+            if (RB) *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(ws[st]) + r * LX + cc) = bw[set][u];
+            else *reinterpret_cast<u32x4 *>(&ws[st][r * LW + cc]) = bw[set][u];
+          }
+        }
+      };
+      __syncthreads();  // earlier readers of the staging buffers are done
+      // KPF register sets: set s holds chunk c (c % KPF == s) until it is
+      // stored.  The chunk count is padded to a multiple of KPF; loads and
+      // stores past the last chunk re-read it (in bounds) and only the FMAs
+      // skip it, so every iteration issues the same loads and the compiler's
+      // waits stay partial.
+#pragma unroll
+      for (int c = 0; c < KP; ++c) loadb(min(c, nchb - 1), c);
+      storeb(0, 0);
+      loadb(min(KP, nchb - 1), 0);
+      __syncthreads();
+      auto body = [&](int ch, auto setc) __attribute__((always_inline)) {
+        constexpr int SET = decltype(setc)::value;  // the register set of chunk ch + 1
+        const int st = ch & 1;
+        if (ch < nchb) {
+          const uint16_t *xr = &xs[st][tl * LX];
+#pragma unroll
+          for (int jj = 0; jj < JB; jj += 8) {
+            float xf[8];
+            widen<OCC_BF16>(*reinterpret_cast<const u32x4 *>(xr + jj), xf);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (i < nmax) {
+                float wf[8];
+                if (RB) {
+                  widen<OCC_BF16>(*reinterpret_cast<const u32x4 *>(
+                                      reinterpret_cast<const uint16_t *>(ws[st]) + ei[i] * LX + jj),
+                                  wf);
+                } else {
+                  const float4 wa = *reinterpret_cast<const float4 *>(&ws[st][ei[i] * LW + jj]);
+                  const float4 wb =
+                      *reinterpret_cast<const float4 *>(&ws[st][ei[i] * LW + jj + 4]);
+                  wf[0] = wa.x; wf[1] = wa.y; wf[2] = wa.z; wf[3] = wa.w;
+                  wf[4] = wb.x; wf[5] = wb.y; wf[6] = wb.z; wf[7] = wb.w;
+                }
+                // j ascending inside every chain
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[i] = __builtin_fmaf(xf[c], wf[c], acc[i]);
+              }
+            }
+          }
+        }
+        // chunk ch + 1 to the other stage, its set refilled with chunk
+        // ch + 1 + KP
+        storeb(st ^ 1, SET);
+        loadb(min(ch + 1 + KP, nchb - 1), SET);
+        __syncthreads();
+      };
+      static_assert(KPF == 4 && 4 % KP == 0, "the loop below is unrolled by four");
+      for (int ch = 0; ch < nchb; ch += 4) {
+        body(ch, std::integral_constant<int, 1 % KP>{});
+        body(ch + 1, std::integral_constant<int, 2 % KP>{});
+        body(ch + 2, std::integral_constant<int, 3 % KP>{});
+        body(ch + 3, std::integral_constant<int, 0>{});
+      }
+    };
+    if (FULL) {
+      if (rexact) run(std::true_type{});
+      else run(std::false_type{});
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = p * kCap + sg + 4 * i;
+        if (q < ntk) agg[(size_t)(t0 + tl) * E + q] = acc[i];  // exact, in place
+      }
+    } else {
+      run(std::true_type{});  // certified blocks have a bf16-exact router
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = sg + 4 * i;
+        if (q < ntk) exl[tl][q] = acc[i];
+      }
+    }
+  };
+  if (!full) {
+    pass(0, std::false_type{});
+  } else {
+    for (int p = 0; p < npass; ++p) pass(p, std::true_type{});
+  }
+  __syncthreads();  // also orders the block's global writes of exact logits before the reads
+
+  // softmax (max over the candidates' chains) and top-k among the candidates
+  for (int tt = wave; tt < kTok; tt += kNT / 64) {
+    const int t = t0 + tt;
+    if (t >= T) continue;
+    const int n = full ? 0 : nc[tt];
+    float val[2], key[2], pp[2];
+    bool sel[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = lane + 64 * h;
+      const bool live = (h == 0 || EPAD > 64) && e < E;
+      val[h] = 0.0f;
+      sel[h] = false;
+      if (full && live) {
+        val[h] = agg[(size_t)t * E + e];
+        sel[h] = true;
+      }
+      for (int q = 0; q < n; ++q)
+        if (live && (int)cl[tt][q] == e) {
+          val[h] = exl[tt][q];
+          sel[h] = true;
+        }
+      key[h] = sel[h] ? (isnan(val[h]) ? -INFINITY : val[h]) : -INFINITY;
+    }
+    float mx = fmaxf(key[0], key[1]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float z = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      pp[h] = sel[h] ? expf(val[h] - mx) : 0.0f;
+      z += pp[h];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+    if (!full) z += znc[tt] * expf(am[tt] - mx);
+    int my_e = -1;
+    float my_p = 0.0f, psum = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      float bk = -INFINITY, bp = 0.0f;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = lane + 64 * h;
+        if (sel[h] && (key[h] > bk || (key[h] == bk && e < be))) {
+          bk = key[h];
+          be = e;
+          bp = pp[h];
+        }
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ok = __shfl_xor(bk, off);
+        const int oe = __shfl_xor(be, off);
+        const float op = __shfl_xor(bp, off);
+        if (ok > bk || (ok == bk && oe < be)) {
+          bk = ok;
+          be = oe;
+          bp = op;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (lane + 64 * h == be) sel[h] = false;
+      psum += bp;
+      if (lane == j) {
+        my_e = be;
+        my_p = bp;
+      }
+    }
+    if (lane < k) {
+      idx_out[(size_t)t * k + lane] = my_e;
+      w_out[(size_t)t * k + lane] = renorm ? my_p / psum : my_p / z;
+    }
+  }
+}
+
+template <int EB>
+hipError_t launch_eb(const occ_layer_desc &L, const void *x, const float *wr, int32_t *idx,
+                     float *w, const FilterWs &f, hipStream_t st) {
+  const dim3 grid((L.T + kTok - 1) / kTok);
+  route_approx_kernel<EB><<<grid, kNT, 0, st>>>(L.T, L.d, L.E, static_cast<const uint16_t *>(x),
+                                                f.wh, f.ag, f.xn);
+  route_exact_kernel<EB><<<grid, kNT, 0, st>>>(L.T, L.d, L.E, L.k, L.renorm,
+                                               static_cast<const uint16_t *>(x), wr, f.wh, f.bnd,
+                                               f.ex, f.ag, f.xn, idx, w);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool route_filter_applies(const occ_layer_desc &L) {
+  return L.dtype == OCC_BF16 && L.E >= 32 && L.E <= 128 && L.k <= kCap && L.d % 64 == 0;
+}
+
+size_t route_filter_workspace_bytes(const occ_layer_desc &L) {
+  if (!route_filter_applies(L)) return 0;
+  return a256((size_t)L.E * L.d * 2) + 2 * a256((size_t)L.E * 4) + a256((size_t)L.T * L.E * 4) +
+         a256((size_t)L.T * 4);
+}
+
+hipError_t launch_route_filtered(const occ_layer_desc &L, const void *x, const float *wr,
+                                 int32_t *idx, float *w, void *ws, hipStream_t st) {
+  if (L.T == 0) return hipSuccess;
+  const FilterWs f = carve(L, ws);
+  route_prep_kernel<<<L.E, 256, 0, st>>>(L.d, wr, f.wh, f.bnd, f.ex);
+  if (L.E > 64) return launch_eb<4>(L, x, wr, idx, w, f, st);
+  return launch_eb<2>(L, x, wr, idx, w, f, st);
+}
+
+}  // namespace occ

@@ -18,6 +18,7 @@ from . import (desc_of, make_brim, occ_backward_workspace_bytes, occ_build_brim,
                occ_grad_combine, occ_grad_dispatch, occ_router_backward, occ_shared_backward,
                occ_combine_direct, occ_dispatch, occ_dispatch_direct, occ_expert_down,
                occ_expert_ffn, occ_expert_up, occ_ffn_workspace_bytes, occ_route_topk,
+               occ_route_topk_ws, occ_route_workspace_bytes,
                occ_workspace_bytes)
 
 
@@ -99,6 +100,17 @@ class MoELayer:
                               S=self.S)
         self.ws_bytes = occ_workspace_bytes(self.desc)
         self.ws = buf((self.ws_bytes,), torch.uint8)
+        # routing without logits goes through the candidate filter
+        # (occ_route_topk_ws) where it measured faster than the plain kernel
+        # (at least 96 experts and 32768 tokens: the plain kernel's work grows
+        # with E, the filter's with the candidates) and the router is
+        # bf16-representable (checked once here); route_filtered = False
+        # forces the plain kernel
+        wr = weights.w_router
+        self.route_filtered = (cfg.E >= 96 and cfg.T >= 32768 and
+                               bool(torch.equal(wr, wr.to(torch.bfloat16).to(wr.dtype))))
+        self.route_ws_bytes = occ_route_workspace_bytes(self.desc)
+        self.route_ws = buf((self.route_ws_bytes,), torch.uint8) if self.route_ws_bytes else None
         self.sfd = buf((S_max, d), el)
         self.epd = buf((R, d), el)
         self.h_bytes = occ_ffn_workspace_bytes(self.desc)
@@ -111,8 +123,12 @@ class MoELayer:
 
     # ---- the hot path ------------------------------------------------------
     def route(self, stream=None):
-        occ_route_topk(self.desc, self.w.x, self.w.w_router, self.topk_idx, self.topk_w,
-                       self.logits, stream)
+        if self.logits is None and self.route_filtered and self.route_ws is not None:
+            occ_route_topk_ws(self.desc, self.w.x, self.w.w_router, self.topk_idx, self.topk_w,
+                              self.route_ws, self.route_ws_bytes, stream)
+        else:
+            occ_route_topk(self.desc, self.w.x, self.w.w_router, self.topk_idx, self.topk_w,
+                           self.logits, stream)
         # the router gradient needs the logits of the forward it differentiates
         self._routed_with_logits = self.logits is not None
 

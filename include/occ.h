@@ -124,6 +124,30 @@ size_t occ_ffn_workspace_bytes(const occ_layer_desc *desc);
 occ_status occ_route_topk(const occ_layer_desc *desc, const void *x, const float *w_router,
                           int32_t *topk_idx, float *topk_w, float *logits, hipStream_t stream);
 
+/* Bytes of device workspace occ_route_topk_ws needs; 0 when the descriptor
+ * is invalid or outside the filtered path (bf16 layers with 32 <= E <= 128,
+ * k <= 16 and d % 64 == 0), where occ_route_topk_ws needs none. */
+size_t occ_route_workspace_bytes(const occ_layer_desc *desc);
+
+/* occ_route_topk without the logits output, through a workspace (Expert
+ * Coupling, Abstract: k of E experts).  Same topk_idx as occ_route_topk, bit
+ * for bit; topk_w within fp32 rounding of it.  On the filtered path the
+ * logits are first approximated by bf16 matrix-core products; an error bound
+ * per token (from |x_t|, the router rows' norms and their bf16 rounding)
+ * leaves the experts that can be among the k largest in-order chains, and
+ * only those chains run (a block of 128 tokens with a token of more than 16
+ * such experts, or a non-finite value, runs every chain).  The softmax sum
+ * takes the other experts' approximate logits.  The filter pays off only
+ * when every router row is bf16-representable (a bf16 router widened to
+ * fp32); otherwise every chain runs, which is correct but slower than
+ * occ_route_topk.  Elsewhere it is occ_route_topk with logits = NULL and ws
+ * is not read.
+ *   ws, ws_bytes  device workspace of occ_route_workspace_bytes(desc) bytes
+ *                 (OCC_ENOSPC when smaller, OCC_EINVAL when NULL and needed) */
+occ_status occ_route_topk_ws(const occ_layer_desc *desc, const void *x, const float *w_router,
+                             int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
 /* BRIM construction (Occult, Figure 5 caption; Expert Coupling, Abstract:
  * each token to each device once).
  *   topk_idx, topk_w  as written by occ_route_topk

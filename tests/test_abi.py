@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(occ):
     names = declared_symbols()
-    assert len(names) == 27, names
+    assert len(names) == 29, names
     lib = C.CDLL(occ.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -65,6 +65,23 @@ def test_bad_descriptors_are_rejected(occ, kw, code):
     assert occ.last_error()
     assert occ.occ_workspace_bytes(d) == 0
 
+
+
+def test_route_workspace_only_on_the_filtered_path(occ):
+    """occ_route_workspace_bytes is positive exactly where the candidate
+    filter applies (bf16, 32 <= E <= 128, k <= 16, d % 64 == 0), and
+    occ_route_topk_ws checks the workspace before it launches anything."""
+    lib = occ.lib()
+    on = _desc(occ, T=300, d=192, E=64, k=6, D=8)
+    assert occ.occ_route_workspace_bytes(on) >= 300 * 64 * 4 + 64 * 192 * 2
+    for kw in (dict(dtype="f32"), dict(E=16, D=2), dict(E=64, D=8, k=17), dict(d=200)):
+        assert occ.occ_route_workspace_bytes(_desc(occ, **{**dict(T=300, d=192, E=64, k=6, D=8),
+                                                           **kw})) == 0, kw
+    n = occ.occ_route_workspace_bytes(on)
+    assert lib.occ_route_topk_ws(C.byref(on), FAKE, FAKE, FAKE, FAKE, None, n, None) == -1
+    assert lib.occ_route_topk_ws(C.byref(on), FAKE, FAKE, FAKE, FAKE, FAKE, n - 1, None) == -3
+    assert "workspace" in occ.last_error()
+    assert lib.occ_route_topk_ws(C.byref(on), None, FAKE, FAKE, FAKE, FAKE, n, None) == -1
 
 def test_null_pointers_and_workspace(occ):
     d = _desc(occ)

@@ -124,6 +124,106 @@ def test_routing_lane_mappings(orc, T, E, k, renorm):
     assert_close(g_w.cpu().numpy(), w, "f32", "topk_w")
 
 
+
+def _filtered_route(cfg, inp):
+    """occ_route_topk_ws on the layer's inputs: (indices, weights) on the host."""
+    import torch
+
+    import expert_top_router_amd as etr
+    from expert_top_router_amd.layer import router_f32, to_device
+
+    desc = etr.desc_of(cfg)
+    nbytes = etr.occ_route_workspace_bytes(desc)
+    assert nbytes > 0, "the candidate filter should apply to this layer"
+    dev = torch.device("cuda")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    g_idx = torch.full((cfg.T, cfg.k), -7, dtype=torch.int32, device=dev)
+    g_w = torch.zeros((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    etr.occ_route_topk_ws(desc, to_device(inp.x), to_device(router_f32(inp.w_router)), g_idx, g_w,
+                          ws, nbytes)
+    torch.cuda.synchronize()
+    return g_idx.cpu().numpy(), g_w.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,E,k,renorm", [
+    (300, 33, 4, 0),      # 64 padded expert rows, ragged last block
+    (1000, 64, 8, 1),
+    (3001, 128, 16, 0),   # k at the candidate cap
+    (20000, 100, 6, 1),
+    (128, 128, 1, 0),     # one whole block, top-1
+])
+def test_filtered_routing(orc, T, E, k, renorm):
+    """Routing through the candidate filter (occ_route_topk_ws): the indices
+    of the in-order definition bit for bit, the weights within the fp32
+    tolerance (the softmax sum takes approximate logits for the experts
+    outside the certified candidates)."""
+    from tests.tolerance import assert_close
+
+    cfg = W.LayerConfig("route_filter", T=T, d=256, E=E, I=64, k=k, D=1, dtype="bf16",
+                        renorm=renorm, clusters=8)
+    inp = W.make_layer(cfg, seed=12)
+    say(f"filtered routing T={T} E={E} k={k} renorm={renorm}")
+    _, idx, w = orc.route(inp.x, inp.w_router, k, renorm, "bf16")
+    g_idx, g_w = _filtered_route(cfg, inp)
+    assert np.array_equal(g_idx, idx)
+    assert_close(g_w, w, "f32", "topk_w")
+
+
+def test_filtered_routing_falls_back_on_ties(orc):
+    """Router rows repeated in groups of 20: equal logits leave more than 16
+    candidates for most tokens, so those blocks run every chain; the result
+    is still the definition's, ties to the lower expert index."""
+    from tests.tolerance import assert_close
+
+    cfg = W.LayerConfig("route_ties", T=700, d=128, E=96, I=64, k=6, D=1, dtype="bf16",
+                        renorm=0, clusters=4)
+    inp = W.make_layer(cfg, seed=13)
+    wr = np.array(inp.w_router)
+    for e in range(cfg.E):
+        wr[e] = wr[(e // 20) * 20]
+    inp.w_router = wr
+    say("filtered routing with tied router rows")
+    _, idx, w = orc.route(inp.x, inp.w_router, cfg.k, 0, "bf16")
+    g_idx, g_w = _filtered_route(cfg, inp)
+    assert np.array_equal(g_idx, idx)
+    assert_close(g_w, w, "f32", "topk_w")
+
+
+
+def test_filtered_routing_fp32_router(orc):
+    """A router that is not bf16-representable: the filter's bound takes the
+    bf16 rounding residual of its rows, and the chains stream the fp32 rows."""
+    from expert_top_router_amd.layer import router_f32
+    from tests.tolerance import assert_close
+
+    cfg = W.LayerConfig("route_f32r", T=1500, d=256, E=128, I=64, k=6, D=1, dtype="bf16",
+                        renorm=0, clusters=8)
+    inp = W.make_layer(cfg, seed=14)
+    wr = router_f32(inp.w_router).copy()
+    rng = np.random.default_rng(14)
+    wr += (rng.standard_normal(wr.shape) * 1e-3 * np.abs(wr)).astype(np.float32)
+    assert np.any((wr.view(np.uint32) & 0xffff) != 0)
+    inp.w_router = wr
+    say("filtered routing with an fp32 router")
+    _, idx, w = orc.route(inp.x, inp.w_router, cfg.k, 0, "bf16")
+    g_idx, g_w = _filtered_route(cfg, inp)
+    assert np.array_equal(g_idx, idx)
+    assert_close(g_w, w, "f32", "topk_w")
+
+@pytest.mark.parametrize("name", ["olmoe_bf16", "dsv2lite_bf16", "stress_bf16"])
+def test_full_size_filtered_routing(orc, name):
+    """The benchmark layers' routing through the candidate filter against the
+    oracle on the full batch."""
+    from tests.tolerance import assert_close
+
+    cfg = W.CONFIGS[name]
+    inp = W.make_layer(cfg, seed=0, experts=False)
+    say(f"full-size filtered routing {name}")
+    _, idx, w = orc.route(inp.x, inp.w_router, cfg.k, cfg.renorm, cfg.dtype)
+    g_idx, g_w = _filtered_route(cfg, inp)
+    assert np.array_equal(g_idx, idx)
+    assert_close(g_w, w, "f32", "topk_w")
+
 def test_coactivation_accumulates(orc):
     import torch
     from expert_top_router_amd.layer import MoELayer, upload_inputs
