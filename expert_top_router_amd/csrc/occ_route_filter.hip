@@ -47,6 +47,63 @@ constexpr int kTok = 128;     // tokens per block (approx and exact kernels)
 constexpr int kNT = 512;      // threads per block (8 waves)
 constexpr float kU = 5.9604645e-8f;  // 2^-24
 
+// Cross-lane reductions through DPP (no LDS round trips): the quad
+// permutations and the half-row and row mirrors combine the 16 lanes of a
+// row (every lane ends with its row's value); row_bcast15 / row_bcast31 then
+// carry rows 0..2 into row 3, whose last lane holds the wave's value.
+template <int CTRL, int RM = 0xf> __device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               RM, 0xf, false));
+}
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dppf<0xb1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dppf<0x4e>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dppf<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dppf<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v += dppf<0xb1>(v);
+  v += dppf<0x4e>(v);
+  v += dppf<0x141>(v);
+  return v + dppf<0x140>(v);
+}
+__device__ __forceinline__ float lane63(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row_max(v);
+  v = fmaxf(v, dppf<0x142, 0xa>(v));  // row_bcast15 into rows 1 and 3
+  v = fmaxf(v, dppf<0x143, 0xc>(v));  // row_bcast31 into rows 2 and 3
+  return lane63(v);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum(v);
+  v += dppf<0x142, 0xa>(v);
+  v += dppf<0x143, 0xc>(v);
+  return lane63(v);
+}
+
+__device__ __forceinline__ int row_min_i(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0xb1, 0xf, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x4e, 0xf, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xf, 0xf, false));
+  return min(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false));
+}
+__device__ __forceinline__ int row_sum_i(int v) {
+  v += __builtin_amdgcn_update_dpp(v, v, 0xb1, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(v, v, 0x4e, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(v, v, 0x141, 0xf, 0xf, false);
+  return v + __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false);
+}
+// inclusive prefix sum over the 16 lanes of a row (row_shr with zero fill)
+__device__ __forceinline__ int row_scan_i(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  return v + __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+}
+
 struct FilterWs {
   uint16_t *wh;  // [E][d] bf16 router
   float *bnd;    // [E] bound factor B_e
@@ -260,8 +317,8 @@ __global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
   constexpr int KPF = 4;                     // register sets of loads in flight
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][kTok * LX];
   __shared__ __attribute__((aligned(16))) float ws[2][EPAD * LW];
-  __shared__ float exl[kTok][kCap];
-  __shared__ uint8_t cl[kTok][kCap];
+  __shared__ __attribute__((aligned(16))) float exl[kTok][kCap];
+  __shared__ __attribute__((aligned(16))) uint8_t cl[kTok][kCap];
   __shared__ int32_t nc[kTok];
   __shared__ float am[kTok], znc[kTok];
   __shared__ int all_flag;
@@ -281,58 +338,79 @@ __global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
   }
   __syncthreads();
 
-  // candidates of each token (16 per wave), from the approximate logits
-  const uint64_t lt = lanemask_lt();
-  for (int tt = wave; tt < kTok; tt += kNT / 64) {
-    const int t = t0 + tt;
-    if (t >= T) {
-      if (lane == 0) nc[tt] = 0;
-      continue;
-    }
-    const int e0 = lane, e1 = lane + 64;
-    const bool l0 = e0 < E, l1 = EPAD > 64 && e1 < E;
-    const float a0 = l0 ? agg[(size_t)t * E + e0] : 0.0f;
-    const float a1 = l1 ? agg[(size_t)t * E + e1] : 0.0f;
-    const bool bad = (l0 && !isfinite(a0)) || (l1 && !isfinite(a1));
-    bool v0 = l0, v1 = l1;
-    float kth = -INFINITY, amax = -INFINITY;
-    for (int j = 0; j < k; ++j) {
-      float m = fmaxf(v0 ? a0 : -INFINITY, v1 ? a1 : -INFINITY);
+  // candidates: a 16-lane segment per token (four tokens per wave at a
+  // time, tt = wave + 8 (4 it + segment)); lane q of a segment holds the
+  // approximate logits of experts PL q .. PL q + PL - 1
+  {
+    constexpr int PL = EPAD / 16;
+    const int sgm = lane >> 4, q = lane & 15;
+    for (int it = 0; it < kTok / (kNT / 64) / 4; ++it) {
+      const int tt = wave + 8 * (4 * it + sgm), t = t0 + tt;
+      const bool tok = t < T;
+      float a[PL];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      if (j == 0) amax = m;
-      kth = m;
-      // retire one expert holding the maximum (the lowest index)
-      const uint64_t h0 = __ballot(v0 && a0 == m), h1 = __ballot(v1 && a1 == m);
-      if (h0 != 0) {
-        if (lane == __ffsll((long long)h0) - 1) v0 = false;
-      } else if (h1 != 0) {
-        if (lane == __ffsll((long long)h1) - 1) v1 = false;
+      for (int c = 0; c < PL; ++c) {
+        const int e = PL * q + c;
+        a[c] = (tok && e < E) ? agg[(size_t)t * E + e] : -INFINITY;
       }
-    }
-    const float delta = xng[t] * bmax * 1.01f;
-    const float theta = kth - 2.0f * delta;
-    const bool c0 = l0 && a0 >= theta, c1 = l1 && a1 >= theta;
-    const uint64_t m0 = __ballot(c0), m1 = __ballot(c1);
-    const int cnt = __popcll(m0) + __popcll(m1);
-    const bool anybad = __ballot(bad) != 0;
-    if (anybad || !isfinite(theta) || !isfinite(amax) || cnt > kCap) {
-      if (lane == 0) {
-        nc[tt] = -1;
-        all_flag = 1;
-      }
-      continue;
-    }
-    if (c0) cl[tt][__popcll(m0 & lt)] = (uint8_t)e0;
-    if (c1) cl[tt][__popcll(m0) + __popcll(m1 & lt)] = (uint8_t)e1;
-    // the other experts' share of the softmax sum, relative to amax
-    float z = (l0 && !c0 ? expf(a0 - amax) : 0.0f) + (l1 && !c1 ? expf(a1 - amax) : 0.0f);
+      bool bad = false;
+      bool live[PL];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
-    if (lane == 0) {
-      nc[tt] = cnt;
-      am[tt] = amax;
-      znc[tt] = z;
+      for (int c = 0; c < PL; ++c) {
+        live[c] = PL * q + c < E;
+        bad |= live[c] && !isfinite(a[c]);
+      }
+      // the k-th largest: k rounds of (segment max, retire its lowest holder)
+      float kth = -INFINITY, amax = -INFINITY;
+      bool v[PL];
+#pragma unroll
+      for (int c = 0; c < PL; ++c) v[c] = live[c];
+      for (int j = 0; j < k; ++j) {
+        float lm = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < PL; ++c) lm = fmaxf(lm, v[c] ? a[c] : -INFINITY);
+        const float m = row_max(lm);
+        if (j == 0) amax = m;
+        kth = m;
+        int le = 0x7fffffff;
+#pragma unroll
+        for (int c = PL - 1; c >= 0; --c)
+          if (v[c] && a[c] == m) le = PL * q + c;
+        const int ge = row_min_i(le);
+#pragma unroll
+        for (int c = 0; c < PL; ++c)
+          if (PL * q + c == ge) v[c] = false;
+      }
+      const float delta = (tok ? xng[t] : 0.0f) * bmax * 1.01f;
+      const float theta = kth - 2.0f * delta;
+      int lc = 0;
+#pragma unroll
+      for (int c = 0; c < PL; ++c) lc += (live[c] && a[c] >= theta) ? 1 : 0;
+      const int pos = row_scan_i(lc) - lc;  // candidates of the lower lanes
+      const int cnt = row_sum_i(lc);
+      const bool segbad = row_max(bad ? 1.0f : 0.0f) > 0.0f;
+      const bool ok = tok && !segbad && isfinite(theta) && isfinite(amax) && cnt <= kCap;
+      if (tok && !ok) {
+        if (q == 0) nc[tt] = -1;
+        all_flag = 1;  // every lane of the segment writes the same value
+      }
+      float zl = 0.0f;
+      int w = pos;
+#pragma unroll
+      for (int c = 0; c < PL; ++c) {
+        const bool cand = live[c] && a[c] >= theta;
+        if (ok && cand) cl[tt][w] = (uint8_t)(PL * q + c);
+        w += cand ? 1 : 0;
+        if (live[c] && !cand) zl += expf(a[c] - amax);
+      }
+      // the other experts' share of the softmax sum, relative to amax
+      const float z = row_sum(zl);
+      if (q == 0 && ok) {
+        nc[tt] = cnt;
+        am[tt] = amax;
+        znc[tt] = z;
+      }
+      if (q == 0 && !tok) nc[tt] = 0;
     }
   }
   __syncthreads();
@@ -490,7 +568,50 @@ __global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
   }
   __syncthreads();  // also orders the block's global writes of exact logits before the reads
 
-  // softmax (max over the candidates' chains) and top-k among the candidates
+  if (!full) {
+    // certified blocks: a 16-lane segment per token (four per wave at a
+    // time), lane q holding candidate q; softmax over the candidates plus the
+    // other experts' precomputed share, and each candidate's rank in
+    // (logit descending, expert ascending) order is its output position
+    const int sgm = lane >> 4, q = lane & 15;
+#pragma unroll
+    for (int it = 0; it < kTok / (kNT / 64) / 4; ++it) {
+      const int tt = wave + 8 * (4 * it + sgm), t = t0 + tt;
+      const int n = t < T ? nc[tt] : 0;
+      const bool valid = q < n;
+      const int e = valid ? (int)cl[tt][q] : 0;
+      const float val = valid ? exl[tt][q] : 0.0f;
+      const float key = valid ? (isnan(val) ? -INFINITY : val) : -INFINITY;
+      const float mx = row_max(key);
+      const float p = valid ? expf(val - mx) : 0.0f;
+      float z = row_sum(p);
+      if (n > 0) z += znc[tt] * expf(am[tt] - mx);
+      int rank = 0;
+      const float4 *kv = reinterpret_cast<const float4 *>(&exl[tt][0]);
+      const u32x4 ev = *reinterpret_cast<const u32x4 *>(&cl[tt][0]);
+#pragma unroll
+      for (int v = 0; v < kCap / 4; ++v) {
+        const float4 f = kv[v];
+        const float fk[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int q2 = 4 * v + c;
+          const int e2 = (int)((ev[q2 >> 2] >> (8 * (q2 & 3))) & 0xffu);
+          const float k2 = isnan(fk[c]) ? -INFINITY : fk[c];
+          rank += (q2 < n && (k2 > key || (k2 == key && e2 < e))) ? 1 : 0;
+        }
+      }
+      const bool sel = valid && rank < k;
+      const float psum = row_sum(sel ? p : 0.0f);
+      if (sel) {
+        idx_out[(size_t)t * k + rank] = e;
+        w_out[(size_t)t * k + rank] = renorm ? p / psum : p / z;
+      }
+    }
+    return;
+  }
+
+  // every chain (uncertified block): softmax over all experts, top-k in k rounds
   for (int tt = wave; tt < kTok; tt += kNT / 64) {
     const int t = t0 + tt;
     if (t >= T) continue;
