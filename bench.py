@@ -39,8 +39,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
-# fp32 vector peak as published (256 CU x 4 SIMD x 32 FMA x 2 flop x 2.4 GHz); plain
-# v_fmac_f32 reaches it without packed math once two waves share a SIMD
+# fp32 peak as published, vector and matrix alike (256 CU x 4 SIMD x 32 FMA x 2 flop x
+# 2.4 GHz); plain v_fmac_f32 reaches it without packed math once two waves share a
+# SIMD, and so does the K = 1 fp32 MFMA that routing runs its chains on at large batches
 PEAK_F32_VALU_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE-layer tokens/sec (route+dispatch+FFN+combine); % HBM and % MFMA peak"
@@ -72,6 +73,15 @@ def parse():
 
 def elem_bytes(cfg):
     return 2 if cfg.dtype == "bf16" else 4
+
+
+def route_unit(cfg) -> str:
+    """Where occ_route_topk runs every chain (the library's choice, restated
+    for the report): the matrix cores from 16384 tokens for routers of 33..128
+    experts when d is a whole number of chunks, else the vector ALUs."""
+    jc = 64 if cfg.dtype == "bf16" else 32
+    mfma = 32 < cfg.E <= 128 and cfg.k <= 16 and cfg.d % jc == 0 and cfg.T >= 16384
+    return "every chain, matrix cores" if mfma else "every chain, vector ALUs"
 
 
 def algorithmic(cfg, S):
@@ -453,7 +463,7 @@ def stage_times(lay, cfg, n, torch):
         # the candidate filter (occ_route_topk_ws) runs the chains of only the
         # certified candidates: against the plain kernel's 2 T d E flop this is
         # an equivalent rate, not the VALU's own
-        "route_path": "candidate filter" if filtered else "every chain",
+        "route_path": "candidate filter" if filtered else route_unit(cfg),
         "route_valu_frac": alg["route_flop"] / t["route"] / 1e12 / PEAK_F32_VALU_TFLOPS,
         "route_hbm_frac": alg["route_bytes"] / t["route"] / 1e9 / PEAK_HBM_GBS,
         "build_brim_us": t["build_brim"] * 1e6,

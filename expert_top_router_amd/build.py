@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build", "occult")
 LIB = os.path.join(PKG, "liboccult.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["occ_api.cpp", "occ_route.hip", "occ_route_filter.hip", "occ_brim.hip", "occ_permute.hip", "occ_coact.hip",
+SOURCES = ["occ_api.cpp", "occ_route.hip", "occ_route_filter.hip", "occ_route_mfma.hip", "occ_brim.hip", "occ_permute.hip", "occ_coact.hip",
            "occ_affinity.hip", "occ_backward.hip", "occ_gemm.hip", "occ_gemm_bwd.hip",
            "occ_bwd_f32.hip"]
 

@@ -64,6 +64,63 @@ template <> __device__ __forceinline__ void widen<OCC_F32>(const u32x4 &u, float
   for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(u[i]);
 }
 
+// Cross-lane reductions through DPP (no LDS round trips): the quad
+// permutations and the half-row and row mirrors combine the 16 lanes of a
+// row (every lane ends with its row's value); row_bcast15 / row_bcast31 then
+// carry rows 0..2 into row 3, whose last lane holds the wave's value.
+template <int CTRL, int RM = 0xf> __device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               RM, 0xf, false));
+}
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dppf<0xb1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dppf<0x4e>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dppf<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dppf<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v += dppf<0xb1>(v);
+  v += dppf<0x4e>(v);
+  v += dppf<0x141>(v);
+  return v + dppf<0x140>(v);
+}
+__device__ __forceinline__ float lane63(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row_max(v);
+  v = fmaxf(v, dppf<0x142, 0xa>(v));  // row_bcast15 into rows 1 and 3
+  v = fmaxf(v, dppf<0x143, 0xc>(v));  // row_bcast31 into rows 2 and 3
+  return lane63(v);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum(v);
+  v += dppf<0x142, 0xa>(v);
+  v += dppf<0x143, 0xc>(v);
+  return lane63(v);
+}
+
+__device__ __forceinline__ int row_min_i(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0xb1, 0xf, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x4e, 0xf, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xf, 0xf, false));
+  return min(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false));
+}
+__device__ __forceinline__ int row_sum_i(int v) {
+  v += __builtin_amdgcn_update_dpp(v, v, 0xb1, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(v, v, 0x4e, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(v, v, 0x141, 0xf, 0xf, false);
+  return v + __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false);
+}
+// inclusive prefix sum over the 16 lanes of a row (row_shr with zero fill)
+__device__ __forceinline__ int row_scan_i(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  return v + __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & (kWave - 1);
   return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
@@ -75,6 +132,11 @@ int device_cu_count();
 
 // ---- launchers (each returns hipGetLastError() of its launches) -----------
 hipError_t launch_route_topk(const occ_layer_desc &L, const void *x, const float *wr,
+                             int32_t *idx, float *w, float *logits, hipStream_t st);
+// routing with the logit chains on the matrix cores (K = 1 fp32 MFMAs):
+// 32 < E <= 128, k <= 16, d a multiple of 64 (bf16) or 32 (fp32)
+bool route_mfma_applies(const occ_layer_desc &L);
+hipError_t launch_route_mfma(const occ_layer_desc &L, const void *x, const float *wr,
                              int32_t *idx, float *w, float *logits, hipStream_t st);
 // filtered routing (occ_route_topk_ws): applies to bf16 layers with
 // 32 <= E <= 128, k <= 16, d % 64 == 0

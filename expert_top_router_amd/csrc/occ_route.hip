@@ -8,8 +8,10 @@
 // j = 0..d-1 in order.  v_fma_f32 rounds once, like C's fmaf, so the chain
 // is bit-identical to any IEEE implementation of that definition; that is
 // what makes the chosen indices reproducible bit for bit.  The chain cannot
-// be split over j, so the contraction stays on the fp32 VALU (not MFMA) and
-// the parallelism is over (token, expert) pairs.
+// be split over j, so the parallelism is over (token, expert) pairs.  This
+// file runs the chains on the fp32 VALU; at batches that give every SIMD a
+// 16-token tile, routers of 33..128 experts run them as K = 1 fp32 MFMAs
+// instead, which round like fmaf (occ_route_mfma.hip).
 //
 // Mapping: a wave is cut into Q = 64/ESEG segments of ESEG lanes; lane el of
 // a segment owns experts el + ESEG*i (i < EP) and the segment owns TPL
@@ -430,6 +432,10 @@ hipError_t launch_dt(const occ_layer_desc &L, const void *x, const float *wr, in
 hipError_t launch_route_topk(const occ_layer_desc &L, const void *x, const float *wr,
                              int32_t *idx, float *w, float *logits, hipStream_t st) {
   if (L.T == 0) return hipSuccess;
+  // Wider routers at batches that give every SIMD a 16-token tile run their
+  // chains on the matrix cores (same bits; occ_route_mfma.hip).
+  if (route_mfma_applies(L) && L.T >= 16384)
+    return launch_route_mfma(L, x, wr, idx, w, logits, st);
   return L.dtype == OCC_F32 ? launch_dt<OCC_F32>(L, x, wr, idx, w, logits, st)
                             : launch_dt<OCC_BF16>(L, x, wr, idx, w, logits, st);
 }

@@ -87,29 +87,31 @@ def test_routing_ties_lower_index_first(orc):
     compare(g, o, inp)
 
 
-@pytest.mark.parametrize("T,E,k,renorm", [
-    (16384, 64, 16, 0),   # 16-lane segments, 4 experts per lane (T >= 16384)
-    (16383, 64, 6, 1),    # the same with a ragged last block
-    (4096, 64, 8, 0),     # whole-wave segments with DPP broadcasts
-    (3001, 128, 16, 0),   # 16-lane segments, 8 experts per lane, k = segment width
-    (20000, 100, 6, 1),   # 8 experts per lane, lanes past E idle
+@pytest.mark.parametrize("T,E,k,renorm,dtype,d", [
+    # from 16384 tokens, routers of 33..128 experts run on the matrix cores
+    # when d is a multiple of the chunk width; fp32 tokens with d = 200 keep
+    # these on the VALU mappings
+    (16384, 64, 16, 0, "f32", 200),   # 16-lane segments, 4 experts per lane
+    (16383, 64, 6, 1, "f32", 200),    # the same with a ragged last block
+    (4096, 64, 8, 0, "bf16", 192),    # whole-wave segments with DPP broadcasts
+    (3001, 128, 16, 0, "bf16", 192),  # 16-lane segments, 8 experts per lane, k = segment width
+    (20000, 100, 6, 1, "f32", 200),   # 8 experts per lane, lanes past E idle
 ])
-def test_routing_lane_mappings(orc, T, E, k, renorm):
+def test_routing_lane_mappings(orc, T, E, k, renorm, dtype, d):
     """Routing alone on the token and expert counts that select each lane
-    mapping of the routing kernel: logits and indices bit for bit, weights
-    within the fp32 tolerance."""
+    mapping of the VALU routing kernel (d: an odd number of LDS chunks):
+    logits and indices bit for bit, weights within the fp32 tolerance."""
     import torch
 
     import expert_top_router_amd as etr
     from expert_top_router_amd.layer import router_f32, to_device
     from tests.tolerance import assert_close
 
-    d = 192  # an odd number of LDS chunks
-    cfg = W.LayerConfig("route_map", T=T, d=d, E=E, I=64, k=k, D=4, dtype="bf16",
+    cfg = W.LayerConfig("route_map", T=T, d=d, E=E, I=64, k=k, D=4, dtype=dtype,
                         renorm=renorm)
     inp = W.make_layer(cfg, seed=11)
-    say(f"routing T={T} E={E} k={k}")
-    lg, idx, w = orc.route(inp.x, inp.w_router, k, renorm, "bf16")
+    say(f"routing T={T} E={E} k={k} {dtype} d={d}")
+    lg, idx, w = orc.route(inp.x, inp.w_router, k, renorm, dtype)
     dev = torch.device("cuda")
     x = to_device(inp.x)
     wr = to_device(router_f32(inp.w_router))
@@ -123,6 +125,49 @@ def test_routing_lane_mappings(orc, T, E, k, renorm):
     assert np.array_equal(g_idx.cpu().numpy(), idx)
     assert_close(g_w.cpu().numpy(), w, "f32", "topk_w")
 
+
+@pytest.mark.parametrize("T,E,k,renorm,dtype,d,tie", [
+    (16384, 128, 6, 0, "bf16", 128, False),   # two accumulators, two chunks
+    (16383, 96, 16, 1, "bf16", 192, False),   # ragged last tile, k = row width
+    (20000, 33, 1, 0, "bf16", 256, False),    # one accumulator, lanes past E idle
+    (16500, 100, 8, 1, "f32", 96, False),     # fp32 tokens, 32-column chunks
+    (16384, 96, 6, 0, "bf16", 128, True),     # equal logits: lower index first
+])
+def test_routing_on_matrix_cores(orc, T, E, k, renorm, dtype, d, tie):
+    """Routing at batches that run the logit chains as K = 1 MFMAs: logits
+    and indices bit for bit against the in-order definition, weights within
+    the fp32 tolerance; the call without a logits output picks the same."""
+    import torch
+
+    import expert_top_router_amd as etr
+    from expert_top_router_amd.layer import router_f32, to_device
+    from tests.tolerance import assert_close
+
+    cfg = W.LayerConfig("route_mfma", T=T, d=d, E=E, I=64, k=k, D=4 if E % 4 == 0 else 3,
+                        dtype=dtype, renorm=renorm)
+    inp = W.make_layer(cfg, seed=13)
+    wr_host = router_f32(inp.w_router)
+    if tie:  # rows repeated in groups of 8: every logit has 7 equal twins
+        wr_host = np.repeat(wr_host[::8], 8, axis=0)[:E].copy()
+    say(f"routing on the matrix cores T={T} E={E} k={k} {dtype} d={d} tie={tie}")
+    lg, idx, w = orc.route(inp.x, wr_host, k, renorm, dtype)
+    dev = torch.device("cuda")
+    x = to_device(inp.x)
+    wr = to_device(wr_host)
+    g_idx = torch.full((T, k), -7, dtype=torch.int32, device=dev)
+    g_w = torch.zeros((T, k), dtype=torch.float32, device=dev)
+    g_lg = torch.zeros((T, E), dtype=torch.float32, device=dev)
+    etr.occ_route_topk(etr.desc_of(cfg), x, wr, g_idx, g_w, g_lg)
+    torch.cuda.synchronize()
+    assert np.array_equal(g_lg.cpu().numpy().view(np.uint32),
+                          np.asarray(lg, np.float32).view(np.uint32))
+    assert np.array_equal(g_idx.cpu().numpy(), idx)
+    assert_close(g_w.cpu().numpy(), w, "f32", "topk_w")
+    n_idx = torch.full((T, k), -7, dtype=torch.int32, device=dev)
+    n_w = torch.zeros((T, k), dtype=torch.float32, device=dev)
+    etr.occ_route_topk(etr.desc_of(cfg), x, wr, n_idx, n_w, None)
+    torch.cuda.synchronize()
+    assert torch.equal(n_idx, g_idx) and torch.equal(n_w, g_w)
 
 
 def _filtered_route(cfg, inp):
