@@ -205,41 +205,83 @@ __global__ __launch_bounds__(kThreads) void router_grad_kernel(
 }
 
 // The router's two products, dx_router = dlogit W_r and dW_r = dlogit^T x,
-// as one fp32 VALU tile kernel (contractions over E and over T in fp32;
-// neither is large enough to pay for a split into bf16 MFMA operands).
+// on the matrix cores in fp32 (v_mfma_f32_16x16x4f32: products exact,
+// fp32 sums; the contractions over E and over T take a different order than
+// a plain loop, within fp32 rounding):
 //   C[z][m][n] = sum over k in chunk z of A(m, k) B(k, n)
 //   A(m, k) = a[k * lda + m] when A_KM (m contiguous), a[m * lda + k] otherwise
 //   B(k, n) = b[k * ldb + n] (fp32 or bf16, n contiguous, ldb % 8 == 0)
-// A block owns a 64 x 128 tile of C and one chunk of K (kchunk % 32 == 0);
-// each thread keeps 8 x 4 outputs in registers, both operands pass through
-// LDS 32 k at a time with the next k-slab's loads in flight.
-constexpr int kRBM = 64, kRBN = 128, kRBK = 32;
+// A block owns a 128 x 128 tile of C and one chunk of K; four waves of
+// 64 x 64 (4 x 4 MFMA blocks of 16 x 16, 64 accumulators per lane).  The
+// operands pass through LDS 32 k at a time, in registers one slab ahead, each
+// stored as it lies in memory (16-byte stores): A as [m][k] (row stride 36
+// floats) or [k][m], B as [k][n] (row stride 132 floats).  MFMA operand
+// layout: lane l supplies row (column) l % 16 at k-slot l / 16.  Per 16 k a
+// lane feeds 4 successive MFMAs with k = k0 + 4 (l / 16) + s (s < 4), the same
+// on both operands: one 16-byte read from a [m][k] tile, four 4-byte reads
+// from a k-major one (conflict-free: the four k rows of a read are 4 rows
+// apart, 16 banks).  Output element i of lane l is row 4 (l / 16) + i,
+// column l % 16.
+constexpr int kRBM = 128, kRBN = 128, kRBK = 32;
+constexpr int kRLK = kRBK + 4;    // [m][k] row stride
+constexpr int kRLN = kRBN + 4;    // [k][m] / [k][n] row stride
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 template <bool A_KM, int DT>
-__global__ __launch_bounds__(kThreads) void router_gemm_kernel(
+__global__ __launch_bounds__(kThreads, 2) void router_gemm_kernel(
     int M, int N, int K, int kchunk, const float *__restrict__ a, int lda,
     const typename Elem<DT>::T *__restrict__ b, int ldb, float *__restrict__ c) {
-  __shared__ float As[kRBK][kRBM + 4];
-  __shared__ float Bs[kRBK][kRBN];
-  constexpr int BW = DT == OCC_BF16 ? 8 : 4;  // B elements per 16-byte load
+  constexpr int AST = A_KM ? kRBK * kRLN : kRBM * kRLK;  // floats per A stage
+  constexpr int BST = kRBK * kRLN;
+  __shared__ __attribute__((aligned(16))) float As[2 * AST];
+  __shared__ __attribute__((aligned(16))) float Bs[2 * BST];
+  constexpr int BW = DT == OCC_BF16 ? 8 : 4;       // B elements per 16-byte load
+  constexpr int ALOADS = kRBM * kRBK / 4 / kThreads;
   constexpr int BLOADS = kRBK * kRBN / BW / kThreads;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * kRBM, n0 = blockIdx.x * kRBN;
   const int k_lo = blockIdx.z * kchunk;
   const int k_hi = min(K, k_lo + kchunk);
-  const int tx = tid % 32, ty = tid / 32;  // outputs: cols n0+4tx.., rows m0+8ty..
-  float acc[8][4] = {};
-  float ar[8];
+  f32x4v acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+  float4 ar[ALOADS];
   u32x4 br[BLOADS];
-
+  // element (r, cq) of a thread's j-th 16-byte piece: A_KM and B pieces are 4
+  // (8) consecutive m (n) at one k, the others 4 consecutive k of one m
+  auto a_piece = [&](int j, int &r, int &cq) {
+    const int q = tid + kThreads * j;
+    if (A_KM) {
+      r = q / (kRBM / 4);
+      cq = (q % (kRBM / 4)) * 4;
+    } else {
+      r = q / (kRBK / 4);
+      cq = (q % (kRBK / 4)) * 4;
+    }
+  };
+  // Rows past M or N and k past the chunk load zeros (their products are 0).
   auto load = [&](int k0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int q = tid + kThreads * j;
-      const int kk = A_KM ? q / kRBM : q % kRBK, mm = A_KM ? q % kRBM : q / kRBK;
-      const int k = k0 + kk, m = m0 + mm;
-      ar[j] = (k < k_hi && m < M) ? (A_KM ? a[(size_t)k * lda + m] : a[(size_t)m * lda + k])
-                                  : 0.0f;
+    for (int j = 0; j < ALOADS; ++j) {
+      int r, cq;
+      a_piece(j, r, cq);
+      const int k = k0 + (A_KM ? r : cq), m = m0 + (A_KM ? cq : r);
+      ar[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int lim_c = A_KM ? M - m : k_hi - k;  // valid elements along the piece
+      if (k < k_hi && m < M) {
+        const float *src = A_KM ? a + (size_t)k * lda + m : a + (size_t)m * lda + k;
+        if (lim_c >= 4 && (lda & 3) == 0) {
+          ar[j] = *reinterpret_cast<const float4 *>(src);
+        } else {
+          ar[j].x = src[0];
+          ar[j].y = lim_c > 1 ? src[1] : 0.f;
+          ar[j].z = lim_c > 2 ? src[2] : 0.f;
+          ar[j].w = lim_c > 3 ? src[3] : 0.f;
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < BLOADS; ++j) {
@@ -251,53 +293,81 @@ __global__ __launch_bounds__(kThreads) void router_gemm_kernel(
                   : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto store = [&]() {
+  auto store = [&](int st) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int q = tid + kThreads * j;
-      As[A_KM ? q / kRBM : q % kRBK][A_KM ? q % kRBM : q / kRBK] = ar[j];
+    for (int j = 0; j < ALOADS; ++j) {
+      int r, cq;
+      a_piece(j, r, cq);
+      *reinterpret_cast<float4 *>(&As[st * AST + r * (A_KM ? kRLN : kRLK) + cq]) = ar[j];
     }
 #pragma unroll
     for (int j = 0; j < BLOADS; ++j) {
       const int q = tid + kThreads * j;
+      const int kk = q / (kRBN / BW), nn = (q % (kRBN / BW)) * BW;
       float f[BW];
       widen<DT>(br[j], f);
-      float *dst = &Bs[q / (kRBN / BW)][(q % (kRBN / BW)) * BW];
 #pragma unroll
       for (int i = 0; i < BW; i += 4)
-        *reinterpret_cast<float4 *>(dst + i) = make_float4(f[i], f[i + 1], f[i + 2], f[i + 3]);
+        *reinterpret_cast<float4 *>(&Bs[st * BST + kk * kRLN + nn + i]) =
+            make_float4(f[i], f[i + 1], f[i + 2], f[i + 3]);
     }
   };
 
-  if (k_lo < k_hi) load(k_lo);
+  const int fr = lane & 15, fk = (lane >> 4) * 4;
+  // fragment bases: [m][k] tiles at row m, column k; k-major tiles at row k
+  const int a_rd = A_KM ? fk * kRLN + wm * 64 + fr : (wm * 64 + fr) * kRLK + fk;
+  const int b_rd = fk * kRLN + wn * 64 + fr;
+  int st = 0;
+  if (k_lo < k_hi) {
+    load(k_lo);
+    store(0);
+    __syncthreads();
+  }
   for (int k0 = k_lo; k0 < k_hi; k0 += kRBK) {
-    __syncthreads();
-    store();
-    __syncthreads();
     if (k0 + kRBK < k_hi) load(k0 + kRBK);
-#pragma unroll 8
-    for (int kk = 0; kk < kRBK; ++kk) {
-      const float4 a0 = *reinterpret_cast<const float4 *>(&As[kk][ty * 8]);
-      const float4 a1 = *reinterpret_cast<const float4 *>(&As[kk][ty * 8 + 4]);
-      const float4 bv = *reinterpret_cast<const float4 *>(&Bs[kk][tx * 4]);
-      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      const float bw[4] = {bv.x, bv.y, bv.z, bv.w};
+    const float *ab = As + st * AST + a_rd;
+    const float *bb = Bs + st * BST + b_rd;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+    for (int g = 0; g < kRBK / 16; ++g) {
+      float af[4][4], bf[4][4];  // [block][step]
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bw[j], acc[i][j]);
+      for (int i = 0; i < 4; ++i) {
+        if (A_KM) {
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) af[i][s4] = ab[(16 * g + s4) * kRLN + i * 16];
+        } else {
+          const float4 v = *reinterpret_cast<const float4 *>(ab + i * 16 * kRLK + 16 * g);
+          af[i][0] = v.x; af[i][1] = v.y; af[i][2] = v.z; af[i][3] = v.w;
+        }
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) bf[i][s4] = bb[(16 * g + s4) * kRLN + i * 16];
+      }
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][s4], bf[j][s4], acc[i][j], 0, 0, 0);
+    }
+    if (k0 + kRBK < k_hi) {
+      store(st ^ 1);  // the other stage: its last readers passed the barrier below
+      __syncthreads();
+      st ^= 1;
     }
   }
-  const int n = n0 + tx * 4;
-  if (n >= N) return;
   float *cz = c + (size_t)blockIdx.z * M * N;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = m0 + ty * 8 + i;
-    if (m < M)
-      *reinterpret_cast<float4 *>(cz + (size_t)m * N + n) =
-          make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-  }
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 64 + j * 16 + fr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 64 + i * 16 + fk + r;
+        if (m < M && n < N) cz[(size_t)m * N + n] = acc[i][j][r];
+      }
+    }
 }
 
 // out[i] = sum over z ascending of part[z][i] (n4 float4 groups per part).
