@@ -38,11 +38,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
-PEAK_F32_TFLOPS = 157.3
 # fp32 peak as published, vector and matrix alike (256 CU x 4 SIMD x 32 FMA x 2 flop x
-# 2.4 GHz); plain v_fmac_f32 reaches it without packed math once two waves share a
-# SIMD, and so does the K = 1 fp32 MFMA that routing runs its chains on at large batches
-PEAK_F32_VALU_TFLOPS = 157.3
+# 2.4 GHz): the fp32 layers' expert GEMMs, the routing chains (plain v_fmac_f32 reaches
+# it without packed math once two waves share a SIMD, and so does the K = 1 fp32 MFMA
+# that routing uses at large batches) and the router backward's fp32 MFMA products
+PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE-layer tokens/sec (route+dispatch+FFN+combine); % HBM and % MFMA peak"
 DEFAULT_WORKLOAD = "stress_bf16"
@@ -332,8 +332,8 @@ def backward(lay, cfg, steps, torch):
             "expert_backward_mfma_frac": ebw_flop / t["expert_backward"] / 1e12
                                          / PEAK_BF16_TFLOPS,
             "router_backward_us": t["router_backward"] * 1e6,
-            "router_backward_valu_frac": rb_flop / t["router_backward"] / 1e12
-                                         / PEAK_F32_VALU_TFLOPS,
+            "router_backward_fp32_frac": rb_flop / t["router_backward"] / 1e12
+                                         / PEAK_F32_TFLOPS,
             "grad_dispatch_us": t["grad_dispatch"] * 1e6,
             "grad_dispatch_hbm_frac": gd_bytes / t["grad_dispatch"] / 1e9 / PEAK_HBM_GBS}
 
@@ -464,7 +464,7 @@ def stage_times(lay, cfg, n, torch):
         # certified candidates: against the plain kernel's 2 T d E flop this is
         # an equivalent rate, not the VALU's own
         "route_path": "candidate filter" if filtered else route_unit(cfg),
-        "route_valu_frac": alg["route_flop"] / t["route"] / 1e12 / PEAK_F32_VALU_TFLOPS,
+        "route_fp32_frac": alg["route_flop"] / t["route"] / 1e12 / PEAK_F32_TFLOPS,
         "route_hbm_frac": alg["route_bytes"] / t["route"] / 1e9 / PEAK_HBM_GBS,
         "build_brim_us": t["build_brim"] * 1e6,
         "build_brim_hbm_frac": alg["brim_bytes"] / t["build_brim"] / 1e9 / PEAK_HBM_GBS,
