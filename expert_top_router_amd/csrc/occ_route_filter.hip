@@ -151,32 +151,39 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
   const bool wact = id0 < NTILE;  // uniform
   const int tb = id0 / EB;
 
-  u32x4 rx[XC], rw[WC];
+  // A ring of KP register sets: set c % KP holds k-chunk c from its load
+  // until it is stored to LDS, so each chunk's loads have KP - 1 chunks of
+  // compute to land (X streams from HBM; one chunk ahead left it latency-
+  // bound at ≈3 TB/s).
+  constexpr int KP = 4;
+  u32x4 rx[KP][XC], rw[KP][WC];
   float sx[XC];
 #pragma unroll
   for (int u = 0; u < XC; ++u) sx[u] = 0.0f;
-  // Loads are unconditional (rows past T or E re-read the last one; no
-  // output takes them), so the compiler's waits can count them.
-  auto load = [&](int j0) __attribute__((always_inline)) {
+  // Loads are unconditional (rows past T or E re-read the last one, chunks
+  // past the last re-read it; no output takes them), so the compiler's waits
+  // can count them.
+  auto load = [&](int ch, int set) __attribute__((always_inline)) {
+    const int j0 = min(ch, nch - 1) * JA;
 #pragma unroll
     for (int u = 0; u < XC; ++u) {
       const int c = tid + kNT * u, r = c >> 3, cc = (c & 7) * 8, t = min(t0 + r, T - 1);
-      rx[u] = *reinterpret_cast<const u32x4 *>(x + (size_t)t * d + j0 + cc);
+      rx[set][u] = *reinterpret_cast<const u32x4 *>(x + (size_t)t * d + j0 + cc);
     }
 #pragma unroll
     for (int u = 0; u < WC; ++u) {
       const int c = min(tid + kNT * u, WCH - 1), r = min(c >> 3, E - 1), cc = (c & 7) * 8;
-      rw[u] = *reinterpret_cast<const u32x4 *>(wh + (size_t)r * d + j0 + cc);
+      rw[set][u] = *reinterpret_cast<const u32x4 *>(wh + (size_t)r * d + j0 + cc);
     }
   };
-  auto store = [&](int st, bool norm) __attribute__((always_inline)) {
+  auto store = [&](int st, int set, bool norm) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < XC; ++u) {
       const int c = tid + kNT * u, r = c >> 3, cc = (c & 7) * 8;
-      *reinterpret_cast<u32x4 *>(&xa[st][r * LA + cc]) = rx[u];
-      if (norm) {  // not for the re-read past the last chunk
+      *reinterpret_cast<u32x4 *>(&xa[st][r * LA + cc]) = rx[set][u];
+      if (norm) {  // not for the re-reads past the last chunk
         float f[8];
-        widen<OCC_BF16>(rx[u], f);
+        widen<OCC_BF16>(rx[set][u], f);
 #pragma unroll
         for (int i = 0; i < 8; ++i) sx[u] = __builtin_fmaf(f[i], f[i], sx[u]);
       }
@@ -184,7 +191,7 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
 #pragma unroll
     for (int u = 0; u < WC; ++u) {
       const int c = tid + kNT * u, r = c >> 3, cc = (c & 7) * 8;
-      if (c < WCH) *reinterpret_cast<u32x4 *>(&wa[st][r * LA + cc]) = rw[u];
+      if (c < WCH) *reinterpret_cast<u32x4 *>(&wa[st][r * LA + cc]) = rw[set][u];
     }
   };
   ff32x16 acc[TPW];
@@ -192,15 +199,18 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
   for (int i = 0; i < TPW; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
-  // the loads past the last chunk re-read it (in bounds), so every iteration
-  // issues the same loads and the compiler's waits stay partial
-  load(0);
-  store(0, true);
+#pragma unroll
+  for (int c = 0; c < KP; ++c) load(c, c);
+  store(0, 0, true);
+  load(KP, 0);
   __syncthreads();
-  for (int ch = 0; ch < nch; ++ch) {
-    load(min(ch + 1, nch - 1) * JA);
+  // chunk ch from LDS stage ch & 1; then chunk ch + 1 (register set SET =
+  // (ch + 1) % KP) goes to the other stage and SET is refilled with chunk
+  // ch + 1 + KP
+  auto body = [&](int ch, auto setc) __attribute__((always_inline)) {
+    constexpr int SET = decltype(setc)::value;
     const int st = ch & 1;
-    if (wact) {
+    if (wact && ch < nch) {
 #pragma unroll
       for (int s = 0; s < JA / 16; ++s) {
         const int ko = s * 16 + (lane >> 5) * 8;
@@ -215,8 +225,16 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
         }
       }
     }
-    store((ch + 1) & 1, ch + 1 < nch);
+    store(st ^ 1, SET, ch + 1 < nch);
+    load(ch + 1 + KP, SET);
     __syncthreads();
+  };
+  static_assert(KP == 4, "the loop below is unrolled by four");
+  for (int ch = 0; ch < nch; ch += 4) {
+    body(ch, std::integral_constant<int, 1>{});
+    body(ch + 1, std::integral_constant<int, 2>{});
+    body(ch + 2, std::integral_constant<int, 3>{});
+    body(ch + 3, std::integral_constant<int, 0>{});
   }
   if (wact) {
 #pragma unroll
