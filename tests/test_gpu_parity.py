@@ -170,6 +170,72 @@ def test_routing_on_matrix_cores(orc, T, E, k, renorm, dtype, d, tie):
     assert torch.equal(n_idx, g_idx) and torch.equal(n_w, g_w)
 
 
+@pytest.mark.parametrize("T,dtype,path", [
+    (1000, "f32", "vector ALUs"),
+    (16384, "f32", "matrix cores"),
+    (16384, "bf16", "matrix cores"),
+    (16384, "bf16", "candidate filter"),
+])
+def test_routing_special_values(orc, T, dtype, path):
+    """Tokens with a NaN, a +inf or a -inf component, or components near the
+    largest finite value (chains that overflow): NaN logits rank as -inf,
+    ties go to the lower index, and every routing path picks the oracle's
+    experts bit for bit; logits and weights match where finite and agree on
+    NaN and infinity elsewhere (NaN payloads differ between the host and the
+    GPU)."""
+    import torch
+
+    import expert_top_router_amd as etr
+    from expert_top_router_amd.layer import router_f32, to_device
+
+    E, k, d = 64, 4, 128
+    cfg = W.LayerConfig("route_special", T=T, d=d, E=E, I=64, k=k, D=4, dtype=dtype)
+    inp = W.make_layer(cfg, seed=17)
+    x = W.to_f32(inp.x, dtype).astype(np.float64)
+    rows = np.arange(64)
+    x[rows, rows % d] = np.nan
+    x[64 + rows, 3] = np.inf
+    x[128 + rows, 5] = -np.inf
+    x[192:256] = np.sign(x[192:256]) * 3.0e38
+    x[256 + rows, 7] = np.inf
+    x[256 + rows, 9] = -np.inf  # +inf and -inf terms: NaN chains
+    inp.x = W.from_f64(x, dtype)
+    wr_host = router_f32(inp.w_router)
+    say(f"routing special values T={T} {dtype} on the {path}")
+    lg, idx, w = orc.route(inp.x, wr_host, k, 0, dtype)
+    dev = torch.device("cuda")
+    g_idx = torch.full((T, k), -7, dtype=torch.int32, device=dev)
+    g_w = torch.zeros((T, k), dtype=torch.float32, device=dev)
+    g_lg = None
+    desc = etr.desc_of(cfg)
+    if path == "candidate filter":
+        nbytes = etr.occ_route_workspace_bytes(desc)
+        assert nbytes > 0
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        etr.occ_route_topk_ws(desc, to_device(inp.x), to_device(wr_host), g_idx, g_w, ws, nbytes)
+    else:
+        g_lg = torch.zeros((T, E), dtype=torch.float32, device=dev)
+        etr.occ_route_topk(desc, to_device(inp.x), to_device(wr_host), g_idx, g_w, g_lg)
+    torch.cuda.synchronize()
+    assert np.isnan(lg[:64]).all() and np.isnan(lg[256:320]).any()
+    assert np.isinf(lg[64:192]).any() and np.isinf(lg[192:256]).any()
+    assert np.array_equal(g_idx.cpu().numpy(), idx)
+
+    def same(g, o, what):
+        fin = np.isfinite(o)
+        assert np.array_equal(np.isnan(g), np.isnan(o)), what
+        assert np.array_equal(g[np.isinf(o)], o[np.isinf(o)]), what
+        return fin
+
+    if g_lg is not None:
+        gl = g_lg.cpu().numpy()
+        fin = same(gl, lg, "logits")
+        assert np.array_equal(gl[fin].view(np.uint32), np.asarray(lg, np.float32)[fin].view(np.uint32))
+    gw = g_w.cpu().numpy()
+    fin = same(gw, w, "topk_w")
+    assert np.all(np.abs(gw[fin] - w[fin]) <= 1e-4 * np.maximum(np.abs(w[fin]), 1e-30) + 1e-7)
+
+
 def _filtered_route(cfg, inp):
     """occ_route_topk_ws on the layer's inputs: (indices, weights) on the host."""
     import torch
