@@ -160,22 +160,34 @@ __global__ __launch_bounds__(kTB) void brim_zero_kernel(int32_t *p, int n) {
 
 // keyscan: one wave per key c; exclusive scan of cnt[c][0..nblk) in place,
 // the key's total into tot[c]
+// (the loads of up to 16 chunks of 64 blocks go out before their scans, so
+// their latencies overlap instead of following each other)
 __global__ __launch_bounds__(kTB) void brim_keyscan_kernel(int nblk, int32_t *cnt,
                                                            int32_t *tot) {
+  constexpr int kChunks = 16;
   const int c = blockIdx.x, lane = threadIdx.x;
   int32_t *row = cnt + (size_t)c * nblk;
   int32_t carry = 0;
-  for (int b0 = 0; b0 < nblk; b0 += kTB) {
-    const int b = b0 + lane;
-    const int32_t v = b < nblk ? row[b] : 0;
-    int32_t x = v;
+  for (int g0 = 0; g0 < nblk; g0 += kTB * kChunks) {
+    int32_t v[kChunks];
 #pragma unroll
-    for (int off = 1; off < kTB; off <<= 1) {
-      const int32_t y = __shfl_up(x, off);
-      if (lane >= off) x += y;
+    for (int u = 0; u < kChunks; ++u) {
+      const int b = g0 + kTB * u + lane;
+      v[u] = b < nblk ? row[b] : 0;
     }
-    if (b < nblk) row[b] = carry + x - v;
-    carry += __shfl(x, kTB - 1);
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u) {
+      if (g0 + kTB * u >= nblk) break;  // uniform: no scans of empty chunks
+      const int b = g0 + kTB * u + lane;
+      int32_t x = v[u];
+#pragma unroll
+      for (int off = 1; off < kTB; off <<= 1) {
+        const int32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+      }
+      if (b < nblk) row[b] = carry + x - v[u];
+      carry += __shfl(x, kTB - 1);
+    }
   }
   if (lane == 0) tot[c] = carry;
 }
