@@ -30,6 +30,9 @@ SMALL = {
     # the largest device count and picks per token the library takes
     "bf16_max_devices_and_k": W.LayerConfig("bf16_max_devices_and_k", T=200, d=64, E=64, I=64,
                                             k=16, D=32, dtype="bf16", clusters=4),
+    # an expert count that is not a multiple of 4 and a ragged token count:
+    # the router gradient's products take their element-wise operand loads
+    "bf16_e6": W.LayerConfig("bf16_e6", T=131, d=64, E=6, I=64, k=2, D=2, dtype="bf16"),
 }
 
 

@@ -131,6 +131,7 @@ def test_routing_lane_mappings(orc, T, E, k, renorm, dtype, d):
     (16383, 96, 16, 1, "bf16", 192, False),   # ragged last tile, k = row width
     (20000, 33, 1, 0, "bf16", 256, False),    # one accumulator, lanes past E idle
     (16500, 100, 8, 1, "f32", 96, False),     # fp32 tokens, 32-column chunks
+    (16400, 40, 3, 0, "f32", 32, False),      # a single chunk
     (16384, 96, 6, 0, "bf16", 128, True),     # equal logits: lower index first
 ])
 def test_routing_on_matrix_cores(orc, T, E, k, renorm, dtype, d, tie):
