@@ -102,23 +102,35 @@ __global__ __launch_bounds__(256, 2) void route_mfma_kernel(
   auto body = [&](int c, auto setc) __attribute__((always_inline)) {
     constexpr int S = decltype(setc)::value;
     const float *wl = &ws[c & 1][lane * LW];
+    // the router reads of group g + 1 go out before the MFMAs of group g
+    // (scheduling barriers keep the order), so their LDS latency hides
+    // under those MFMAs
+    float4 wv[2][EACC];
+#pragma unroll
+    for (int a = 0; a < EACC; ++a)
+      wv[0][a] = *reinterpret_cast<const float4 *>(wl + a * 64 * LW);
 #pragma unroll
     for (int g = 0; g < JC / 4; ++g) {  // 4-column groups, j ascending
-      float4 wv[EACC];
+      const int cu = g & 1;
+      if (g + 1 < JC / 4) {
 #pragma unroll
-      for (int a = 0; a < EACC; ++a)
-        wv[a] = *reinterpret_cast<const float4 *>(wl + a * 64 * LW + 4 * g);
+        for (int a = 0; a < EACC; ++a)
+          wv[cu ^ 1][a] = *reinterpret_cast<const float4 *>(wl + a * 64 * LW + 4 * (g + 1));
+      }
       float xf[VPL];
       widen<DT>(xb[S][4 * g / VPL], xf);
       const int o = (4 * g) % VPL;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
 #pragma unroll
         for (int a = 0; a < EACC; ++a) {
-          const float b = c4 == 0 ? wv[a].x : c4 == 1 ? wv[a].y : c4 == 2 ? wv[a].z : wv[a].w;
+          const float4 &w4 = wv[cu][a];
+          const float b = c4 == 0 ? w4.x : c4 == 1 ? w4.y : c4 == 2 ? w4.z : w4.w;
           acc[a] = __builtin_amdgcn_mfma_f32_16x16x1f32(xf[o + c4], b, acc[a], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     store_w((c + 1) & 1);
     load_w(c + 2);
