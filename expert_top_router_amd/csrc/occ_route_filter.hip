@@ -153,9 +153,10 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
 
   // A ring of KP register sets: set c % KP holds k-chunk c from its load
   // until it is stored to LDS, so each chunk's loads have KP - 1 chunks of
-  // compute to land (X streams from HBM; one chunk ahead left it latency-
-  // bound at ≈3 TB/s).
-  constexpr int KP = 4;
+  // compute to land.  Two sets keep the kernel at 110 registers, two blocks
+  // per CU (stress layer in the step: one set 250.5 us, four sets at one
+  // block per CU 243.3, two sets 238.7).
+  constexpr int KP = 2;
   u32x4 rx[KP][XC], rw[KP][WC];
   float sx[XC];
 #pragma unroll
@@ -229,11 +230,11 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
     load(ch + 1 + KP, SET);
     __syncthreads();
   };
-  static_assert(KP == 4, "the loop below is unrolled by four");
+  static_assert(4 % KP == 0, "the loop below is unrolled by four");
   for (int ch = 0; ch < nch; ch += 4) {
-    body(ch, std::integral_constant<int, 1>{});
-    body(ch + 1, std::integral_constant<int, 2>{});
-    body(ch + 2, std::integral_constant<int, 3>{});
+    body(ch, std::integral_constant<int, 1 % KP>{});
+    body(ch + 1, std::integral_constant<int, 2 % KP>{});
+    body(ch + 2, std::integral_constant<int, 3 % KP>{});
     body(ch + 3, std::integral_constant<int, 0>{});
   }
   if (wact) {
