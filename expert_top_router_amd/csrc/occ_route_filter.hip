@@ -43,7 +43,6 @@ typedef float ff32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t fu32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kCap = 16;      // candidates per token
-constexpr int kTok = 128;     // tokens per block (approx and exact kernels)
 constexpr int kNT = 512;      // threads per block (8 waves)
 constexpr float kU = 5.9604645e-8f;  // 2^-24
 
@@ -128,24 +127,26 @@ __global__ __launch_bounds__(256) void route_prep_kernel(int d, const float *__r
 // row (token or expert) l % 32 and the 8 k values 8*(l/32)..+7 of a 16-deep
 // step; output element r of lane l is token 8*(r/4) + 4*(l/32) + r%4 of the
 // tile, expert l % 32.
-template <int EB>
+template <int EB, int KT>
 __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
                                                            const uint16_t *__restrict__ x,
                                                            const uint16_t *__restrict__ wh,
                                                            float *__restrict__ ag,
                                                            float *__restrict__ xn) {
+  constexpr int kTok = KT;             // tokens per block
   constexpr int EPAD = 32 * EB;
   constexpr int JA = 64, LA = JA + 8;  // k-chunk and padded row stride (bf16)
-  constexpr int XC = kTok * JA / 8 / kNT;
+  constexpr int XCT = kTok * JA / 8;   // 16-byte token chunks per k-chunk
+  constexpr int XC = (XCT + kNT - 1) / kNT;
   constexpr int WCH = EPAD * JA / 8;   // 16-byte router chunks per k-chunk
   constexpr int WC = (WCH + kNT - 1) / kNT;
-  static_assert(XC * kNT * 8 == kTok * JA, "whole token chunks");
+  static_assert(kTok % 32 == 0, "whole 32-token MFMA tiles");
   __shared__ __attribute__((aligned(16))) uint16_t xa[2][kTok * LA];
   __shared__ __attribute__((aligned(16))) uint16_t wa[2][EPAD * LA];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kTok;
   const int nch = d / JA;
-  constexpr int NTILE = 4 * EB;
+  constexpr int NTILE = kTok / 32 * EB;
   constexpr int TPW = NTILE >= 8 ? NTILE / 8 : 1;
   const int id0 = wave * TPW;
   const bool wact = id0 < NTILE;  // uniform
@@ -153,10 +154,12 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
 
   // A ring of KP register sets: set c % KP holds k-chunk c from its load
   // until it is stored to LDS, so each chunk's loads have KP - 1 chunks of
-  // compute to land.  Two sets keep the kernel at 110 registers, two blocks
-  // per CU (stress layer in the step: one set 250.5 us, four sets at one
-  // block per CU 243.3, two sets 238.7).
-  constexpr int KP = 2;
+  // compute to land.  128-token blocks: two sets keep the kernel at 110
+  // registers, two blocks per CU (stress layer in the step: one set 250.5
+  // us, four sets at one block per CU 243.3, two sets 238.7); 32-token
+  // blocks have little compute per chunk, so eight sets keep enough bytes
+  // in flight.
+  constexpr int KP = kTok == 128 ? 2 : 8;
   u32x4 rx[KP][XC], rw[KP][WC];
   float sx[XC];
 #pragma unroll
@@ -168,7 +171,8 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
     const int j0 = min(ch, nch - 1) * JA;
 #pragma unroll
     for (int u = 0; u < XC; ++u) {
-      const int c = tid + kNT * u, r = c >> 3, cc = (c & 7) * 8, t = min(t0 + r, T - 1);
+      const int c = min(tid + kNT * u, XCT - 1), r = c >> 3, cc = (c & 7) * 8;
+      const int t = min(t0 + r, T - 1);
       rx[set][u] = *reinterpret_cast<const u32x4 *>(x + (size_t)t * d + j0 + cc);
     }
 #pragma unroll
@@ -181,6 +185,7 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
 #pragma unroll
     for (int u = 0; u < XC; ++u) {
       const int c = tid + kNT * u, r = c >> 3, cc = (c & 7) * 8;
+      if (c >= XCT) continue;
       *reinterpret_cast<u32x4 *>(&xa[st][r * LA + cc]) = rx[set][u];
       if (norm) {  // not for the re-reads past the last chunk
         float f[8];
@@ -230,12 +235,16 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
     load(ch + 1 + KP, SET);
     __syncthreads();
   };
-  static_assert(4 % KP == 0, "the loop below is unrolled by four");
-  for (int ch = 0; ch < nch; ch += 4) {
+  static_assert(8 % KP == 0, "the loop below is unrolled by eight");
+  for (int ch = 0; ch < nch; ch += 8) {
     body(ch, std::integral_constant<int, 1 % KP>{});
     body(ch + 1, std::integral_constant<int, 2 % KP>{});
     body(ch + 2, std::integral_constant<int, 3 % KP>{});
-    body(ch + 3, std::integral_constant<int, 0>{});
+    body(ch + 3, std::integral_constant<int, 4 % KP>{});
+    body(ch + 4, std::integral_constant<int, 5 % KP>{});
+    body(ch + 5, std::integral_constant<int, 6 % KP>{});
+    body(ch + 6, std::integral_constant<int, 7 % KP>{});
+    body(ch + 7, std::integral_constant<int, 0>{});
   }
   if (wact) {
 #pragma unroll
@@ -255,8 +264,8 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
     v += __shfl_xor(v, 1);
     v += __shfl_xor(v, 2);
     v += __shfl_xor(v, 4);
-    const int t = t0 + ((tid + kNT * u) >> 3);
-    if ((tid & 7) == 0 && t < T) xn[t] = sqrtf(v);
+    const int c = tid + kNT * u, t = t0 + (c >> 3);
+    if ((tid & 7) == 0 && c < XCT && t < T) xn[t] = sqrtf(v);
   }
 }
 
@@ -267,14 +276,18 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
 // bf16-exact (else fp32), four chunks of loads ahead in registers; 69 KB
 // of LDS lets two blocks share a CU.
 // (four waves per SIMD: two blocks per CU)
-template <int EB>
-__global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
+template <int EB, int KT>
+__global__ __launch_bounds__(kNT, KT == 128 ? 4 : 2) void route_exact_kernel(
     int T, int d, int E, int k, int renorm, const uint16_t *__restrict__ x,
     const float *__restrict__ wr, const uint16_t *__restrict__ wh, const float *__restrict__ bnd,
     const int32_t *__restrict__ ex, float *__restrict__ agg, const float *__restrict__ xng,
     int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+  constexpr int kTok = KT;                   // tokens per block
+  static_assert(kTok == 128 || kTok == 32, "the two lane mappings below");
   constexpr int EPAD = 32 * EB;
-  constexpr int JB = 32;                     // columns per chunk
+  // columns per chunk: 64 for 32-token blocks, whose chunks carry little
+  // compute, so that more bytes are in flight
+  constexpr int JB = kTok == 128 ? 32 : 64;
   constexpr int LX = JB + 8, LW = JB + 4;    // row strides: bf16 X, fp32 router
   constexpr int KPF = 4;                     // register sets of loads in flight
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][kTok * LX];
@@ -401,12 +414,19 @@ __global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
     }
     __syncthreads();
   }
-  const int tl = 64 * (wave >> 2) + lane, sg = wave & 3;
+  // chain slots: 128 tokens -> a lane keeps token 64 (wave / 4) + lane and
+  // slots (wave % 4) + 4 i, i < 4; 32 tokens -> token lane % 32 and the one
+  // slot 2 wave + lane / 32
+  constexpr int SPL = kCap * kTok / kNT;     // slots per lane
+  constexpr int NSG = kCap / SPL;            // slot groups
+  const int tl = kTok == 128 ? 64 * (wave >> 2) + lane : (lane & 31);
+  const int sg = kTok == 128 ? (wave & 3) : 2 * wave + (lane >> 5);
   const int tok = full ? tl : (int)perm_s[tl];  // the token of this lane's chains
   const int ntk = t0 + tok < T ? (full ? E : nc[tok]) : 0;
-  const int xrow = full ? tid / (JB / 8) : (int)pos_s[tid / (JB / 8)];  // LDS row of this thread's X piece
-  constexpr int XCB = kTok * JB / 8 / kNT;   // 16-byte X loads per thread per chunk
-  static_assert(XCB == 1, "one X load per thread and chunk");
+  constexpr int XCT = kTok * JB / 8;         // 16-byte X pieces per chunk (one per thread at most)
+  static_assert(XCT <= kNT, "one X load per thread and chunk");
+  const int xr0 = min(tid, XCT - 1) / (JB / 8);  // this thread's X row (token)
+  const int xrow = full ? xr0 : (int)pos_s[xr0];  // ... and its LDS row
   const int nchb = d / JB;
   // one pass over d for the chains of slots p * kCap + sg + 4 i.  The
   // certified path (one pass) writes only LDS, the every-chain path writes
@@ -415,11 +435,11 @@ __global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
   // share the completion counter with the loads in flight)
   auto pass = [&](int p, auto fullc) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(fullc)::value;
-    int ei[4];
+    int ei[SPL];
     int mine = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = p * kCap + sg + 4 * i;
+    for (int i = 0; i < SPL; ++i) {
+      const int q = p * kCap + sg + NSG * i;
       const bool v = q < ntk;
       ei[i] = v ? (FULL ? q : (int)cl[tok][q]) : 0;
       mine += v ? 1 : 0;
@@ -427,7 +447,9 @@ __global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
     int nmax = mine;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) nmax = max(nmax, __shfl_xor(nmax, off));
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[SPL];
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) acc[i] = 0.0f;
     // One pass over d.  RB: the router rows are bf16-exact and stream from the
     // workspace's bf16 copy (one 16-byte LDS read per chain and 8 columns,
     // widened in registers); otherwise fp32 rows (two reads).
@@ -446,7 +468,7 @@ __global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
       auto loadb = [&](int c, int set) __attribute__((always_inline)) {
         const int j0 = c * JB;
         {
-          const int r = tid / (JB / 8), cc = (tid % (JB / 8)) * 8, t = min(t0 + r, T - 1);
+          const int cc = (tid % (JB / 8)) * 8, t = min(t0 + xr0, T - 1);
           bx[set] = *reinterpret_cast<const u32x4 *>(x + (size_t)t * d + j0 + cc);
         }
 #pragma unroll
@@ -458,7 +480,7 @@ __global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
         }
       };
       auto storeb = [&](int st, int set) __attribute__((always_inline)) {
-        {
+        if (tid < XCT) {
           const int cc = (tid % (JB / 8)) * 8;
           *reinterpret_cast<u32x4 *>(&xs[st][xrow * LX + cc]) = bx[set];
         }
@@ -492,7 +514,7 @@ __global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
             float xf[8];
             widen<OCC_BF16>(*reinterpret_cast<const u32x4 *>(xr + jj), xf);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < SPL; ++i) {
               if (i < nmax) {
                 float wf[8];
                 if (RB) {
@@ -531,15 +553,15 @@ __global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
       if (rexact) run(std::true_type{});
       else run(std::false_type{});
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = p * kCap + sg + 4 * i;
+      for (int i = 0; i < SPL; ++i) {
+        const int q = p * kCap + sg + NSG * i;
         if (q < ntk) agg[(size_t)(t0 + tl) * E + q] = acc[i];  // exact, in place
       }
     } else {
       run(std::true_type{});  // certified blocks have a bf16-exact router
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = sg + 4 * i;
+      for (int i = 0; i < SPL; ++i) {
+        const int q = sg + NSG * i;
         if (q < ntk) exl[tok][q] = acc[i];
       }
     }
@@ -671,15 +693,15 @@ __global__ __launch_bounds__(kNT, 4) void route_exact_kernel(
   }
 }
 
-template <int EB>
+template <int EB, int KT>
 hipError_t launch_eb(const occ_layer_desc &L, const void *x, const float *wr, int32_t *idx,
                      float *w, const FilterWs &f, hipStream_t st) {
-  const dim3 grid((L.T + kTok - 1) / kTok);
-  route_approx_kernel<EB><<<grid, kNT, 0, st>>>(L.T, L.d, L.E, static_cast<const uint16_t *>(x),
-                                                f.wh, f.ag, f.xn);
-  route_exact_kernel<EB><<<grid, kNT, 0, st>>>(L.T, L.d, L.E, L.k, L.renorm,
-                                               static_cast<const uint16_t *>(x), wr, f.wh, f.bnd,
-                                               f.ex, f.ag, f.xn, idx, w);
+  const dim3 grid((L.T + KT - 1) / KT);
+  route_approx_kernel<EB, KT><<<grid, kNT, 0, st>>>(
+      L.T, L.d, L.E, static_cast<const uint16_t *>(x), f.wh, f.ag, f.xn);
+  route_exact_kernel<EB, KT><<<grid, kNT, 0, st>>>(L.T, L.d, L.E, L.k, L.renorm,
+                                                   static_cast<const uint16_t *>(x), wr, f.wh,
+                                                   f.bnd, f.ex, f.ag, f.xn, idx, w);
   return hipGetLastError();
 }
 
@@ -700,8 +722,16 @@ hipError_t launch_route_filtered(const occ_layer_desc &L, const void *x, const f
   if (L.T == 0) return hipSuccess;
   const FilterWs f = carve(L, ws);
   route_prep_kernel<<<L.E, 256, 0, st>>>(L.d, wr, f.wh, f.bnd, f.ex);
-  if (L.E > 64) return launch_eb<4>(L, x, wr, idx, w, f, st);
-  return launch_eb<2>(L, x, wr, idx, w, f, st);
+  // 128-token blocks from 32768 tokens (one per CU and more), 32-token
+  // blocks below, where 128-token blocks leave most CUs idle (OLMoE-shaped
+  // layer, 4096 tokens: 119 -> 49 us; DeepSeek-V2-Lite-shaped, 16384: 123 ->
+  // 87 us; the chains of a 32-token block are one per lane, so their
+  // latency bounds it)
+  const bool big = L.T >= 32768;
+  if (L.E > 64) return big ? launch_eb<4, 128>(L, x, wr, idx, w, f, st)
+                           : launch_eb<4, 32>(L, x, wr, idx, w, f, st);
+  return big ? launch_eb<2, 128>(L, x, wr, idx, w, f, st)
+             : launch_eb<2, 32>(L, x, wr, idx, w, f, st);
 }
 
 }  // namespace occ

@@ -258,11 +258,13 @@ def _filtered_route(cfg, inp):
 
 
 @pytest.mark.parametrize("T,E,k,renorm", [
+    # 32-token blocks below 32768 tokens, 128-token blocks from there
     (300, 33, 4, 0),      # 64 padded expert rows, ragged last block
     (1000, 64, 8, 1),
     (3001, 128, 16, 0),   # k at the candidate cap
     (20000, 100, 6, 1),
-    (128, 128, 1, 0),     # one whole block, top-1
+    (128, 128, 1, 0),     # whole blocks, top-1
+    (40000, 96, 6, 1),    # 128-token blocks, ragged last block
 ])
 def test_filtered_routing(orc, T, E, k, renorm):
     """Routing through the candidate filter (occ_route_topk_ws): the indices
