@@ -264,6 +264,8 @@ def _filtered_route(cfg, inp):
     (3001, 128, 16, 0),   # k at the candidate cap
     (20000, 100, 6, 1),
     (128, 128, 1, 0),     # whole blocks, top-1
+    (1, 64, 4, 0),        # a single token
+    (33, 33, 4, 1),       # a block of 32 and one token alone
     (40000, 96, 6, 1),    # 128-token blocks, ragged last block
 ])
 def test_filtered_routing(orc, T, E, k, renorm):
