@@ -270,12 +270,13 @@ __global__ __launch_bounds__(kNT) void route_approx_kernel(int T, int d, int E,
 }
 
 // ---- exact: certify, run the candidates' chains, softmax and top-k ---------
-// Chains: lane = token 64 * (wave / 4) + lane, slots q = (wave % 4) + 4 i of
-// that token's candidate list.  X is staged as bf16 (widened when read, one
-// 16-byte read per 8 columns), the router as bf16 when every row is
-// bf16-exact (else fp32), four chunks of loads ahead in registers; 69 KB
-// of LDS lets two blocks share a CU.
-// (four waves per SIMD: two blocks per CU)
+// Chains, KT = 128 tokens per block: lane = token 64 (wave / 4) + lane,
+// slots q = (wave % 4) + 4 i of that token's candidate list (i < 4); KT = 32:
+// lane = token lane % 32, the one slot 2 wave + lane / 32.  X is staged as
+// bf16 (widened when read, one 16-byte read per 8 columns), the router as
+// bf16 when every row is bf16-exact (else fp32), four chunks of loads ahead
+// in registers.  KT = 128: 69 KB of LDS and at most 128 registers, so two
+// blocks (four waves per SIMD) share a CU; KT = 32: one block per CU.
 template <int EB, int KT>
 __global__ __launch_bounds__(kNT, KT == 128 ? 4 : 2) void route_exact_kernel(
     int T, int d, int E, int k, int renorm, const uint16_t *__restrict__ x,
