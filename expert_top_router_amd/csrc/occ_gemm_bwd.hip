@@ -357,10 +357,77 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bwd_kernel(GemmArgs a) {
     }
   } else {
     // bf16 rows staged in LDS and written with 16-byte stores; the SwiGLU
-    // backward writes dG (pass 0, columns [0, N)) and dU (pass 1, [N, 2N)).
-    constexpr int PASSES = EPI == EPI_SWIGLU_BWD ? 2 : 1;
+    // backward writes dG (columns [0, N)) and dU ([N, 2N)).  It reads G and U
+    // once, in two halves of the tile's rows (each wave's 32-row blocks 0-1,
+    // then 2-3): a half's dG and dU rows are staged side by side (2 x 128
+    // rows) and written out before the next half.
     constexpr int RCH = BN / 8;
     const uint16_t *GU = static_cast<const uint16_t *>(a.aux);
+    if (EPI == EPI_SWIGLU_BWD) {
+      static_assert(MI == 4 && 2 * (BM / 2) * CLD <= 2 * STAGE, "two half tiles staged");
+      uint16_t *CsG = smem, *CsU = smem + (BM / 2) * CLD;
+      int prow = crow;
+      asm volatile("" : "+v"(prow));
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int mh = 0; mh < 2; ++mh) {
+          const int mi = 2 * half + mh;
+          const int row = wm * WM + mi * 32 + prow;   // tile row
+          const int srow = wm * (WM / 2) + mh * 32 + prow;  // staging row
+          const int grow = m0 + min(row, mrows - 1);
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            const int col = wn * WN + ni * 32 + ccol;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int gc = min(n0 + col + 8 * q, a.N - 4);
+              const u32x2 gp = *reinterpret_cast<const u32x2 *>(GU + (int64_t)grow * a.ldaux + gc);
+              const u32x2 up =
+                  *reinterpret_cast<const u32x2 *>(GU + (int64_t)grow * a.ldaux + a.N + gc);
+              const float gv[4] = {__uint_as_float(gp.x << 16), __uint_as_float(gp.x & 0xffff0000u),
+                                   __uint_as_float(gp.y << 16), __uint_as_float(gp.y & 0xffff0000u)};
+              const float uv[4] = {__uint_as_float(up.x << 16), __uint_as_float(up.x & 0xffff0000u),
+                                   __uint_as_float(up.y << 16), __uint_as_float(up.y & 0xffff0000u)};
+              float vg[4], vu[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float dh = acc[mi][ni][4 * q + j];
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[j]));
+                vg[j] = dh * uv[j] * silu_grad(gv[j], sg);
+                vu[j] = dh * gv[j] * sg;
+              }
+              const f32x2v glo = {vg[0], vg[1]}, ghi = {vg[2], vg[3]};
+              const f32x2v ulo = {vu[0], vu[1]}, uhi = {vu[2], vu[3]};
+              *reinterpret_cast<u32x2 *>(CsG + srow * CLD + col + 8 * q) = u32x2{
+                  __builtin_bit_cast(uint32_t, __builtin_convertvector(glo, bf16x2v)),
+                  __builtin_bit_cast(uint32_t, __builtin_convertvector(ghi, bf16x2v))};
+              *reinterpret_cast<u32x2 *>(CsU + srow * CLD + col + 8 * q) = u32x2{
+                  __builtin_bit_cast(uint32_t, __builtin_convertvector(ulo, bf16x2v)),
+                  __builtin_bit_cast(uint32_t, __builtin_convertvector(uhi, bf16x2v))};
+            }
+          }
+          // one 32-row block at a time: keeps the G / U loads from being
+          // hoisted all together (register pressure)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        uint16_t *Cg = static_cast<uint16_t *>(a.C) + (int64_t)m0 * a.ldc + n0;
+        for (int c = tid; c < 2 * (BM / 2) * RCH; c += NT) {
+          const int part = c / ((BM / 2) * RCH);        // 0: dG, 1: dU
+          const int cr = c - part * (BM / 2) * RCH;
+          const int sr = cr / RCH, cc = cr - sr * RCH;
+          // staging row sr is tile row (sr / 64) * 128 + 64 half + sr % 64
+          const int r = (sr / (WM / 2)) * WM + half * (WM / 2) + sr % (WM / 2);
+          const uint16_t *src = (part ? CsU : CsG) + sr * CLD + cc * 8;
+          if (r < mrows && n0 + cc * 8 < a.N)
+            *reinterpret_cast<u32x4 *>(Cg + (int64_t)r * a.ldc + part * a.N + cc * 8) =
+                *reinterpret_cast<const u32x4 *>(src);
+        }
+        __syncthreads();
+      }
+    } else {
+    constexpr int PASSES = 1;
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
       uint16_t *Cs = smem;
@@ -416,6 +483,7 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_bwd_kernel(GemmArgs a) {
               *reinterpret_cast<const u32x4 *>(Cs + r * CLD + cc * 8);
       }
       __syncthreads();
+    }
     }
   }
   __syncthreads();  // the staging area is the next tile's first LDS stage
