@@ -291,8 +291,18 @@ __global__ __launch_bounds__(kNT, KT == 128 ? 4 : 2) void route_exact_kernel(
   constexpr int JB = kTok == 128 ? 32 : 64;
   constexpr int LX = JB + 8, LW = JB + 4;    // row strides: bf16 X, fp32 router
   constexpr int KPF = 4;                     // register sets of loads in flight
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kTok * LX];
-  __shared__ __attribute__((aligned(16))) float ws[2][EPAD * LW];
+  // X staging rows for every thread's piece: threads past the block's
+  // tokens store into spare rows that nothing reads, so the stores (and the
+  // loads feeding them) stay unconditional; a guarded store lets the
+  // compiler sink its load next to it, one full memory latency per chunk
+  constexpr int XROWS = kNT / (JB / 8) > kTok ? kNT / (JB / 8) : kTok;
+  // router rows likewise (bf16 rows of JB / 8 pieces or fp32 rows of JB / 4)
+  constexpr int WPN_B = (EPAD * JB / 8 + kNT - 1) / kNT, WPN_F = (EPAD * JB / 4 + kNT - 1) / kNT;
+  constexpr int WROWS_B = WPN_B * kNT / (JB / 8), WROWS_F = WPN_F * kNT / (JB / 4);
+  constexpr int WROWS = WROWS_B > WROWS_F ? (WROWS_B > EPAD ? WROWS_B : EPAD)
+                                          : (WROWS_F > EPAD ? WROWS_F : EPAD);
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][XROWS * LX];
+  __shared__ __attribute__((aligned(16))) float ws[2][WROWS * LW];
   __shared__ __attribute__((aligned(16))) float exl[kTok][kCap];
   __shared__ __attribute__((aligned(16))) uint8_t cl[kTok][kCap];
   __shared__ int32_t nc[kTok];
@@ -427,7 +437,8 @@ __global__ __launch_bounds__(kNT, KT == 128 ? 4 : 2) void route_exact_kernel(
   constexpr int XCT = kTok * JB / 8;         // 16-byte X pieces per chunk (one per thread at most)
   static_assert(XCT <= kNT, "one X load per thread and chunk");
   const int xr0 = min(tid, XCT - 1) / (JB / 8);  // this thread's X row (token)
-  const int xrow = full ? xr0 : (int)pos_s[xr0];  // ... and its LDS row
+  const int xrow = tid >= XCT ? tid / (JB / 8)    // a spare row
+                   : full ? xr0 : (int)pos_s[xr0];  // ... and its LDS row
   const int nchb = d / JB;
   // one pass over d for the chains of slots p * kCap + sg + 4 i.  The
   // certified path (one pass) writes only LDS, the every-chain path writes
@@ -481,17 +492,15 @@ __global__ __launch_bounds__(kNT, KT == 128 ? 4 : 2) void route_exact_kernel(
         }
       };
       auto storeb = [&](int st, int set) __attribute__((always_inline)) {
-        if (tid < XCT) {
+        {
           const int cc = (tid % (JB / 8)) * 8;
           *reinterpret_cast<u32x4 *>(&xs[st][xrow * LX + cc]) = bx[set];
         }
 #pragma unroll
-        for (int u = 0; u < WPN; ++u) {
+        for (int u = 0; u < WPN; ++u) {  // pieces past the router go to spare rows
           const int cw = tid + kNT * u, r = cw / WPR, cc = (cw % WPR) * (RB ? 8 : 4);
-          if (cw < WCN) {
-            if (RB) *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(ws[st]) + r * LX + cc) = bw[set][u];
-            else *reinterpret_cast<u32x4 *>(&ws[st][r * LW + cc]) = bw[set][u];
-          }
+          if (RB) *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(ws[st]) + r * LX + cc) = bw[set][u];
+          else *reinterpret_cast<u32x4 *>(&ws[st][r * LW + cc]) = bw[set][u];
         }
       };
       __syncthreads();  // earlier readers of the staging buffers are done
